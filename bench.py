@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of document-masked causal GQA attention (forward + backward) for
+one context-parallel rank on one MI355X.
+
+A step is one pass of the whole hot path -- forward call then backward call
+of the C-ABI library -- over one seed's synthetic input.  The timed steps
+cycle over the seeds (all inputs resident in HBM before timing starts).
+`value` is useful TFLOP/s over the timed steps: useful FLOPs count
+4*D (forward) + 8*D (backward) per allowed (query, key) pair per query head,
+excluding recomputation as model-FLOPs utilisation does ("Training
+Infrastructure and Systems", "Model FLOPs Utilization").
+
+    python bench.py [--steps K] [--warmup W] [--workload tp405b]
+
+Prints one JSON line.  Only one GPU is used; --gpus N with N > 1 exits.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np
+
+# MI355X published dense MFMA peak for bf16: 256 CUs x 2.4 GHz x 4096 flop/clk/CU.
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+PEAK_HBM_GBS = 8000.0
+
+
+def local_positions(S: int, cp: int, r: int) -> np.ndarray:
+    c = S // (2 * cp)
+    return np.concatenate([np.arange(r * c, (r + 1) * c),
+                           np.arange((2 * cp - 1 - r) * c, (2 * cp - r) * c)])
+
+
+def allowed_pairs(lengths, S: int, cp: int, r: int) -> int:
+    """Allowed (query, key) pairs of the rank's local rows (per query head):
+    each local position p may attend to its document's keys start(p)..p."""
+    starts = np.repeat(np.concatenate([[0], np.cumsum(lengths)[:-1]]), lengths)
+    pos = local_positions(S, cp, r)
+    return int((pos - starts[pos] + 1).sum())
+
+
+def useful_flops(pairs: int, Hq: int, D: int, backward: bool) -> dict:
+    """Useful FLOPs split by the kernel that does each product:
+    forward Q K^T and P V (4D per pair-head); dQ kernel dS K (2D); dK/dV kernel
+    dO V^T, P^T dO and dS^T Q (6D)."""
+    ph = pairs * Hq
+    f = {"fwd": 4 * D * ph}
+    if backward:
+        f["bwd_dq"] = 2 * D * ph
+        f["bwd_dkdv"] = 6 * D * ph
+    f["total"] = sum(f.values())
+    return f
+
+
+def algorithmic_bytes(case, backward: bool) -> int:
+    """Minimum HBM bytes of one step: read Q and reachable K/V, write out/lse
+    (forward); read Q, out, dO, lse, reachable K/V, write dQ, dK, dV
+    (backward, dK/dV fp32 over the whole key prefix)."""
+    B, Sq, Hq, D = case.q.shape
+    Skv, Hkv = case.k.shape[1], case.k.shape[2]
+    q = B * Sq * Hq * D * 2
+    kv = 2 * B * Skv * Hkv * D * 2
+    lse = B * Sq * Hq * 4
+    fwd = q + kv + q + lse
+    if not backward:
+        return fwd
+    bwd = 3 * q + lse + kv + q + 2 * B * Skv * Hkv * D * 4
+    return fwd + bwd
+
+
+def cpu_baseline(runs, min_s: float = 10.0, max_s: float = 30.0) -> dict:
+    """The CPU oracle (fp64 numpy, all host cores) on the same inputs: whole
+    ranks' forward + backward, cycling over the seeds until at least min_s
+    seconds of work (stopping before max_s)."""
+    import oracle
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    done, flops, t0 = [], 0.0, time.perf_counter()
+    i = 0
+    while True:
+        r = runs[i % len(runs)]
+        c = r["case"]
+        t1 = time.perf_counter()
+        oracle.attn_bwd(c.q, c.k, c.v, c.dout, c.doc_ids, c.cfg.cp_size, c.rank, c.scale,
+                        threads=cores, return_fwd=True)
+        last = time.perf_counter() - t1
+        flops += r["flops"]["total"]
+        done.append(c.seed)
+        i += 1
+        el = time.perf_counter() - t0
+        if el >= min_s or el + last > max_s:
+            break
+    dt = time.perf_counter() - t0
+    cfg = runs[0]["case"].cfg
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{cfg.name} rank {runs[0]['case'].rank}: the oracle's whole-rank forward + "
+                      f"backward on seeds {done} (same inputs as the GPU steps)"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="tp405b")
+    ap.add_argument("--rank", type=int, default=None, help="CP rank (default: first listed)")
+    ap.add_argument("--seeds", default="0,1,2,3,4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): this "
+              "library has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import context_gqa_amd as M
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    M.lib()
+    cfg = W.CONFIGS[args.workload]
+    rank = cfg.ranks[0] if args.rank is None else args.rank
+    seeds = [int(s) for s in args.seeds.split(",") if s != ""]
+    dev = torch.device("cuda:0")
+
+    runs = []
+    for seed in seeds:
+        case = W.make_case(cfg, seed, rank)
+        B, Sq, Hq, D = case.q.shape
+        Skv, Hkv = case.Skv, cfg.Hkv
+        S = cfg.S
+        t = dict(q=case.q.to(dev), k=case.k.to(dev), v=case.v.to(dev), dout=case.dout.to(dev),
+                 doc=torch.from_numpy(case.doc_ids).to(dev))
+        t["out"] = torch.empty_like(t["q"])
+        t["lse"] = torch.empty(B, Sq, Hq, dtype=torch.float32, device=dev)
+        t["dq"] = torch.empty_like(t["q"])
+        t["dk"] = torch.empty(B, Skv, Hkv, D, dtype=torch.float32, device=dev)
+        t["dv"] = torch.empty_like(t["dk"])
+        t["wsf"] = torch.empty(max(1, M.docmask_gqa_fwd_workspace_size(B, S, Skv, Hq, Hkv, D,
+                                                                      cfg.cp_size)),
+                               dtype=torch.uint8, device=dev)
+        t["wsb"] = torch.empty(max(1, M.docmask_gqa_bwd_workspace_size(B, S, Skv, Hq, Hkv, D,
+                                                                      cfg.cp_size)),
+                               dtype=torch.uint8, device=dev)
+        pairs = sum(allowed_pairs(l, S, cfg.cp_size, rank) for l in case.lengths)
+        runs.append(dict(case=case, t=t, pairs=pairs,
+                         flops=useful_flops(pairs, Hq, D, cfg.backward),
+                         bytes=algorithmic_bytes(case, cfg.backward)))
+
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        r = runs[i % len(runs)]
+        t, case = r["t"], r["case"]
+        M.docmask_gqa_attn_fwd(t["q"], t["k"], t["v"], doc_ids=t["doc"], cp_size=cfg.cp_size,
+                               cp_rank=rank, softmax_scale=case.scale, out=t["out"],
+                               lse=t["lse"], workspace=t["wsf"], stream=stream)
+        if cfg.backward:
+            M.docmask_gqa_attn_bwd(t["q"], t["k"], t["v"], t["out"], t["dout"], t["lse"],
+                                   doc_ids=t["doc"], cp_size=cfg.cp_size, cp_rank=rank,
+                                   softmax_scale=case.scale, dq=t["dq"], dk=t["dk"], dv=t["dv"],
+                                   workspace=t["wsb"], stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    flops = sum(runs[i % len(runs)]["flops"]["total"] for i in range(args.steps))
+    value = flops / (ms * 1e-3) / 1e12
+
+    per_seed = []
+    for j, r in enumerate(runs):   # per-seed time for the median
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
+        reps = max(3, args.steps // len(runs))
+        a.record(stream)
+        for _ in range(reps):
+            step(j)
+        b.record(stream)
+        torch.cuda.synchronize()
+        per_seed.append(r["flops"]["total"] / (a.elapsed_time(b) / reps * 1e-3) / 1e12)
+
+    roofline = None
+    kernels = {}
+    if not args.no_kernel_timing:
+        M.docmask_gqa_timing_enable(True)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        times = M.docmask_gqa_kernel_times()
+        M.docmask_gqa_timing_enable(False)
+        kernels = {k: {"avg_us": round(1e3 * v[0] / v[1], 3), "launches": v[1]}
+                   for k, v in times.items() if v[1] > 0}
+        dom = max((k for k in times if times[k][1] > 0), key=lambda k: times[k][0])
+        tot_ms, n = times[dom]
+        alg = sum(runs[i % len(runs)]["flops"].get(dom, 0) for i in range(args.steps)) / args.steps
+        achieved = alg / (tot_ms / n * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                    "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "avg_launch_us": round(1e3 * tot_ms / n, 3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(runs)
+
+    res = {
+        "metric": "doc-masked GQA attn fwd+bwd useful TFLOP/s; % MI355X bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.description}", "cp_size": cfg.cp_size,
+                   "cp_rank": rank, "seq_len": cfg.S, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
+                   "head_dim": cfg.D, "global_batch": cfg.B, "seeds": seeds,
+                   "parallelism": "one CP rank's share on one GPU"},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "per_seed_tflops": [round(x, 2) for x in per_seed],
+        "median_seed_tflops": round(float(np.median(per_seed)), 2),
+        "useful_gflop_per_seed": [round(r["flops"]["total"] / 1e9, 2) for r in runs],
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

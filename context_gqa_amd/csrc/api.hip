@@ -1,0 +1,279 @@
+// C-ABI entry points of libdocmask_gqa: argument validation (before any HIP
+// call), workspace layout and kernel launches.  The operation and the
+// argument contract are documented in include/docmask_gqa.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <unordered_set>
+#include <vector>
+
+#include "../../include/docmask_gqa.h"
+#include "kernels.hpp"
+
+namespace dmgqa {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Shape {
+  int B, S, Skv, Hq, Hkv, D, cp, rank;
+  int G, c, Sq;
+  bool empty;
+};
+
+// Scalar checks shared by both passes.  Returns DMGQA_OK or an error.
+int check_shape(int B, int S, int Skv, int Hq, int Hkv, int D, int cp, int rank, Shape* sh) {
+  if (B < 0 || S < 0 || Skv < 0 || Hq <= 0 || Hkv <= 0 || cp <= 0) return DMGQA_ERR_INVALID_ARG;
+  if (rank < 0 || rank >= cp) return DMGQA_ERR_INVALID_ARG;
+  if (S % (2 * cp) != 0) return DMGQA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return DMGQA_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return DMGQA_ERR_UNSUPPORTED;
+  const int c = S / (2 * cp);
+  const long long need = (long long)(2 * cp - rank) * c;
+  if ((long long)Skv < need || Skv > S) return DMGQA_ERR_INVALID_ARG;
+  const int G = Hq / Hkv;
+  const long long Sq = 2LL * c;
+  // row index within a KV group and grid sizes are 32-bit
+  if (Sq * G >= (1LL << 30) || (long long)Skv * 2 >= (1LL << 31)) return DMGQA_ERR_UNSUPPORTED;
+  const long long tiles = (Sq * G + kFwdBM - 1) / kFwdBM * (long long)B * Hkv;
+  if (tiles >= (1LL << 31)) return DMGQA_ERR_UNSUPPORTED;
+  sh->B = B; sh->S = S; sh->Skv = Skv; sh->Hq = Hq; sh->Hkv = Hkv; sh->D = D;
+  sh->cp = cp; sh->rank = rank; sh->G = G; sh->c = c; sh->Sq = (int)Sq;
+  sh->empty = (B == 0 || S == 0);
+  return DMGQA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_docs_args(const int32_t* doc_ids, const int32_t* cu, int n_docs, const Shape& s) {
+  if ((doc_ids == nullptr) == (cu == nullptr)) return DMGQA_ERR_INVALID_ARG;
+  if (doc_ids && !aligned(doc_ids, 4)) return DMGQA_ERR_INVALID_ARG;
+  if (cu) {
+    if (s.B > 1) return DMGQA_ERR_UNSUPPORTED;
+    if (n_docs < 1 || n_docs > s.S || !aligned(cu, 4)) return DMGQA_ERR_INVALID_ARG;
+  }
+  return DMGQA_OK;
+}
+
+// Workspace layout.
+struct Layout {
+  size_t dstart, dend, agg, Dbuf, hdr, tile_info, items, partial, total;
+  int nkt, max_split_base;
+};
+
+Layout layout(const Shape& s, bool backward) {
+  Layout L{};
+  size_t off = 0;
+  const size_t pos = (size_t)s.B * s.Skv * sizeof(int32_t);
+  const int nblk = (s.Skv + 1023) / 1024;
+  L.dstart = off; off = align_up(off + pos);
+  L.dend = off; off = align_up(off + pos);
+  L.agg = off; off = align_up(off + 2 * (size_t)s.B * nblk * sizeof(int32_t));
+  if (backward) {
+    L.nkt = (s.Skv + kDkdvBN - 1) / kDkdvBN;
+    L.max_split_base = kMaxSplitTotal / s.Hkv > 1 ? kMaxSplitTotal / s.Hkv : 1;
+    const size_t ntiles = (size_t)s.B * L.nkt;
+    L.Dbuf = off; off = align_up(off + (size_t)s.B * s.Sq * s.Hq * sizeof(float));
+    L.hdr = off; off = align_up(off + sizeof(SchedHeader));
+    L.tile_info = off; off = align_up(off + ntiles * sizeof(int2));
+    L.items = off; off = align_up(off + (ntiles + L.max_split_base) * sizeof(int2));
+    const size_t slots = 2 * (size_t)L.max_split_base * s.Hkv;
+    L.partial = off; off = align_up(off + slots * 2 * kDkdvBN * s.D * sizeof(float));
+  }
+  L.total = off;
+  return L;
+}
+
+Geo make_geo(const Shape& s, float scale) {
+  Geo g;
+  g.B = s.B; g.S = s.S; g.Skv = s.Skv; g.Hq = s.Hq; g.Hkv = s.Hkv; g.G = s.G;
+  g.Sq = s.Sq; g.c = s.c; g.cp = s.cp; g.rank = s.rank;
+  g.scale = scale;
+  g.scale_log2 = scale * kLog2e;
+  return g;
+}
+
+int prep(const int32_t* doc_ids, const int32_t* cu, int n_docs, const Shape& s, char* ws,
+         const Layout& L, hipStream_t st) {
+  int32_t* dstart = reinterpret_cast<int32_t*>(ws + L.dstart);
+  int32_t* dend = reinterpret_cast<int32_t*>(ws + L.dend);
+  timing_begin(kKPrep, st);
+  hipError_t e = doc_ids ? launch_prep_docs(doc_ids, s.B, s.S, s.Skv, dstart, dend,
+                                            reinterpret_cast<int32_t*>(ws + L.agg), st)
+                         : launch_prep_cu(cu, n_docs, s.Skv, dstart, dend, st);
+  timing_end(kKPrep, st);
+  return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace dmgqa
+
+using namespace dmgqa;
+
+extern "C" {
+
+size_t docmask_gqa_fwd_workspace_size(int32_t B, int32_t S, int32_t Skv, int32_t Hq, int32_t Hkv,
+                                      int32_t D, int32_t cp_size) {
+  Shape s;
+  // the rank does not change the size; rank 0 needs the longest prefix, so
+  // validate against the largest Skv any rank may pass
+  if (check_shape(B, S, S, Hq, Hkv, D, cp_size, 0, &s) != DMGQA_OK) return 0;
+  s.Skv = Skv > 0 && Skv <= S ? Skv : S;
+  if (s.empty) return 0;
+  return layout(s, false).total;
+}
+
+size_t docmask_gqa_bwd_workspace_size(int32_t B, int32_t S, int32_t Skv, int32_t Hq, int32_t Hkv,
+                                      int32_t D, int32_t cp_size) {
+  Shape s;
+  if (check_shape(B, S, S, Hq, Hkv, D, cp_size, 0, &s) != DMGQA_OK) return 0;
+  s.Skv = Skv > 0 && Skv <= S ? Skv : S;
+  if (s.empty) return 0;
+  return layout(s, true).total;
+}
+
+int docmask_gqa_attn_fwd(const void* q, const void* k, const void* v, const int32_t* doc_ids,
+                         const int32_t* cu_seqlens, int32_t n_docs, int32_t B, int32_t S,
+                         int32_t Skv, int32_t Hq, int32_t Hkv, int32_t D, int32_t cp_size,
+                         int32_t cp_rank, float softmax_scale, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  int rc = check_shape(B, S, Skv, Hq, Hkv, D, cp_size, cp_rank, &s);
+  if (rc != DMGQA_OK) return rc;
+  if (!std::isfinite(softmax_scale) || softmax_scale == 0.f) return DMGQA_ERR_INVALID_ARG;
+  if (s.empty) return DMGQA_OK;
+  if (!q || !k || !v || !out || !lse || !workspace) return DMGQA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, 16))
+    return DMGQA_ERR_INVALID_ARG;
+  rc = check_docs_args(doc_ids, cu_seqlens, n_docs, s);
+  if (rc != DMGQA_OK) return rc;
+  const Layout L = layout(s, false);
+  if (workspace_bytes < L.total) return DMGQA_ERR_WORKSPACE;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  rc = prep(doc_ids, cu_seqlens, n_docs, s, ws, L, st);
+  if (rc != DMGQA_OK) return rc;
+  const Geo g = make_geo(s, softmax_scale);
+  timing_begin(kKFwd, st);
+  hipError_t e = launch_fwd(D, static_cast<const u16*>(q), static_cast<const u16*>(k),
+                            static_cast<const u16*>(v),
+                            reinterpret_cast<const int32_t*>(ws + L.dstart),
+                            static_cast<u16*>(out), lse, g, st);
+  timing_end(kKFwd, st);
+  return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
+}
+
+int docmask_gqa_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                         const void* dout, const float* lse, const int32_t* doc_ids,
+                         const int32_t* cu_seqlens, int32_t n_docs, int32_t B, int32_t S,
+                         int32_t Skv, int32_t Hq, int32_t Hkv, int32_t D, int32_t cp_size,
+                         int32_t cp_rank, float softmax_scale, void* dq, float* dk, float* dv,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  int rc = check_shape(B, S, Skv, Hq, Hkv, D, cp_size, cp_rank, &s);
+  if (rc != DMGQA_OK) return rc;
+  if (!std::isfinite(softmax_scale) || softmax_scale == 0.f) return DMGQA_ERR_INVALID_ARG;
+  if (s.empty) return DMGQA_OK;
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return DMGQA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(lse, 4) || !aligned(dk, 16) ||
+      !aligned(dv, 16) || !aligned(workspace, 16))
+    return DMGQA_ERR_INVALID_ARG;
+  rc = check_docs_args(doc_ids, cu_seqlens, n_docs, s);
+  if (rc != DMGQA_OK) return rc;
+  const Layout L = layout(s, true);
+  if (workspace_bytes < L.total) return DMGQA_ERR_WORKSPACE;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  rc = prep(doc_ids, cu_seqlens, n_docs, s, ws, L, st);
+  if (rc != DMGQA_OK) return rc;
+  const Geo g = make_geo(s, softmax_scale);
+  const int32_t* dstart = reinterpret_cast<const int32_t*>(ws + L.dstart);
+  const int32_t* dend = reinterpret_cast<const int32_t*>(ws + L.dend);
+  float* Dbuf = reinterpret_cast<float*>(ws + L.Dbuf);
+  SchedHeader* hdr = reinterpret_cast<SchedHeader*>(ws + L.hdr);
+  int2* tile_info = reinterpret_cast<int2*>(ws + L.tile_info);
+  int2* items = reinterpret_cast<int2*>(ws + L.items);
+  float* partial = reinterpret_cast<float*>(ws + L.partial);
+
+  timing_begin(kKSched, st);
+  hipError_t e = launch_sched_dkdv(dend, g, L.nkt, L.max_split_base, hdr, tile_info, items, st);
+  timing_end(kKSched, st);
+  if (e != hipSuccess) return DMGQA_ERR_HIP;
+  timing_begin(kKDq, st);
+  e = launch_bwd_dq(D, static_cast<const u16*>(q), static_cast<const u16*>(k),
+                    static_cast<const u16*>(v), static_cast<const u16*>(out),
+                    static_cast<const u16*>(dout), lse, dstart, static_cast<u16*>(dq), Dbuf, g,
+                    st);
+  timing_end(kKDq, st);
+  if (e != hipSuccess) return DMGQA_ERR_HIP;
+  timing_begin(kKDkdv, st);
+  e = launch_bwd_dkdv(D, static_cast<const u16*>(q), static_cast<const u16*>(k),
+                      static_cast<const u16*>(v), static_cast<const u16*>(dout), lse, dstart,
+                      dend, Dbuf, hdr, tile_info, items, partial, dk, dv, g, L.nkt, st);
+  timing_end(kKDkdv, st);
+  if (e != hipSuccess) return DMGQA_ERR_HIP;
+  timing_begin(kKReduce, st);
+  e = launch_bwd_reduce(D, tile_info, partial, dk, dv, g, L.nkt, st);
+  timing_end(kKReduce, st);
+  return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
+}
+
+int docmask_gqa_check_docs(const int32_t* doc_ids, int32_t B, int32_t S, void* stream) {
+  if (B < 0 || S < 0) return DMGQA_ERR_INVALID_ARG;
+  if (B == 0 || S == 0) return 0;
+  if (!doc_ids) return DMGQA_ERR_INVALID_ARG;
+  std::vector<int32_t> h((size_t)B * S);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(h.data(), doc_ids, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return DMGQA_ERR_HIP;
+  for (int b = 0; b < B; ++b) {
+    std::unordered_set<int32_t> seen;
+    const int32_t* d = h.data() + (size_t)b * S;
+    for (int t = 0; t < S; ++t) {
+      if (t > 0 && d[t] == d[t - 1]) continue;
+      if (!seen.insert(d[t]).second) return 1;
+    }
+  }
+  return 0;
+}
+
+int docmask_gqa_check_cu_seqlens(const int32_t* cu_seqlens, int32_t n_docs, int32_t S,
+                                 void* stream) {
+  if (n_docs < 1 || S < 0 || !cu_seqlens) return DMGQA_ERR_INVALID_ARG;
+  std::vector<int32_t> h((size_t)n_docs + 1);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(h.data(), cu_seqlens, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+                     st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return DMGQA_ERR_HIP;
+  if (h[0] != 0 || h[n_docs] != S) return 1;
+  for (int i = 0; i < n_docs; ++i)
+    if (h[i + 1] <= h[i]) return 1;
+  return 0;
+}
+
+const char* docmask_gqa_status_string(int status) {
+  switch (status) {
+    case DMGQA_OK: return "ok";
+    case DMGQA_ERR_INVALID_ARG: return "invalid argument";
+    case DMGQA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DMGQA_ERR_WORKSPACE: return "workspace too small";
+    case DMGQA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int docmask_gqa_version(void) { return 100; }
+
+}  // extern "C"

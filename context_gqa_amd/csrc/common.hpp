@@ -1,0 +1,105 @@
+// Shared device helpers for the gfx950 document-masked GQA attention kernels.
+//
+// MFMA conventions used throughout (v_mfma_f32_32x32x16_bf16, wave64):
+//   lane l = 32*h + i  (h = l/32 in {0,1}, i = l%32)
+//   A operand [32 x 16]: lane l holds A[m = i][k = 8h .. 8h+7]
+//   B operand [16 x 32]: lane l holds B[k = 8h .. 8h+7][n = i]
+//   C/D [32 x 32] fp32:  lane l, register r holds C[m = 8(r/4) + 4h + r%4][n = i]
+// A kernel keeps the score tile as S^T (kv along m, queries along n) so each
+// lane owns one query row; the 16 registers then hold 16 key columns of that
+// row.  Feeding those registers back as the B operand of the next product
+// (P^T, dS^T) pairs register slot (h, e) of a 16-wide k-step ks with key
+// index 16*ks + 8*(e/4) + 4*h + e%4; the other operand is read from LDS in the
+// same key order with ds_read_b64_tr_b16 (see tr_operand below).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dmgqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+// 16-byte global load of 8 bf16.
+__device__ __forceinline__ bf16x8 ld_bf16x8(const u16* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+// 16-byte LDS load of 8 bf16.
+__device__ __forceinline__ bf16x8 lds_bf16x8(const u16* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, result lane j element e
+// is element (j % 4) of the 4 bf16 that source lane 4*e + j/4 addresses.
+// So if source lane s (s = lane % 16) points at row (k0 + s/4), column
+// (n0 + 4*(s%4)) of a row-major tile, lane j receives rows k0..k0+3 of column
+// n0 + j: four consecutive k values of one column.
+__device__ __forceinline__ i16x4 ds_read_tr(const u16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+}
+
+// MFMA operand holding, for lane l = 32*h + i, column (n0 + i) of a
+// row-major bf16 LDS tile `base` (row stride `ld` elements) at the 8 rows
+// that register slot (h, e) pairs with in k-step ks:
+//   row = 16*ks + 8*(e/4) + 4*h + e%4.
+// Two transposed reads, each giving four consecutive rows.
+__device__ __forceinline__ bf16x8 tr_operand(const u16* base, int ld, int ks, int n0,
+                                             int lane) {
+  const int s = lane & 15;
+  const int grp = lane >> 4;        // 0..3
+  const int h = grp >> 1;
+  const int col = n0 + 16 * (grp & 1) + 4 * (s & 3);
+  const int row = 16 * ks + 4 * h + (s >> 2);
+  i16x4 lo = ds_read_tr(base + row * ld + col);
+  i16x4 hi = ds_read_tr(base + (row + 8) * ld + col);
+  bf16x8 r;
+  bf16x4 a = __builtin_bit_cast(bf16x4, lo);
+  bf16x4 b = __builtin_bit_cast(bf16x4, hi);
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+// Registers 8*(ks%2) .. 8*(ks%2)+7 of an S^T-shaped accumulator as a bf16
+// MFMA operand (round to nearest even).
+__device__ __forceinline__ bf16x8 pack_bf16(const f32x16& acc, int half) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)acc[8 * half + e];
+  return r;
+}
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+// Global position of local row j (chunk layout of the rank).
+__device__ __forceinline__ int local_pos(int j, int c, int cp, int rank) {
+  return j < c ? rank * c + j : (2 * cp - 1 - rank) * c + (j - c);
+}
+
+// Per-call geometry shared by every kernel.
+struct Geo {
+  int B, S, Skv, Hq, Hkv, G, Sq, c, cp, rank;
+  float scale;       // softmax scale
+  float scale_log2;  // scale * log2(e)
+};
+
+}  // namespace dmgqa

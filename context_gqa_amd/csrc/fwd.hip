@@ -1,0 +1,160 @@
+// Forward kernel: document-masked causal GQA attention for one CP rank.
+//
+// Method ("Training Infrastructure and Systems", "FlashAttention: never write
+// the score matrix", sections "Online softmax" and "Tiling"): a workgroup
+// keeps a tile of query rows in registers and walks the key/value tiles its
+// rows can reach, never writing scores to HBM.  Per key tile it forms the
+// raw scores with MFMA, masks them only when the tile is partial, updates the
+// running row maximum m and sum l with the rescaling factor
+// exp(scale*(m_old - m_new)), rescales the running output by the same factor
+// and adds P V.  At the end it writes out = O / l and lse = scale*m + ln l.
+//
+// Layout on gfx950: 4 waves x 32 query rows; rows are (token, head-in-group)
+// pairs of one KV head, so one K/V tile in LDS serves all G query heads
+// sharing it (GQA).  Scores are held as S^T = K Q^T so that each lane owns
+// one query row (two lanes per row, 16 keys each): the row max and sum need
+// one cross-lane exchange.  P V is computed as O^T = V^T P^T with V read
+// from LDS by transposed reads.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "qtile.hpp"
+
+namespace dmgqa {
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(const u16* __restrict__ q,
+                                                     const u16* __restrict__ k,
+                                                     const u16* __restrict__ v,
+                                                     const int32_t* __restrict__ dstart,
+                                                     u16* __restrict__ out,
+                                                     float* __restrict__ lse, Geo g) {
+  constexpr int BM = kFwdBM, BN = kFwdBN, LD = D + 8, KK = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(16))) u16 sK[BN * LD];
+  __shared__ __attribute__((aligned(16))) u16 sV[BN * LD];
+
+  const int nrows = g.Sq * g.G;
+  const int nt = (nrows + BM - 1) / BM;
+  const int nbg = g.B * g.Hkv;
+  // heaviest tiles (latest positions) are dispatched first
+  const int tile = nt - 1 - (int)(blockIdx.x / nbg);
+  const int bg = blockIdx.x % nbg;
+  const int b = bg / g.Hkv, kvh = bg % g.Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, i = lane & 31;
+
+  const int row0 = tile * BM;
+  const int row = row0 + wave * 32 + i;
+  const bool valid = row < nrows;
+  const int rr = valid ? row : nrows - 1;
+  const int tok = rr / g.G;
+  const int head = kvh * g.G + rr % g.G;
+  const int pos = local_pos(tok, g.c, g.cp, g.rank);
+  const int32_t* ds = dstart + (size_t)b * g.Skv;
+  const int lo = ds[pos];
+
+  const size_t qoff = (((size_t)b * g.Sq + tok) * g.Hq + head) * D;
+  bf16x8 qop[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) qop[kk] = ld_bf16x8(q + qoff + 8 * h + 16 * kk);
+
+  const QTileKeys kr = qtile_keys<BM, BN>(row0, ds, g);
+
+  float m = -INFINITY, l = 0.f;
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = zero16();
+
+  const size_t kvstride = (size_t)g.Hkv * D;
+  const u16* kbase = k + (size_t)b * g.Skv * kvstride + (size_t)kvh * D;
+  const u16* vbase = v + (size_t)b * g.Skv * kvstride + (size_t)kvh * D;
+
+  for (int it = 0; it < kr.na + kr.nb; ++it) {
+    const int kt = it < kr.na ? kr.a0 + it : kr.b0 + (it - kr.na);
+    const int t0 = kt * BN;
+    __syncthreads();
+#pragma unroll
+    for (int x = threadIdx.x; x < BN * (D / 8); x += 256) {
+      const int rk = x / (D / 8), col = (x % (D / 8)) * 8;
+      const int src = min(t0 + rk, g.Skv - 1);
+      *reinterpret_cast<uint4*>(&sK[rk * LD + col]) =
+          *reinterpret_cast<const uint4*>(kbase + (size_t)src * kvstride + col);
+      *reinterpret_cast<uint4*>(&sV[rk * LD + col]) =
+          *reinterpret_cast<const uint4*>(vbase + (size_t)src * kvstride + col);
+    }
+    __syncthreads();
+
+    f32x16 s0 = zero16(), s1 = zero16();
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      s0 = mfma32(lds_bf16x8(&sK[i * LD + 8 * h + 16 * kk]), qop[kk], s0);
+      s1 = mfma32(lds_bf16x8(&sK[(32 + i) * LD + 8 * h + 16 * kk]), qop[kk], s1);
+    }
+    const bool full = kr.max_lo <= t0 && t0 + BN - 1 <= kr.min_pos;
+    if (!full) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kv = t0 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (kv < lo || kv > pos) s0[r] = -INFINITY;
+        if (kv + 32 < lo || kv + 32 > pos) s1[r] = -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    mx = fmaxf(mx, xor32(mx));
+    const float mnew = fmaxf(m, mx);
+    const float muse = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f((m - muse) * g.scale_log2);
+    const float msc = muse * g.scale_log2;
+    float rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], g.scale_log2, -msc));
+      s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], g.scale_log2, -msc));
+      rs += s0[r] + s1[r];
+    }
+    l = l * alpha + rs;
+    m = mnew;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+
+#pragma unroll
+    for (int ks = 0; ks < BN / 16; ++ks) {
+      const bf16x8 pop = pack_bf16(ks < 2 ? s0 : s1, ks & 1);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        o[db] = mfma32(tr_operand(sV, LD, ks, 32 * db, lane), pop, o[db]);
+    }
+  }
+
+  const float lt = l + xor32(l);
+  if (valid) {
+    const float inv = 1.f / lt;
+    u16* orow = out + qoff;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * r4 + e] * inv);
+        *reinterpret_cast<uint2*>(orow + 32 * db + 8 * r4 + 4 * h) = __builtin_bit_cast(uint2, w);
+      }
+    if (h == 0) lse[((size_t)b * g.Sq + tok) * g.Hq + head] = m * g.scale + logf(lt);
+  }
+}
+
+hipError_t launch_fwd(int D, const u16* q, const u16* k, const u16* v, const int32_t* dstart,
+                      u16* out, float* lse, const Geo& g, hipStream_t st) {
+  const int nt = (g.Sq * g.G + kFwdBM - 1) / kFwdBM;
+  const unsigned grid = (unsigned)nt * g.B * g.Hkv;
+  if (D == 128)
+    fwd_kernel<128><<<grid, 256, 0, st>>>(q, k, v, dstart, out, lse, g);
+  else
+    fwd_kernel<64><<<grid, 256, 0, st>>>(q, k, v, dstart, out, lse, g);
+  return hipGetLastError();
+}
+
+}  // namespace dmgqa

@@ -1,0 +1,58 @@
+// Tile sizes, workspace records and launcher declarations shared by the
+// kernels and the C-ABI entry points.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace dmgqa {
+
+// Forward and dQ kernels: 128 query rows (tokens x group heads) per
+// workgroup of 4 waves (32 rows per wave), 64 keys per step.
+constexpr int kFwdBM = 128;
+constexpr int kFwdBN = 64;
+// dK/dV kernel: 64 keys per work item (2 waves x 32), query rows streamed
+// 64 at a time (2 waves x 32).
+constexpr int kDkdvBN = 64;
+constexpr int kDkdvBM = 64;
+// Split of the query rows reaching one key tile into work items: at least
+// this many rows per item, and about kMaxSplitTotal split items per call.
+constexpr int kMinRowsPerSplit = 512;
+constexpr int kMaxSplitTotal = 1024;
+constexpr int kDkdvGrid = 512;  // persistent workgroups of the dK/dV kernel
+
+struct SchedHeader {
+  int n_base_items;    // work items per KV head
+  int rows_per_split;  // query rows per item
+  int n_slots_base;    // partial-sum slots per KV head
+  int counter;         // work counter of the persistent dK/dV kernel
+  int pad[12];
+};
+
+hipError_t launch_prep_docs(const int32_t* doc, int B, int S, int Skv, int32_t* dstart,
+                            int32_t* dend, int32_t* agg, hipStream_t st);
+hipError_t launch_prep_cu(const int32_t* cu, int n_docs, int Skv, int32_t* dstart, int32_t* dend,
+                          hipStream_t st);
+hipError_t launch_sched_dkdv(const int32_t* dend, const Geo& g, int nkt, int max_split_base,
+                             SchedHeader* hdr, int2* tile_info, int2* items, hipStream_t st);
+hipError_t launch_fwd(int D, const u16* q, const u16* k, const u16* v, const int32_t* dstart,
+                      u16* out, float* lse, const Geo& g, hipStream_t st);
+hipError_t launch_bwd_dq(int D, const u16* q, const u16* k, const u16* v, const u16* out,
+                         const u16* dout, const float* lse, const int32_t* dstart, u16* dq,
+                         float* Dbuf, const Geo& g, hipStream_t st);
+hipError_t launch_bwd_dkdv(int D, const u16* q, const u16* k, const u16* v, const u16* dout,
+                           const float* lse, const int32_t* dstart, const int32_t* dend,
+                           const float* Dbuf, SchedHeader* hdr, const int2* tile_info,
+                           const int2* items, float* partial, float* dk, float* dv, const Geo& g,
+                           int nkt, hipStream_t st);
+hipError_t launch_bwd_reduce(int D, const int2* tile_info, const float* partial, float* dk,
+                             float* dv, const Geo& g, int nkt, hipStream_t st);
+
+// Kernel timing (benchmark use): when enabled, each launch below is
+// bracketed by HIP events recorded on the launch stream.
+enum KernelId { kKPrep = 0, kKFwd, kKSched, kKDq, kKDkdv, kKReduce, kNumKernels };
+void timing_begin(int kernel, hipStream_t st);
+void timing_end(int kernel, hipStream_t st);
+
+}  // namespace dmgqa

@@ -1,0 +1,262 @@
+// Document bounds and the dK/dV work schedule.
+//
+// For every key position t < Skv of every batch row the prep kernels write
+//   dstart[t] = first position of t's document
+//   dend[t]   = one past the last position of t's document, capped at Skv.
+// With packed documents (each id one contiguous run) the document mask of
+// "Paper notes: The Llama 3 Herd of Models" ("Two architectural choices",
+// no attention across document boundaries) together with the causal mask
+// becomes an interval per query position p: keys dstart[p] .. p.  The
+// attention kernels read these arrays instead of comparing document ids.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dmgqa {
+
+constexpr int kScanThreads = 1024;
+
+// Inclusive block-wide scan with max (forward) of `v`.
+__device__ int block_scan_max(int v, int* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int u = __shfl_up(v, o);
+    if (lane >= o) v = max(v, u);
+  }
+  if (lane == 63) sh[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < (kScanThreads / 64) ? sh[lane] : INT32_MIN;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      int u = __shfl_up(w, o);
+      if (lane >= o) w = max(w, u);
+    }
+    if (lane < kScanThreads / 64) sh[16 + lane] = w;
+  }
+  __syncthreads();
+  if (wave > 0) v = max(v, sh[16 + wave - 1]);
+  __syncthreads();
+  return v;
+}
+
+// Inclusive block-wide suffix scan with min of `v` (from the last thread).
+__device__ int block_rscan_min(int v, int* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int u = __shfl_down(v, o);
+    if (lane + o < 64) v = min(v, u);
+  }
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < (kScanThreads / 64) ? sh[lane] : INT32_MAX;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      int u = __shfl_down(w, o);
+      if (lane + o < 16) w = min(w, u);
+    }
+    if (lane < kScanThreads / 64) sh[16 + lane] = w;
+  }
+  __syncthreads();
+  if (wave < kScanThreads / 64 - 1) v = min(v, sh[16 + wave + 1]);
+  __syncthreads();
+  return v;
+}
+
+// Pass 1: per 1024-position block, the latest document start at or before t
+// and the earliest document end after t, within the block; plus the block
+// aggregates.  grid = (nblk, B).
+__global__ __launch_bounds__(kScanThreads) void prep_scan_local(
+    const int32_t* __restrict__ doc, int S, int Skv, int nblk,
+    int32_t* __restrict__ dstart, int32_t* __restrict__ dend,
+    int32_t* __restrict__ agg_start, int32_t* __restrict__ agg_end) {
+  __shared__ int sh[32];
+  const int b = blockIdx.y;
+  const int t = blockIdx.x * kScanThreads + threadIdx.x;
+  const int32_t* d = doc + (size_t)b * S;
+  int vs = -1, ve = INT32_MAX;
+  if (t < Skv) {
+    const int cur = d[t];
+    if (t == 0 || d[t - 1] != cur) vs = t;
+    if (t == Skv - 1 || d[t + 1] != cur) ve = t + 1;
+  }
+  const int s = block_scan_max(vs, sh);
+  const int e = block_rscan_min(ve, sh);
+  if (t < Skv) {
+    dstart[(size_t)b * Skv + t] = s;
+    dend[(size_t)b * Skv + t] = e;
+  }
+  if (threadIdx.x == kScanThreads - 1) agg_start[b * nblk + blockIdx.x] = s;
+  if (threadIdx.x == 0) agg_end[b * nblk + blockIdx.x] = e;
+}
+
+// Pass 2: combine with the aggregates of the other blocks.
+__global__ __launch_bounds__(kScanThreads) void prep_scan_fix(
+    int Skv, int nblk, int32_t* __restrict__ dstart, int32_t* __restrict__ dend,
+    const int32_t* __restrict__ agg_start, const int32_t* __restrict__ agg_end) {
+  __shared__ int red[2][16];
+  const int b = blockIdx.y, blk = blockIdx.x;
+  int ps = -1, se = INT32_MAX;
+  for (int x = threadIdx.x; x < nblk; x += kScanThreads) {
+    if (x < blk) ps = max(ps, agg_start[b * nblk + x]);
+    if (x > blk) se = min(se, agg_end[b * nblk + x]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    ps = max(ps, __shfl_xor(ps, o));
+    se = min(se, __shfl_xor(se, o));
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) { red[0][wave] = ps; red[1][wave] = se; }
+  __syncthreads();
+  ps = -1; se = INT32_MAX;
+#pragma unroll
+  for (int w = 0; w < kScanThreads / 64; ++w) { ps = max(ps, red[0][w]); se = min(se, red[1][w]); }
+  const int t = blk * kScanThreads + threadIdx.x;
+  if (t < Skv) {
+    const size_t i = (size_t)b * Skv + t;
+    dstart[i] = max(dstart[i], ps);
+    dend[i] = min(dend[i], se);
+  }
+}
+
+// cu_seqlens form (B == 1): binary search of each position's document.
+__global__ __launch_bounds__(256) void prep_cu(const int32_t* __restrict__ cu, int n_docs,
+                                               int Skv, int32_t* __restrict__ dstart,
+                                               int32_t* __restrict__ dend) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= Skv) return;
+  int lo = 0, hi = n_docs - 1;  // find the last i with cu[i] <= t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  dstart[t] = cu[lo];
+  dend[t] = min(cu[lo + 1], Skv);
+}
+
+// Local token range(s) whose positions fall in [p0, p1): at most one range
+// in each of the rank's two chunks.
+__device__ __forceinline__ void token_ranges(int p0, int p1, const Geo& g, int& a0, int& na,
+                                             int& b0, int& nb) {
+  const int baseA = g.rank * g.c;
+  const int baseB = (2 * g.cp - 1 - g.rank) * g.c;
+  const int la = min(max(p0 - baseA, 0), g.c), ha = min(max(p1 - baseA, 0), g.c);
+  const int lb = min(max(p0 - baseB, 0), g.c), hb = min(max(p1 - baseB, 0), g.c);
+  a0 = la; na = max(0, ha - la);
+  b0 = g.c + lb; nb = max(0, hb - lb);
+}
+
+__device__ void dkdv_tile_tokens(const int32_t* dend_b, int kt, const Geo& g, int& a0, int& na,
+                                 int& b0, int& nb) {
+  const int t0 = kt * kDkdvBN;
+  const int tl = min(t0 + kDkdvBN - 1, g.Skv - 1);
+  const int pe = dend_b[tl];
+  token_ranges(t0, pe, g, a0, na, b0, nb);
+}
+
+// One block.  For every (batch, key tile): the number of query rows (local
+// tokens x group heads) that reach it; then a split of those rows into
+// pieces of `rows_per_split` (chosen so the total stays under kMaxSplitBase),
+// the work-item list and the partial-sum slots.
+__global__ __launch_bounds__(kScanThreads) void sched_dkdv(const int32_t* __restrict__ dend, Geo g,
+                                                           int nkt, int max_split_base,
+                                                           SchedHeader* __restrict__ hdr,
+                                                           int2* __restrict__ tile_info,
+                                                           int2* __restrict__ items) {
+  __shared__ int sh[32];
+  __shared__ long long red[16];
+  const int ntiles = g.B * nkt;
+  const int per = (ntiles + kScanThreads - 1) / kScanThreads;
+  const int first = threadIdx.x * per;
+  // 1. rows per tile and the total
+  long long tot = 0;
+  for (int x = first; x < min(first + per, ntiles); ++x) {
+    const int b = x / nkt, kt = x % nkt;
+    int a0, na, b0, nb;
+    dkdv_tile_tokens(dend + (size_t)b * g.Skv, kt, g, a0, na, b0, nb);
+    tot += (long long)(na + nb) * g.G;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = tot;
+  __syncthreads();
+  long long total = 0;
+  for (int w = 0; w < kScanThreads / 64; ++w) total += red[w];
+  long long rps = (total + max_split_base - 1) / max_split_base;
+  if (rps < kMinRowsPerSplit) rps = kMinRowsPerSplit;
+  rps = (rps + kDkdvBM - 1) / kDkdvBM * kDkdvBM;
+  // 2. splits per tile, prefix sums of items and of partial slots
+  int my_items = 0, my_slots = 0;
+  for (int x = first; x < min(first + per, ntiles); ++x) {
+    const int b = x / nkt, kt = x % nkt;
+    int a0, na, b0, nb;
+    dkdv_tile_tokens(dend + (size_t)b * g.Skv, kt, g, a0, na, b0, nb);
+    const long long rows = (long long)(na + nb) * g.G;
+    const int ns = rows == 0 ? 1 : (int)((rows + rps - 1) / rps);
+    my_items += ns;
+    my_slots += ns > 1 ? ns : 0;
+  }
+  // exclusive scans via the inclusive max-scan helper on prefix sums
+  __shared__ int scan_i[kScanThreads], scan_s[kScanThreads];
+  scan_i[threadIdx.x] = my_items;
+  scan_s[threadIdx.x] = my_slots;
+  __syncthreads();
+  for (int o = 1; o < kScanThreads; o <<= 1) {
+    int vi = threadIdx.x >= o ? scan_i[threadIdx.x - o] : 0;
+    int vs = threadIdx.x >= o ? scan_s[threadIdx.x - o] : 0;
+    __syncthreads();
+    scan_i[threadIdx.x] += vi;
+    scan_s[threadIdx.x] += vs;
+    __syncthreads();
+  }
+  int item = scan_i[threadIdx.x] - my_items;
+  int slot = scan_s[threadIdx.x] - my_slots;
+  for (int x = first; x < min(first + per, ntiles); ++x) {
+    const int b = x / nkt, kt = x % nkt;
+    int a0, na, b0, nb;
+    dkdv_tile_tokens(dend + (size_t)b * g.Skv, kt, g, a0, na, b0, nb);
+    const long long rows = (long long)(na + nb) * g.G;
+    const int ns = rows == 0 ? 1 : (int)((rows + rps - 1) / rps);
+    tile_info[x] = make_int2(ns, ns > 1 ? slot : -1);
+    for (int s = 0; s < ns; ++s) items[item + s] = make_int2(x, s);
+    item += ns;
+    slot += ns > 1 ? ns : 0;
+  }
+  if (threadIdx.x == kScanThreads - 1) {
+    hdr->n_base_items = scan_i[kScanThreads - 1];
+    hdr->rows_per_split = (int)rps;
+    hdr->n_slots_base = scan_s[kScanThreads - 1];
+    hdr->counter = 0;
+  }
+  (void)sh;
+}
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_prep_docs(const int32_t* doc, int B, int S, int Skv, int32_t* dstart,
+                            int32_t* dend, int32_t* agg, hipStream_t st) {
+  const int nblk = (Skv + kScanThreads - 1) / kScanThreads;
+  dim3 grid(nblk, B);
+  prep_scan_local<<<grid, kScanThreads, 0, st>>>(doc, S, Skv, nblk, dstart, dend, agg,
+                                                 agg + (size_t)B * nblk);
+  prep_scan_fix<<<grid, kScanThreads, 0, st>>>(Skv, nblk, dstart, dend, agg,
+                                               agg + (size_t)B * nblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_cu(const int32_t* cu, int n_docs, int Skv, int32_t* dstart, int32_t* dend,
+                          hipStream_t st) {
+  prep_cu<<<(Skv + 255) / 256, 256, 0, st>>>(cu, n_docs, Skv, dstart, dend);
+  return hipGetLastError();
+}
+
+hipError_t launch_sched_dkdv(const int32_t* dend, const Geo& g, int nkt, int max_split_base,
+                             SchedHeader* hdr, int2* tile_info, int2* items, hipStream_t st) {
+  sched_dkdv<<<1, kScanThreads, 0, st>>>(dend, g, nkt, max_split_base, hdr, tile_info, items);
+  return hipGetLastError();
+}
+
+}  // namespace dmgqa

@@ -1,0 +1,154 @@
+/*
+ * docmask_gqa.h -- document-masked causal grouped-query attention for one
+ * context-parallel (CP) rank, forward and backward, on AMD Instinct MI355X
+ * (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * The operation (from the pages this library follows):
+ *
+ *  - Context parallelism ("The Llama 3 Herd of Models", section 3.3.2,
+ *    "Context parallelism for long sequences"): the sequence of S tokens is
+ *    cut into 2*cp_size equal chunks of c = S/(2*cp_size) tokens; rank i holds
+ *    chunk i and chunk 2*cp_size-1-i.  K and V of the whole sequence are
+ *    all-gathered first and attention is computed for the rank's local
+ *    queries.  Here the gathered K/V are already in device memory.
+ *  - Document mask ("Paper notes: The Llama 3 Herd of Models", "Two
+ *    architectural choices"): a token never attends across a document
+ *    boundary.  With the causal mask of a decoder, key position t is allowed
+ *    for query position p iff t <= p and doc(t) == doc(p).
+ *  - GQA (same sections): query head h uses KV head h / (Hq/Hkv).
+ *  - Attention ("Training Infrastructure and Systems", "FlashAttention: never
+ *    write the score matrix"): out = softmax(scale * Q K^T) V over the allowed
+ *    keys, computed tile by tile with an online softmax; only out and one
+ *    per-row statistic are written.  The statistic is
+ *    lse = ln(sum over allowed t of exp(scale * <q, k_t>)), natural log.
+ *  - Backward: the scores are recomputed; dq, dk, dv follow the chain rule of
+ *    softmax attention.  dk and dv are summed over the Hq/Hkv query heads of
+ *    each KV head and returned in fp32 (the pages accumulate gradients in
+ *    FP32, Herd section 3.3.2, "Numerical stability").
+ *
+ * Local row layout.  q, out, dout, dq hold Sq = 2*c rows per batch entry:
+ * rows 0..c-1 are chunk cp_rank (global positions cp_rank*c + j), rows
+ * c..2c-1 are chunk 2*cp_size-1-cp_rank, both in ascending position order.
+ *
+ * Tensor layouts (all contiguous, row-major, device memory):
+ *   q, out, dout, dq : bf16  [B, Sq, Hq, D]
+ *   k, v             : bf16  [B, Skv, Hkv, D]  global sequence order 0..Skv-1
+ *   dk, dv           : fp32  [B, Skv, Hkv, D]
+ *   lse              : fp32  [B, Sq, Hq]
+ *   doc_ids          : int32 [B, S]   per-token document id
+ *   cu_seqlens       : int32 [n_docs+1] document offsets 0 = cu[0] < ... <
+ *                      cu[n_docs] = S (B == 1 only)
+ * bf16 tensors must be 16-byte aligned; fp32 and int32 tensors 4-byte aligned.
+ *
+ * Preconditions that are not checked by the calls (see
+ * docmask_gqa_check_docs for a synchronous debug check): equal document ids
+ * form one contiguous run of positions; cu_seqlens is strictly increasing.
+ * |dout| must be finite.
+ *
+ * Ownership.  The caller allocates and frees every buffer, including the
+ * workspace (size from the *_workspace_size queries).  The library allocates
+ * no device memory and keeps no state between calls; calls are asynchronous
+ * on `stream` (a hipStream_t; NULL = the default stream) and re-entrant when
+ * different calls use different workspaces.  Every element of out, lse, dq,
+ * dk and dv is written, including zeros for dk/dv rows that no local query
+ * reaches.  The workspace contents are not needed after a call returns.
+ *
+ * Errors.  Every function returns 0 on success or a negative status.  All
+ * argument checks happen before any HIP call, so a rejected call touches no
+ * memory.  Device-side faults surface at the caller's next synchronisation.
+ */
+#ifndef DOCMASK_GQA_H
+#define DOCMASK_GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DMGQA_OK = 0,
+  DMGQA_ERR_INVALID_ARG = -1,  /* null pointer, misalignment, bad rank,
+                                  S % (2*cp_size) != 0, Hq % Hkv != 0, Skv
+                                  outside [(2*cp_size-cp_rank)*c, S], both or
+                                  neither of doc_ids / cu_seqlens, non-finite
+                                  or zero softmax_scale, negative sizes */
+  DMGQA_ERR_UNSUPPORTED = -2,  /* D not in {64, 128}; cu_seqlens with B > 1;
+                                  sizes whose element offsets overflow */
+  DMGQA_ERR_WORKSPACE = -3,    /* workspace_bytes below the required size */
+  DMGQA_ERR_HIP = -4           /* a HIP launch or runtime call failed */
+};
+
+/* Bytes of workspace the forward call needs.  Depends only on the sizes;
+ * 0 when there is nothing to compute. */
+size_t docmask_gqa_fwd_workspace_size(int32_t B, int32_t S, int32_t Skv,
+                                      int32_t Hq, int32_t Hkv, int32_t D,
+                                      int32_t cp_size);
+
+/* Bytes of workspace the backward call needs. */
+size_t docmask_gqa_bwd_workspace_size(int32_t B, int32_t S, int32_t Skv,
+                                      int32_t Hq, int32_t Hkv, int32_t D,
+                                      int32_t cp_size);
+
+/* Forward: out = softmax(scale * q k^T, masked) v and lse for the rank's
+ * local rows.  Exactly one of doc_ids / cu_seqlens is non-NULL; n_docs is
+ * read only with cu_seqlens.  softmax_scale is normally 1/sqrt(D). */
+int docmask_gqa_attn_fwd(const void* q, const void* k, const void* v,
+                         const int32_t* doc_ids, const int32_t* cu_seqlens,
+                         int32_t n_docs, int32_t B, int32_t S, int32_t Skv,
+                         int32_t Hq, int32_t Hkv, int32_t D, int32_t cp_size,
+                         int32_t cp_rank, float softmax_scale, void* out,
+                         float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Backward: given the forward's out and lse and the output gradient dout,
+ * writes dq (bf16), dk and dv (fp32, summed over each KV head's query
+ * heads).  Same masking arguments as the forward. */
+int docmask_gqa_attn_bwd(const void* q, const void* k, const void* v,
+                         const void* out, const void* dout, const float* lse,
+                         const int32_t* doc_ids, const int32_t* cu_seqlens,
+                         int32_t n_docs, int32_t B, int32_t S, int32_t Skv,
+                         int32_t Hq, int32_t Hkv, int32_t D, int32_t cp_size,
+                         int32_t cp_rank, float softmax_scale, void* dq,
+                         float* dk, float* dv, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Debug check of the document-id precondition.  Copies doc_ids [B, S] to the
+ * host, synchronising `stream`.  Returns 0 if every id forms one contiguous
+ * run in each batch row, 1 if some id reappears after a different id,
+ * or a negative status. */
+int docmask_gqa_check_docs(const int32_t* doc_ids, int32_t B, int32_t S,
+                           void* stream);
+
+/* Debug check of cu_seqlens [n_docs+1] (synchronises `stream`).  Returns 0
+ * if cu[0] == 0, cu[n_docs] == S and the offsets strictly increase, 1
+ * otherwise, or a negative status. */
+int docmask_gqa_check_cu_seqlens(const int32_t* cu_seqlens, int32_t n_docs,
+                                 int32_t S, void* stream);
+
+/* Kernel timing, for benchmarks.  docmask_gqa_timing_enable(1) clears the
+ * records and makes every later kernel launch of the library record a HIP
+ * event before and after it on the call's stream (events are created on
+ * first use and kept until the process ends); enable(0) stops recording.
+ * docmask_gqa_timing_read(kernel, &ms, &n) waits for the recorded events and
+ * returns the summed duration and launch count of one kernel since the last
+ * enable.  Kernel ids are 0 .. docmask_gqa_kernel_count()-1 with names from
+ * docmask_gqa_kernel_name().  Not thread-safe with concurrent calls that
+ * also record. */
+int docmask_gqa_timing_enable(int on);
+int docmask_gqa_timing_read(int kernel, double* total_ms, int* launches);
+int docmask_gqa_kernel_count(void);
+const char* docmask_gqa_kernel_name(int kernel);
+
+/* Static description of a status code. */
+const char* docmask_gqa_status_string(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int docmask_gqa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DOCMASK_GQA_H */

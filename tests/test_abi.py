@@ -1,0 +1,150 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and rejects bad arguments with the documented status before any
+HIP call (so none of these calls needs a GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import context_gqa_amd as M
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "docmask_gqa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(docmask_gqa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert "docmask_gqa_attn_fwd" in names and "docmask_gqa_attn_bwd" in names
+    lib = M.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in M.SIGNATURES, n
+    assert set(M.SIGNATURES) == set(names)
+
+
+def test_status_strings():
+    assert M.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4):
+        assert M.status_string(s) not in ("ok", "unknown status")
+    assert M.status_string(-99) == "unknown status"
+
+
+def test_workspace_sizes():
+    f = M.docmask_gqa_fwd_workspace_size
+    b = M.docmask_gqa_bwd_workspace_size
+    assert f(1, 8192, 8192, 16, 1, 128, 1) > 0
+    assert b(1, 8192, 8192, 16, 1, 128, 1) > f(1, 8192, 8192, 16, 1, 128, 1)
+    assert f(0, 8192, 8192, 16, 1, 128, 1) == 0          # empty batch
+    assert f(1, 8190, 8190, 16, 1, 128, 4) == 0          # S % (2*cp) != 0 -> invalid -> 0
+    assert f(1, 8192, 8192, 16, 3, 128, 1) == 0          # Hq % Hkv != 0
+    assert f(1, 8192, 8192, 16, 1, 96, 1) == 0           # unsupported D
+    # independent of the document layout, monotone in the key length
+    assert f(1, 131072, 102400, 16, 1, 128, 16) <= f(1, 131072, 131072, 16, 1, 128, 16)
+
+
+class _Buf:
+    """16-byte aligned host memory standing in for device pointers: every call
+    below is rejected before any pointer is dereferenced."""
+
+    def __init__(self, n=4096):
+        self.raw = ctypes.create_string_buffer(n + 16)
+        a = ctypes.addressof(self.raw)
+        self.p = a + (-a) % 16
+
+
+def _fwd(**kw):
+    b = _Buf()
+    args = dict(q=b.p, k=b.p, v=b.p, doc=b.p, cu=None, n_docs=0, B=1, S=512, Skv=512, Hq=4,
+                Hkv=1, D=64, cp=1, rank=0, scale=0.125, out=b.p, lse=b.p, ws=b.p, wsb=0)
+    args.update(kw)
+    a = args
+    return M.lib().docmask_gqa_attn_fwd(a["q"], a["k"], a["v"], a["doc"], a["cu"], a["n_docs"],
+                                        a["B"], a["S"], a["Skv"], a["Hq"], a["Hkv"], a["D"],
+                                        a["cp"], a["rank"], a["scale"], a["out"], a["lse"],
+                                        a["ws"], a["wsb"], None)
+
+
+def _bwd(**kw):
+    b = _Buf()
+    a = dict(q=b.p, k=b.p, v=b.p, out=b.p, dout=b.p, lse=b.p, doc=b.p, cu=None, n_docs=0, B=1,
+             S=512, Skv=512, Hq=4, Hkv=1, D=64, cp=1, rank=0, scale=0.125, dq=b.p, dk=b.p,
+             dv=b.p, ws=b.p, wsb=0)
+    a.update(kw)
+    return M.lib().docmask_gqa_attn_bwd(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"],
+                                        a["doc"], a["cu"], a["n_docs"], a["B"], a["S"], a["Skv"],
+                                        a["Hq"], a["Hkv"], a["D"], a["cp"], a["rank"], a["scale"],
+                                        a["dq"], a["dk"], a["dv"], a["ws"], a["wsb"], None)
+
+
+INV, UNS, WS = M.DMGQA_ERR_INVALID_ARG, M.DMGQA_ERR_UNSUPPORTED, M.DMGQA_ERR_WORKSPACE
+
+CASES = [
+    (dict(q=None), INV),
+    (dict(lse=None), INV),
+    (dict(ws=None), INV),
+    (dict(rank=1), INV),                       # rank >= cp_size
+    (dict(rank=-1), INV),
+    (dict(cp=0), INV),
+    (dict(S=500, Skv=500, cp=3), INV),          # S % (2*cp) != 0
+    (dict(Hq=6, Hkv=4), INV),                   # Hq % Hkv != 0
+    (dict(Skv=511), INV),                       # below the needed prefix
+    (dict(Skv=513), INV),                       # beyond S
+    (dict(S=512, Skv=383, cp=4, rank=1), INV),  # prefix (8-1)*64 = 448 needed
+    (dict(doc=None), INV),                      # neither doc_ids nor cu_seqlens
+    (dict(cu="same"), INV),                     # both
+    (dict(D=96), UNS),
+    (dict(D=256), UNS),
+    (dict(doc=None, cu="same", B=2, n_docs=3), UNS),   # cu_seqlens with B > 1
+    (dict(doc=None, cu="same", n_docs=0), INV),
+    (dict(scale=float("nan")), INV),
+    (dict(scale=float("inf")), INV),
+    (dict(scale=0.0), INV),
+    (dict(B=-1), INV),
+    (dict(wsb=0), WS),                          # all valid but workspace too small
+]
+
+
+@pytest.mark.parametrize("kw,want", CASES, ids=[str(c[0]) for c in CASES])
+def test_fwd_rejects(kw, want):
+    b = _Buf()
+    kw = {k: (b.p if v == "same" else v) for k, v in kw.items()}
+    assert _fwd(**kw) == want
+
+
+@pytest.mark.parametrize("kw,want", CASES + [(dict(dout=None), INV), (dict(dk=None), INV)],
+                         ids=[str(c[0]) for c in CASES] + ["dout=None", "dk=None"])
+def test_bwd_rejects(kw, want):
+    b = _Buf()
+    kw = {k: (b.p if v == "same" else v) for k, v in kw.items()}
+    assert _bwd(**kw) == want
+
+
+def test_misaligned_pointer_rejected():
+    b = _Buf()
+    assert _fwd(q=b.p + 2) == INV
+    assert _bwd(dq=b.p + 8) == INV
+
+
+def test_empty_is_noop():
+    # nothing to compute: success without touching any pointer
+    assert _fwd(B=0, q=None, k=None, v=None, out=None, lse=None, ws=None) == 0
+    assert _fwd(S=0, Skv=0, q=None, k=None, v=None, out=None, lse=None, ws=None) == 0
+    assert _bwd(B=0, q=None, dq=None, dk=None, dv=None, ws=None) == 0
+
+
+def test_binding_requires_device_tensors():
+    import torch
+    q = torch.zeros(1, 512, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 512, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        M.docmask_gqa_attn_fwd(q, k, k, doc_ids=torch.zeros(1, 512, dtype=torch.int32),
+                               cp_size=1, cp_rank=0)
+    with pytest.raises(TypeError):
+        M.docmask_gqa_attn_fwd(q.float(), k, k, doc_ids=torch.zeros(1, 512, dtype=torch.int32),
+                               cp_size=1, cp_rank=0)

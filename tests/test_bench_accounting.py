@@ -1,0 +1,49 @@
+"""bench.py's FLOP accounting against the oracle's explicit mask."""
+import numpy as np
+import pytest
+
+import bench
+import oracle
+import workloads as W
+
+
+@pytest.mark.parametrize("name,seed", [("tiny", 0), ("tiny", 3), ("tp405b", 0), ("short_docs", 1)])
+def test_allowed_pairs_matches_explicit_mask(name, seed):
+    cfg = W.CONFIGS[name]
+    L = W.doc_lengths(cfg.doc_kind, cfg.S, seed)
+    doc = W.doc_ids_from_lengths(L)[None]
+    for r in cfg.ranks[:2]:
+        Skv = W.kv_prefix_len(cfg.S, cfg.cp_size, r)
+        want = int(oracle.allowed_counts(doc, cfg.cp_size, r, Skv).sum())
+        assert bench.allowed_pairs(L, cfg.S, cfg.cp_size, r) == want
+
+
+def test_single_doc_pairs_closed_form():
+    S, cp = 32768, 4
+    for r in range(cp):
+        assert bench.allowed_pairs([S], S, cp, r) == 134_221_824
+
+
+def test_seed0_useful_gflop():
+    """Seed-0 useful work of the 405B TP-share workload: 5,359,333 pairs per
+    head x 16 heads x 12 x 128 flops = 131.7 GFLOP."""
+    cfg = W.CONFIGS["tp405b"]
+    L = W.doc_lengths(cfg.doc_kind, cfg.S, 0)
+    p = bench.allowed_pairs(L, cfg.S, 1, 0)
+    assert p == 5_359_333
+    f = bench.useful_flops(p, 16, 128, True)
+    assert abs(f["total"] / 1e9 - 131.7) < 0.05
+    assert f["fwd"] + f["bwd_dq"] + f["bwd_dkdv"] == f["total"]
+
+
+def test_score_matrix_bytes_example():
+    """The pages' example of the score-matrix size that tiling avoids:
+    32 heads x 8192^2 x 2 bytes = 4.3 GB."""
+    import json, os
+    facts = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_facts.json")))
+    f = facts["score_matrix_bytes"]
+    assert round(f["heads"] * f["L"] ** 2 * f["bytes_per_elem"] / 1e9, 1) == f["bytes_rounded_GB"]
+
+
+def test_multi_gpu_request_exits():
+    assert bench.main(["--gpus", "2"]) == 2

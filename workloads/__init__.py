@@ -177,12 +177,12 @@ class Case:
 
 
 def make_case(cfg: Config, seed: int, rank: int, Skv: Optional[int] = None,
-              full=None) -> Case:
+              full=None, lengths: Optional[List[List[int]]] = None) -> Case:
     """Everything one rank's attention call receives.  `full` may pass
     tensors already drawn by full_tensors(cfg, seed) to share them between
-    ranks."""
-    lengths = [doc_lengths(cfg.doc_kind, cfg.S, seed + 1000 * b) if b else
-               doc_lengths(cfg.doc_kind, cfg.S, seed) for b in range(cfg.B)]
+    ranks; `lengths` may fix the document lengths of each batch row."""
+    if lengths is None:
+        lengths = [doc_lengths(cfg.doc_kind, cfg.S, seed + 1000 * b) for b in range(cfg.B)]
     doc_ids = np.stack([doc_ids_from_lengths(l) for l in lengths])
     cu = cu_seqlens_from_lengths(lengths[0]) if cfg.B == 1 else None
     q, k, v, dout = full if full is not None else full_tensors(cfg, seed)
