@@ -41,6 +41,10 @@ int check_shape(int B, int S, int Skv, int Hq, int Hkv, int D, int cp, int rank,
   if (Sq * G >= (1LL << 30) || (long long)Skv * 2 >= (1LL << 31)) return DMGQA_ERR_UNSUPPORTED;
   const long long tiles = (Sq * G + kFwdBM - 1) / kFwdBM * (long long)B * Hkv;
   if (tiles >= (1LL << 31)) return DMGQA_ERR_UNSUPPORTED;
+  // element offsets inside q/out/dout/dq and k/v/dk/dv are 32-bit
+  if ((long long)B * Sq * Hq * D >= (1LL << 31) || (long long)B * Skv * Hkv * D >= (1LL << 31) ||
+      G >= (1 << 16))
+    return DMGQA_ERR_UNSUPPORTED;
   sh->B = B; sh->S = S; sh->Skv = Skv; sh->Hq = Hq; sh->Hkv = Hkv; sh->D = D;
   sh->cp = cp; sh->rank = rank; sh->G = G; sh->c = c; sh->Sq = (int)Sq;
   sh->empty = (B == 0 || S == 0);
@@ -92,6 +96,10 @@ Geo make_geo(const Shape& s, float scale) {
   Geo g;
   g.B = s.B; g.S = s.S; g.Skv = s.Skv; g.Hq = s.Hq; g.Hkv = s.Hkv; g.G = s.G;
   g.Sq = s.Sq; g.c = s.c; g.cp = s.cp; g.rank = s.rank;
+  g.g_magic = s.G >= 2 ? (unsigned)((((uint64_t)1 << 32) + (uint64_t)s.G - 1) / (uint64_t)s.G) : 0u;
+  g.g_log2 = -1;
+  for (int e = 0; e < 31; ++e)
+    if ((1 << e) == s.G) g.g_log2 = e;
   g.scale = scale;
   g.scale_log2 = scale * kLog2e;
   return g;

@@ -26,6 +26,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "qtile.hpp"
+#include "tileload.hpp"
 
 namespace dmgqa {
 
@@ -34,9 +35,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ out, const u16* __restrict__ dout, const float* __restrict__ lse,
     const int32_t* __restrict__ dstart, u16* __restrict__ dq, float* __restrict__ Dbuf, Geo g) {
-  constexpr int BM = kFwdBM, BN = kFwdBN, LD = D + 8, KK = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) u16 sK[BN * LD];
-  __shared__ __attribute__((aligned(16))) u16 sV[BN * LD];
+  constexpr int BM = kFwdBM, BN = kFwdBN, LD = D, KK = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(16))) u16 sK[2][BN * LD];
+  __shared__ __attribute__((aligned(16))) u16 sV[2][BN * LD];
 
   const int nrows = g.Sq * g.G;
   const int nt = (nrows + BM - 1) / BM;
@@ -74,6 +75,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const float lse2 = lse[roff] * kLog2e;
 
   const QTileKeys kr = qtile_keys<BM, BN>(row0, ds, g);
+  const int ntiles = kr.na + kr.nb;
 
   f32x16 acc[DB];
 #pragma unroll
@@ -82,50 +84,56 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const size_t kvstride = (size_t)g.Hkv * D;
   const u16* kbase = k + (size_t)b * g.Skv * kvstride + (size_t)kvh * D;
   const u16* vbase = v + (size_t)b * g.Skv * kvstride + (size_t)kvh * D;
+  TileRegs<BN, D, 256> rk, rv;
+  auto fetch = [&](int it) __attribute__((always_inline)) {
+    const int t0 = (it < kr.na ? kr.a0 + it : kr.b0 + (it - kr.na)) * BN;
+    rk.load([&](int r) { return kbase + (size_t)min(t0 + r, g.Skv - 1) * kvstride; });
+    rv.load([&](int r) { return vbase + (size_t)min(t0 + r, g.Skv - 1) * kvstride; });
+  };
+  fetch(0);
+  rk.store(sK[0]);
+  rv.store(sV[0]);
+  __syncthreads();
 
-  for (int it = 0; it < kr.na + kr.nb; ++it) {
-    const int kt = it < kr.na ? kr.a0 + it : kr.b0 + (it - kr.na);
-    const int t0 = kt * BN;
-    __syncthreads();
-#pragma unroll
-    for (int x = threadIdx.x; x < BN * (D / 8); x += 256) {
-      const int rk = x / (D / 8), col = (x % (D / 8)) * 8;
-      const int src = min(t0 + rk, g.Skv - 1);
-      *reinterpret_cast<uint4*>(&sK[rk * LD + col]) =
-          *reinterpret_cast<const uint4*>(kbase + (size_t)src * kvstride + col);
-      *reinterpret_cast<uint4*>(&sV[rk * LD + col]) =
-          *reinterpret_cast<const uint4*>(vbase + (size_t)src * kvstride + col);
-    }
-    __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int t0 = (it < kr.na ? kr.a0 + it : kr.b0 + (it - kr.na)) * BN;
+    const int cur = it & 1;
+    if (it + 1 < ntiles) fetch(it + 1);
+    const u16* cK = sK[cur];
+    const u16* cV = sV[cur];
 
-    f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      s0 = mfma32(lds_bf16x8(&sK[i * LD + 8 * h + 16 * kk]), qop[kk], s0);
-      s1 = mfma32(lds_bf16x8(&sK[(32 + i) * LD + 8 * h + 16 * kk]), qop[kk], s1);
-      p0 = mfma32(lds_bf16x8(&sV[i * LD + 8 * h + 16 * kk]), dop[kk], p0);
-      p1 = mfma32(lds_bf16x8(&sV[(32 + i) * LD + 8 * h + 16 * kk]), dop[kk], p1);
-    }
     const bool full = kr.max_lo <= t0 && t0 + BN - 1 <= kr.min_pos;
+    // two 32-key halves, to keep the score/dP accumulators at 32 registers
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float e0 = __builtin_amdgcn_exp2f(fmaf(s0[r], g.scale_log2, -lse2));
-      float e1 = __builtin_amdgcn_exp2f(fmaf(s1[r], g.scale_log2, -lse2));
-      if (!full) {
-        const int kv = t0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (kv < lo || kv > pos) e0 = 0.f;
-        if (kv + 32 < lo || kv + 32 > pos) e1 = 0.f;
+    for (int half = 0; half < 2; ++half) {
+      f32x16 s0 = zero16(), p0 = zero16();
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        s0 = mfma32(lds_bf16x8(&cK[swz<D>(32 * half + i, 8 * h + 16 * kk)]), qop[kk], s0);
+        p0 = mfma32(lds_bf16x8(&cV[swz<D>(32 * half + i, 8 * h + 16 * kk)]), dop[kk], p0);
       }
-      s0[r] = e0 * (p0[r] - Dv);
-      s1[r] = e1 * (p1[r] - Dv);
-    }
 #pragma unroll
-    for (int ks = 0; ks < BN / 16; ++ks) {
-      const bf16x8 dsop = pack_bf16(ks < 2 ? s0 : s1, ks & 1);
+      for (int r = 0; r < 16; ++r) {
+        float e0 = __builtin_amdgcn_exp2f(fmaf(s0[r], g.scale_log2, -lse2));
+        if (!full) {
+          const int kv = t0 + 32 * half + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (kv < lo || kv > pos) e0 = 0.f;
+        }
+        s0[r] = e0 * (p0[r] - Dv);
+      }
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        acc[db] = mfma32(tr_operand(sK, LD, ks, 32 * db, lane), dsop, acc[db]);
+      for (int kh = 0; kh < 2; ++kh) {
+        const bf16x8 dsop = pack_bf16(s0, kh);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          acc[db] = mfma32(tr_operand<D>(cK, 0, 2 * half + kh, 32 * db, lane), dsop, acc[db]);
+      }
     }
+    if (it + 1 < ntiles) {
+      rk.store(sK[cur ^ 1]);
+      rv.store(sV[cur ^ 1]);
+    }
+    __syncthreads();
   }
 
   if (valid) {
@@ -166,21 +174,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int2* __restrict__ tile_info, const int2* __restrict__ items,
     float* __restrict__ partial, float* __restrict__ dk, float* __restrict__ dv, Geo g,
     int nkt) {
-  constexpr int BN = kDkdvBN, BM = kDkdvBM, LD = D + 8, KK = D / 16, DB = D / 32;
-  constexpr int kQBytes = 2 * BM * LD * 2;           // sQ + sdO
-  constexpr int kRedBytes = 2 * 32 * D * 4;          // two waves' accumulator
-  constexpr int kSmem = kQBytes > kRedBytes ? kQBytes : kRedBytes;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
-  __shared__ int s_pos[BM], s_lo[BM];
-  __shared__ float s_lse2[BM], s_D[BM];
+  // Work item: 128 keys (wave w owns keys t0 + 32w .. t0 + 32w + 31) x one
+  // slice of the query rows reaching them.  Query rows stream through two LDS
+  // stages in blocks of BM = 64 (every wave uses every row, as two sub-blocks
+  // of 32); the global loads of block n+1 are issued before block n is
+  // computed and written to the other stage after it.
+  constexpr int BN = kDkdvBN, BM = kDkdvBM, KK = D / 16, DB = D / 32;
+  constexpr int kTile = BM * D;                     // elements of one Q or dO block
+  __shared__ __attribute__((aligned(16))) u16 sQ[2][kTile];
+  __shared__ __attribute__((aligned(16))) u16 sdO[2][kTile];
+  __shared__ __attribute__((aligned(16))) float s_lse2[2][BM];
+  __shared__ __attribute__((aligned(16))) float s_D[2][BM];
+  __shared__ __attribute__((aligned(16))) int s_lo[2][BM];
+  __shared__ __attribute__((aligned(16))) int s_pos[2][BM];
   __shared__ int s_item;
-  u16* sQ = reinterpret_cast<u16*>(smem);
-  u16* sdO = sQ + BM * LD;
-  float* sRed = reinterpret_cast<float*>(smem);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, i = lane & 31;
-  const int kvhalf = wave & 1, qhalf = wave >> 1;
   const int total = hdr->n_base_items * g.Hkv;
   const int rps = hdr->rows_per_split;
   const size_t kvstride = (size_t)g.Hkv * D;
@@ -188,7 +198,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   for (;;) {
     if (threadIdx.x == 0) s_item = atomicAdd(&hdr->counter, 1);
     __syncthreads();
-    const int it = s_item;
+    const int it = uniform(s_item);
+    __syncthreads();
     if (it >= total) break;
     const int base = it / g.Hkv, kvh = it % g.Hkv;
     const int2 itm = items[base];
@@ -201,8 +212,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int rows_total = (na + nb) * g.G;
     const int r_begin = split * rps;
     const int r_end = min(r_begin + rps, rows_total);
+    const int nblk = r_end > r_begin ? (r_end - r_begin + BM - 1) / BM : 0;
 
-    const int kv_l = t0 + kvhalf * 32 + i;
+    const int kv_l = t0 + wave * 32 + i;
     const int kv_c = min(kv_l, g.Skv - 1);
     const u16* krow = k + ((size_t)b * g.Skv + kv_c) * kvstride + (size_t)kvh * D;
     const u16* vrow = v + ((size_t)b * g.Skv + kv_c) * kvstride + (size_t)kvh * D;
@@ -216,76 +228,122 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
     for (int db = 0; db < DB; ++db) { dka[db] = zero16(); dva[db] = zero16(); }
 
-    for (int vr0 = r_begin; vr0 < r_end; vr0 += BM) {
-      __syncthreads();
-      for (int xx = threadIdx.x; xx < BM * (D / 8); xx += 256) {
-        const int rq = xx / (D / 8), col = (xx % (D / 8)) * 8;
-        const int vr = min(vr0 + rq, r_end - 1);
-        const int ti = vr / g.G;
+    // Query rows of a block: virtual row vr0 + r (r < BM) is head-in-group
+    // (hh0 + r) % G of token index ti0 + (hh0 + r) / G of the reaching
+    // token run; vr0, ti0, hh0 are uniform.  Offsets are 32-bit (checked on
+    // the host).
+    TileRegs<BM, D, 256> rq, rdo;
+    float m_lse2 = 0.f, m_D = 0.f;
+    int m_lo = 0, m_pos = -1;
+    auto fetch = [&](int blk) __attribute__((always_inline)) {
+      const int vr0 = r_begin + blk * BM;
+      const int ti0 = vr0 / g.G, hh0 = vr0 - ti0 * g.G;
+      const int nrow = r_end - vr0;   // rows of this block that exist
+      auto row_of = [&](int r) __attribute__((always_inline)) -> unsigned {
+        const int t = hh0 + min(r, nrow - 1);
+        const int qd = div_small(t, g);
+        const int ti = ti0 + qd;
         const int tok = ti < na ? a0 + ti : b0 + (ti - na);
-        const int head = kvh * g.G + vr % g.G;
-        const size_t off = (((size_t)b * g.Sq + tok) * g.Hq + head) * D + col;
-        *reinterpret_cast<uint4*>(&sQ[rq * LD + col]) = *reinterpret_cast<const uint4*>(q + off);
-        *reinterpret_cast<uint4*>(&sdO[rq * LD + col]) = *reinterpret_cast<const uint4*>(dout + off);
-      }
+        return (unsigned)((b * g.Sq + tok) * g.Hq + kvh * g.G + (t - qd * g.G));
+      };
+      rq.load([&](int r) { return q + row_of(r) * (unsigned)D; });
+      rdo.load([&](int r) { return dout + row_of(r) * (unsigned)D; });
       if (threadIdx.x < BM) {
-        const int vr = vr0 + threadIdx.x;
-        const bool ok = vr < r_end;
-        const int vc = ok ? vr : r_end - 1;
-        const int ti = vc / g.G;
+        const int r = threadIdx.x;
+        const bool ok = r < nrow;
+        const int t = hh0 + min(r, nrow - 1);
+        const int qd = div_small(t, g);
+        const int ti = ti0 + qd;
         const int tok = ti < na ? a0 + ti : b0 + (ti - na);
-        const int head = kvh * g.G + vc % g.G;
         const int p = local_pos(tok, g.c, g.cp, g.rank);
-        const size_t roff = ((size_t)b * g.Sq + tok) * g.Hq + head;
-        s_pos[threadIdx.x] = ok ? p : -1;
-        s_lo[threadIdx.x] = ok ? ds[p] : 0;
-        s_lse2[threadIdx.x] = lse[roff] * kLog2e;
-        s_D[threadIdx.x] = Dbuf[roff];
+        const unsigned ro = (unsigned)((b * g.Sq + tok) * g.Hq + kvh * g.G + (t - qd * g.G));
+        m_pos = ok ? p : -1;
+        m_lo = ok ? ds[p] : 0;
+        m_lse2 = lse[ro] * kLog2e;
+        m_D = Dbuf[ro];
       }
-      __syncthreads();
-      const bool full =
-          vr0 + BM <= r_end && s_lo[BM - 1] <= t0 && t0 + BN - 1 <= s_pos[0];
+    };
+    auto stash = [&](int st) __attribute__((always_inline)) {
+      rq.store(sQ[st]);
+      rdo.store(sdO[st]);
+      if (threadIdx.x < BM) {
+        s_pos[st][threadIdx.x] = m_pos;
+        s_lo[st][threadIdx.x] = m_lo;
+        s_lse2[st][threadIdx.x] = m_lse2;
+        s_D[st][threadIdx.x] = m_D;
+      }
+    };
+    if (nblk > 0) {
+      fetch(0);
+      stash(0);
+    }
+    __syncthreads();
 
-      f32x16 s = zero16(), dp = zero16();
-      const u16* qa = sQ + (qhalf * 32 + i) * LD + 8 * h;
-      const u16* da = sdO + (qhalf * 32 + i) * LD + 8 * h;
+    for (int blk = 0; blk < nblk; ++blk) {
+      const int st = blk & 1;
+      const int vr0 = r_begin + blk * BM;
+      if (blk + 1 < nblk) fetch(blk + 1);
+      const u16* cQ = sQ[st];
+      const u16* cdO = sdO[st];
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        s = mfma32(lds_bf16x8(qa + 16 * kk), kop[kk], s);
-        dp = mfma32(lds_bf16x8(da + 16 * kk), vop[kk], dp);
-      }
+      for (int sb = 0; sb < BM / 32; ++sb) {
+        const int q0 = 32 * sb;
+        const bool full = vr0 + q0 + 32 <= r_end && s_lo[st][q0 + 31] <= t0 &&
+                          t0 + BN - 1 <= s_pos[st][q0];
+        f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = qhalf * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        float p = __builtin_amdgcn_exp2f(fmaf(s[r], g.scale_log2, -s_lse2[qr]));
-        if (!full && (kv_l < s_lo[qr] || kv_l > s_pos[qr])) p = 0.f;
-        s[r] = p;
-        dp[r] = p * (dp[r] - s_D[qr]);
-      }
-      const u16* qt = sQ + qhalf * 32 * LD;
-      const u16* dt = sdO + qhalf * 32 * LD;
+        for (int kk = 0; kk < KK; ++kk) {
+          s = mfma32(lds_bf16x8(cQ + swz<D>(q0 + i, 8 * h + 16 * kk)), kop[kk], s);
+          dp = mfma32(lds_bf16x8(cdO + swz<D>(q0 + i, 8 * h + 16 * kk)), vop[kk], dp);
+        }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        // P enters dV = P^T dO as bf16 hi + lo parts (16 significant bits):
-        // dV sums P over every query row and head of the group, and a single
-        // bf16 rounding of P (8 bits) is not accurate enough there.
-        const bf16x8 pop = pack_bf16(s, ks);
-        bf16x8 plo;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int qb = q0 + 8 * r4 + 4 * h;
+          const f32x4 L = *reinterpret_cast<const f32x4*>(&s_lse2[st][qb]);
+          const f32x4 Dd = *reinterpret_cast<const f32x4*>(&s_D[st][qb]);
+          int4 LO = make_int4(0, 0, 0, 0), PO = make_int4(0, 0, 0, 0);
+          if (!full) {
+            LO = *reinterpret_cast<const int4*>(&s_lo[st][qb]);
+            PO = *reinterpret_cast<const int4*>(&s_pos[st][qb]);
+          }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) plo[e] = (__bf16)(s[8 * ks + e] - (float)pop[e]);
-        const bf16x8 dsop = pack_bf16(dp, ks);
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e;
+            float p = __builtin_amdgcn_exp2f(fmaf(s[r], g.scale_log2, -L[e]));
+            if (!full) {
+              const int lo_e = e == 0 ? LO.x : e == 1 ? LO.y : e == 2 ? LO.z : LO.w;
+              const int po_e = e == 0 ? PO.x : e == 1 ? PO.y : e == 2 ? PO.z : PO.w;
+              if (kv_l < lo_e || kv_l > po_e) p = 0.f;
+            }
+            s[r] = p;
+            dp[r] = p * (dp[r] - Dd[e]);
+          }
+        }
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 dot = tr_operand(dt, LD, ks, 32 * db, lane);
-          dva[db] = mfma32(pop, dot, dva[db]);
-          dva[db] = mfma32(plo, dot, dva[db]);
-          dka[db] = mfma32(dsop, tr_operand(qt, LD, ks, 32 * db, lane), dka[db]);
+        for (int ks = 0; ks < 2; ++ks) {
+          // P enters dV = P^T dO as bf16 hi + lo parts (16 significant bits):
+          // dV sums P over every query row and head of the group, and a single
+          // bf16 rounding of P (8 bits) is not accurate enough there.
+          const bf16x8 pop = pack_bf16(s, ks);
+          bf16x8 plo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) plo[e] = (__bf16)(s[8 * ks + e] - (float)pop[e]);
+          const bf16x8 dsop = pack_bf16(dp, ks);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x8 dot = tr_operand<D>(cdO, q0, ks, 32 * db, lane);
+            dva[db] = mfma32(pop, dot, dva[db]);
+            dva[db] = mfma32(plo, dot, dva[db]);
+            dka[db] = mfma32(dsop, tr_operand<D>(cQ, q0, ks, 32 * db, lane), dka[db]);
+          }
         }
       }
+      if (blk + 1 < nblk) stash(st ^ 1);
+      __syncthreads();
     }
 
-    // Add the qhalf = 1 waves' sums into the qhalf = 0 waves (fixed order),
-    // first dK then dV, through LDS.
+    // Write this wave's 32 keys: directly (scaled) if the tile was not
+    // split, else to the item's partial-sum slot.
     const int2 info = tile_info[x];
     const bool split_tile = info.x > 1;
     float* dst_k;
@@ -303,62 +361,48 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     }
     const float kscale = split_tile ? 1.f : g.scale;
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      f32x16* acc = pass == 0 ? dka : dva;
-      __syncthreads();
-      if (qhalf == 1) {
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            sRed[((kvhalf * DB + db) * 16 + r) * 64 + lane] = acc[db][r];
+      for (int r = 0; r < 16; ++r) {
+        const int kvloc = wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (split_tile || t0 + kvloc < g.Skv) {
+          dst_k[(size_t)kvloc * rstride + 32 * db + i] = dka[db][r] * kscale;
+          dst_v[(size_t)kvloc * rstride + 32 * db + i] = dva[db][r];
+        }
       }
-      __syncthreads();
-      if (qhalf == 0) {
-        float* dst = pass == 0 ? dst_k : dst_v;
-        const float sc = pass == 0 ? kscale : 1.f;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float val = (acc[db][r] + sRed[((kvhalf * DB + db) * 16 + r) * 64 + lane]) * sc;
-            const int kvloc = kvhalf * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (split_tile || t0 + kvloc < g.Skv)
-              dst[(size_t)kvloc * rstride + 32 * db + i] = val;
-          }
-      }
-    }
-    __syncthreads();
   }
 }
 
-// Sum of the partial slots of each split key tile, in item order.
+// Sum of the partial slots of each split key tile, in item order.  One
+// workgroup per (key tile, KV head, 1024-float chunk).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const int2* __restrict__ tile_info,
                                                          const float* __restrict__ partial,
                                                          float* __restrict__ dk,
                                                          float* __restrict__ dv, Geo g, int nkt) {
   constexpr int BN = kDkdvBN;
-  const int x = blockIdx.x / g.Hkv, kvh = blockIdx.x % g.Hkv;
+  constexpr int kChunks = 2 * BN * D / 1024;
+  const int chunk = blockIdx.x % kChunks;
+  const int th = blockIdx.x / kChunks;
+  const int x = th / g.Hkv, kvh = th % g.Hkv;
   const int2 info = tile_info[x];
   if (info.x <= 1) return;
   const int b = x / nkt, kt = x % nkt;
   const int t0 = kt * BN;
   const size_t kvstride = (size_t)g.Hkv * D;
-  for (int e = threadIdx.x * 4; e < 2 * BN * D; e += 256 * 4) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < info.x; ++sp) {
-      const size_t slot = (size_t)(info.y + sp) * g.Hkv + kvh;
-      s += *reinterpret_cast<const f32x4*>(partial + slot * 2 * BN * D + e);
-    }
-    const int which = e / (BN * D);
-    const int kvloc = (e % (BN * D)) / D, col = e % D;
-    if (t0 + kvloc >= g.Skv) continue;
-    if (which == 0) s *= g.scale;
-    float* dst = (which == 0 ? dk : dv) + ((size_t)b * g.Skv + t0 + kvloc) * kvstride +
-                 (size_t)kvh * D + col;
-    *reinterpret_cast<f32x4*>(dst) = s;
+  const int e = chunk * 1024 + threadIdx.x * 4;
+  const int which = e / (BN * D);
+  const int kvloc = (e % (BN * D)) / D, col = e % D;
+  if (t0 + kvloc >= g.Skv) return;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < info.x; ++sp) {
+    const size_t slot = (size_t)(info.y + sp) * g.Hkv + kvh;
+    s += *reinterpret_cast<const f32x4*>(partial + slot * 2 * BN * D + e);
   }
+  if (which == 0) s *= g.scale;
+  float* dst = (which == 0 ? dk : dv) + ((size_t)b * g.Skv + t0 + kvloc) * kvstride +
+               (size_t)kvh * D + col;
+  *reinterpret_cast<f32x4*>(dst) = s;
 }
 
 hipError_t launch_bwd_dq(int D, const u16* q, const u16* k, const u16* v, const u16* out,
@@ -389,7 +433,7 @@ hipError_t launch_bwd_dkdv(int D, const u16* q, const u16* k, const u16* v, cons
 
 hipError_t launch_bwd_reduce(int D, const int2* tile_info, const float* partial, float* dk,
                              float* dv, const Geo& g, int nkt, hipStream_t st) {
-  const unsigned rgrid = (unsigned)g.B * nkt * g.Hkv;
+  const unsigned rgrid = (unsigned)g.B * nkt * g.Hkv * (2 * kDkdvBN * D / 1024);
   if (D == 128)
     bwd_reduce_kernel<128><<<rgrid, 256, 0, st>>>(tile_info, partial, dk, dv, g, nkt);
   else

@@ -23,6 +23,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -57,20 +58,64 @@ __device__ __forceinline__ i16x4 ds_read_tr(const u16* p) {
       (__attribute__((address_space(3))) i16x4*)(p));
 }
 
-// MFMA operand holding, for lane l = 32*h + i, column (n0 + i) of a
-// row-major bf16 LDS tile `base` (row stride `ld` elements) at the 8 rows
-// that register slot (h, e) pairs with in k-step ks:
-//   row = 16*ks + 8*(e/4) + 4*h + e%4.
+// LDS tiles are row-major with D bf16 per row (no padding) and the 16-byte
+// chunks of each row permuted by an XOR with a function f(row).  Measured on
+// gfx950 (SQ_LDS_BANK_CONFLICT), the LDS serves these reads as 64 four-byte
+// banks; f is chosen so that both access patterns of the kernels are
+// conflict-free:
+//  - ds_read_b128 of one chunk from 16 consecutive rows (16 lanes a cycle);
+//  - ds_read_b64_tr_b16 of 4 adjacent chunks (the first a multiple of 4) from
+//    4 consecutive rows starting at a multiple of 4 (32 lanes a cycle).
+// D = 128 (256-byte rows, one bank line): f = 4*(row%4) + (row/4)%4 takes 16
+// distinct values on 16 consecutive rows, and f/4 differs on the 4 rows of a
+// transposed read, so their 4-chunk blocks land in different banks.
+// D = 64 (128-byte rows, half a bank line; row parity picks the half):
+// f = 4*((row/2)%2) + (row/4)%4 gives 8 distinct values per parity on 16
+// rows, and rows r, r+2 of a transposed read differ in bit 2 of f.
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {
+  static_assert(D == 64 || D == 128, "head dim");
+  const int f = D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
+                         : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+  return row * D + ((((col >> 3) ^ f) << 3) | (col & 7));
+}
+
+// MFMA operand holding, for lane l = 32*h + i, column (n0 + i) of a swizzled
+// row-major bf16 LDS tile `base` at the 8 rows that register slot (h, e)
+// pairs with in k-step ks:
+//   row = row0 + 16*ks + 8*(e/4) + 4*h + e%4.
 // Two transposed reads, each giving four consecutive rows.
-__device__ __forceinline__ bf16x8 tr_operand(const u16* base, int ld, int ks, int n0,
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const u16* base, int row0, int ks, int n0,
                                              int lane) {
   const int s = lane & 15;
   const int grp = lane >> 4;        // 0..3
   const int h = grp >> 1;
   const int col = n0 + 16 * (grp & 1) + 4 * (s & 3);
-  const int row = 16 * ks + 4 * h + (s >> 2);
-  i16x4 lo = ds_read_tr(base + row * ld + col);
-  i16x4 hi = ds_read_tr(base + (row + 8) * ld + col);
+  const int row = row0 + 16 * ks + 4 * h + (s >> 2);
+  i16x4 lo = ds_read_tr(base + swz<D>(row, col));
+  i16x4 hi = ds_read_tr(base + swz<D>(row + 8, col));
+  bf16x8 r;
+  bf16x4 a = __builtin_bit_cast(bf16x4, lo);
+  bf16x4 b = __builtin_bit_cast(bf16x4, hi);
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+// Same operand from a padded row-major LDS tile with row stride LD elements
+// (no swizzle), so every read of a k-step is a constant offset from one
+// per-lane address.
+template <int LD>
+__device__ __forceinline__ bf16x8 tr_operand_pad(const u16* base, int row0, int ks, int n0,
+                                                 int lane) {
+  const int s = lane & 15;
+  const int grp = lane >> 4;
+  const int h = grp >> 1;
+  const u16* p = base + (row0 + 4 * h + (s >> 2)) * LD + 16 * (grp & 1) + 4 * (s & 3) +
+                 16 * ks * LD + n0;
+  i16x4 lo = ds_read_tr(p);
+  i16x4 hi = ds_read_tr(p + 8 * LD);
   bf16x8 r;
   bf16x4 a = __builtin_bit_cast(bf16x4, lo);
   bf16x4 b = __builtin_bit_cast(bf16x4, hi);
@@ -90,6 +135,21 @@ __device__ __forceinline__ bf16x8 pack_bf16(const f32x16& acc, int half) {
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
+// Scheduling hint for a run of N MFMAs that each consume one LDS read:
+// issue AHEAD reads first, then groups of STEP MFMAs each followed by STEP
+// more reads, then the remaining MFMAs.  Keeps LDS latency off the MFMA
+// issue path without holding every operand in registers at once.
+template <int N, int AHEAD, int STEP>
+__device__ __forceinline__ void sched_reads_ahead() {
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);   // DS read
+#pragma unroll
+  for (int j = 0; j < (N - AHEAD) / STEP; ++j) {
+    __builtin_amdgcn_sched_group_barrier(0x008, STEP, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, STEP, 0);  // DS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
 // Global position of local row j (chunk layout of the rank).
 __device__ __forceinline__ int local_pos(int j, int c, int cp, int rank) {
   return j < c ? rank * c + j : (2 * cp - 1 - rank) * c + (j - c);
@@ -98,8 +158,28 @@ __device__ __forceinline__ int local_pos(int j, int c, int cp, int rank) {
 // Per-call geometry shared by every kernel.
 struct Geo {
   int B, S, Skv, Hq, Hkv, G, Sq, c, cp, rank;
+  int g_log2;        // log2(G) if G is a power of two, else -1
+  unsigned g_magic;  // ceil(2^32 / G) for G >= 2 (see div_small)
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
 };
+
+// x / G and x % G (x >= 0); shifts when G is a power of two.
+__device__ __forceinline__ int div_g(int x, const Geo& g) {
+  return g.g_log2 >= 0 ? (x >> g.g_log2) : x / g.G;
+}
+__device__ __forceinline__ int mod_g(int x, const Geo& g) {
+  return g.g_log2 >= 0 ? (x & (g.G - 1)) : x % g.G;
+}
+
+// t / G for 0 <= t < 2^16 (and G < 2^16): with M = ceil(2^32/G) = (2^32+e)/G,
+// 0 <= e < G, t*M / 2^32 = t/G + t*e/(G*2^32) and t*e < 2^32, so the excess
+// never reaches the next multiple of 1/G and the high word is floor(t/G).
+__device__ __forceinline__ int div_small(int t, const Geo& g) {
+  return g.G == 1 ? t : (int)__umulhi((unsigned)t, g.g_magic);
+}
+
+// A value the caller knows is the same in every lane, as a scalar.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 }  // namespace dmgqa

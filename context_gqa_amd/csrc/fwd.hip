@@ -18,8 +18,15 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "qtile.hpp"
+#include "dma.hpp"
 
 namespace dmgqa {
+
+// Lazy rescaling: the running maximum used as the exponent reference is only
+// raised when a row's new maximum exceeds it by more than 2^kRescaleLog2 (in
+// exp2 units); otherwise P may reach 2^kRescaleLog2, which bf16 and fp32
+// represent exactly as well as values below 1.  out = O / l is unchanged.
+constexpr float kRescaleLog2 = 8.f;
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const u16* __restrict__ q,
@@ -28,9 +35,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const u16* __restrict__ q,
                                                      const int32_t* __restrict__ dstart,
                                                      u16* __restrict__ out,
                                                      float* __restrict__ lse, Geo g) {
-  constexpr int BM = kFwdBM, BN = kFwdBN, LD = D + 8, KK = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) u16 sK[BN * LD];
-  __shared__ __attribute__((aligned(16))) u16 sV[BN * LD];
+  constexpr int BM = kFwdBM, BN = kFwdBN, KK = D / 16, DB = D / 32;
+  // Padded layouts, each conflict-free for its one access pattern on the
+  // 64-bank LDS: K is read by ds_read_b128 (16 consecutive rows, one chunk)
+  // -> row stride D + 8; V by ds_read_b64_tr_b16 (4 rows x 4 chunks) -> row
+  // stride D + 32.  Two stages, each its own array (see dma.hpp).
+  constexpr int LDK = D + 8, LDV = D + 32;
+  __shared__ __attribute__((aligned(1024))) u16 sK0[BN * LDK];
+  __shared__ __attribute__((aligned(1024))) u16 sK1[BN * LDK];
+  __shared__ __attribute__((aligned(1024))) u16 sV0[BN * LDV];
+  __shared__ __attribute__((aligned(1024))) u16 sV1[BN * LDV];
 
   const int nrows = g.Sq * g.G;
   const int nt = (nrows + BM - 1) / BM;
@@ -58,6 +72,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const u16* __restrict__ q,
   for (int kk = 0; kk < KK; ++kk) qop[kk] = ld_bf16x8(q + qoff + 8 * h + 16 * kk);
 
   const QTileKeys kr = qtile_keys<BM, BN>(row0, ds, g);
+  const int ntiles = kr.na + kr.nb;
 
   float m = -INFINITY, l = 0.f;
   f32x16 o[DB];
@@ -67,28 +82,39 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const u16* __restrict__ q,
   const size_t kvstride = (size_t)g.Hkv * D;
   const u16* kbase = k + (size_t)b * g.Skv * kvstride + (size_t)kvh * D;
   const u16* vbase = v + (size_t)b * g.Skv * kvstride + (size_t)kvh * D;
+  PadTileDma<BN, D, LDK, 4> dmak;
+  PadTileDma<BN, D, LDV, 4> dmav;
+  dmak.init((unsigned)kvstride, wave, lane);
+  dmav.init((unsigned)kvstride, wave, lane);
+  auto issue = [&](int it, u16* dK, u16* dV) __attribute__((always_inline)) {
+    const int t0 = uniform((it < kr.na ? kr.a0 + it : kr.b0 + (it - kr.na)) * BN);
+    dmak.issue(kbase, (unsigned)kvstride, t0, g.Skv - 1, dK, wave, lane);
+    dmav.issue(vbase, (unsigned)kvstride, t0, g.Skv - 1, dV, wave, lane);
+  };
+  issue(0, sK0, sV0);
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
 
-  for (int it = 0; it < kr.na + kr.nb; ++it) {
-    const int kt = it < kr.na ? kr.a0 + it : kr.b0 + (it - kr.na);
-    const int t0 = kt * BN;
-    __syncthreads();
+  auto step = [&](int it, const u16* cK, const u16* cV, u16* nK, u16* nV)
+                  __attribute__((always_inline)) {
+    const int t0 = (it < kr.na ? kr.a0 + it : kr.b0 + (it - kr.na)) * BN;
+    if (it + 1 < ntiles) issue(it + 1, nK, nV);
+
+    // K operands for all k-steps are read up front (2*KK LDS reads in
+    // flight), so LDS latency overlaps the MFMA chain.
+    bf16x8 kf0[KK], kf1[KK];
 #pragma unroll
-    for (int x = threadIdx.x; x < BN * (D / 8); x += 256) {
-      const int rk = x / (D / 8), col = (x % (D / 8)) * 8;
-      const int src = min(t0 + rk, g.Skv - 1);
-      *reinterpret_cast<uint4*>(&sK[rk * LD + col]) =
-          *reinterpret_cast<const uint4*>(kbase + (size_t)src * kvstride + col);
-      *reinterpret_cast<uint4*>(&sV[rk * LD + col]) =
-          *reinterpret_cast<const uint4*>(vbase + (size_t)src * kvstride + col);
+    for (int kk = 0; kk < KK; ++kk) {
+      kf0[kk] = lds_bf16x8(&cK[i * LDK + 8 * h + 16 * kk]);
+      kf1[kk] = lds_bf16x8(&cK[(32 + i) * LDK + 8 * h + 16 * kk]);
     }
-    __syncthreads();
-
     f32x16 s0 = zero16(), s1 = zero16();
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      s0 = mfma32(lds_bf16x8(&sK[i * LD + 8 * h + 16 * kk]), qop[kk], s0);
-      s1 = mfma32(lds_bf16x8(&sK[(32 + i) * LD + 8 * h + 16 * kk]), qop[kk], s1);
+      s0 = mfma32(kf0[kk], qop[kk], s0);
+      s1 = mfma32(kf1[kk], qop[kk], s1);
     }
+    sched_reads_ahead<2 * KK, KK, 2>();
     const bool full = kr.max_lo <= t0 && t0 + BN - 1 <= kr.min_pos;
     if (!full) {
 #pragma unroll
@@ -98,35 +124,47 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const u16* __restrict__ q,
         if (kv + 32 < lo || kv + 32 > pos) s1[r] = -INFINITY;
       }
     }
-    float mx = -INFINITY;
+    float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
     mx = fmaxf(mx, xor32(mx));
-    const float mnew = fmaxf(m, mx);
-    const float muse = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f((m - muse) * g.scale_log2);
-    const float msc = muse * g.scale_log2;
-    float rs = 0.f;
+    const bool need = mx != -INFINITY && (m == -INFINITY || (mx - m) * g.scale_log2 > kRescaleLog2);
+    if (__any(need)) {
+      const float mnew = need ? mx : m;
+      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * g.scale_log2);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m = mnew;
+    }
+    const float msc = m == -INFINITY ? 0.f : m * g.scale_log2;
+    float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], g.scale_log2, -msc));
       s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], g.scale_log2, -msc));
-      rs += s0[r] + s1[r];
+      rs0 += s0[r];
+      rs1 += s1[r];
     }
-    l = l * alpha + rs;
-    m = mnew;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    l += rs0 + rs1;
 
 #pragma unroll
     for (int ks = 0; ks < BN / 16; ++ks) {
       const bf16x8 pop = pack_bf16(ks < 2 ? s0 : s1, ks & 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        o[db] = mfma32(tr_operand(sV, LD, ks, 32 * db, lane), pop, o[db]);
+        o[db] = mfma32(tr_operand_pad<LDV>(cV, 0, ks, 32 * db, lane), pop, o[db]);
     }
+    // this wave's loads of the next tile are done; after the barrier every
+    // wave's are, and every wave has finished reading the current stage
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, sK0, sV0, sK1, sV1);
+    if (it + 1 < ntiles) step(it + 1, sK1, sV1, sK0, sV0);
   }
 
   const float lt = l + xor32(l);

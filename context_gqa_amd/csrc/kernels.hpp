@@ -12,15 +12,15 @@ namespace dmgqa {
 // workgroup of 4 waves (32 rows per wave), 64 keys per step.
 constexpr int kFwdBM = 128;
 constexpr int kFwdBN = 64;
-// dK/dV kernel: 64 keys per work item (2 waves x 32), query rows streamed
-// 64 at a time (2 waves x 32).
-constexpr int kDkdvBN = 64;
+// dK/dV kernel: 128 keys per work item (4 waves x 32), query rows streamed
+// 64 at a time.
+constexpr int kDkdvBN = 128;
 constexpr int kDkdvBM = 64;
 // Split of the query rows reaching one key tile into work items: at least
 // this many rows per item, and about kMaxSplitTotal split items per call.
 constexpr int kMinRowsPerSplit = 512;
-constexpr int kMaxSplitTotal = 1024;
-constexpr int kDkdvGrid = 512;  // persistent workgroups of the dK/dV kernel
+constexpr int kMaxSplitTotal = 512;
+constexpr int kDkdvGrid = 256;  // persistent workgroups of the dK/dV kernel
 
 struct SchedHeader {
   int n_base_items;    // work items per KV head
