@@ -135,6 +135,23 @@ __device__ __forceinline__ bf16x8 pack_bf16(const f32x16& acc, int half) {
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
+// max(a, b, c) as one v_max3_f32.  Written as an instruction so the compiler
+// does not add NaN-quieting copies of MFMA results before each max (scores
+// are finite or -inf here).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// acc + x0 + x1 for a bf16 pair, one v_dot2_f32_bf16 against (1, 1).
+__device__ __forceinline__ float sum2_bf16(bf16x2 x, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
+}
+
 // Scheduling hint for a run of N MFMAs that each consume one LDS read:
 // issue AHEAD reads first, then groups of STEP MFMAs each followed by STEP
 // more reads, then the remaining MFMAs.  Keeps LDS latency off the MFMA

@@ -117,16 +117,20 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const u16* __restrict__ q,
     sched_reads_ahead<2 * KK, KK, 2>();
     const bool full = kr.max_lo <= t0 && t0 + BN - 1 <= kr.min_pos;
     if (!full) {
+      // allowed keys lo..pos relative to this lane's first key t0 + 4h;
+      // register r holds key offset 8*(r/4) + r%4 (+32 for s1)
+      const int lo_rel = lo - (t0 + 4 * h), hi_rel = pos - (t0 + 4 * h);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kv = t0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (kv < lo || kv > pos) s0[r] = -INFINITY;
-        if (kv + 32 < lo || kv + 32 > pos) s1[r] = -INFINITY;
+        const int c = 8 * (r >> 2) + (r & 3);
+        if (c < lo_rel || c > hi_rel) s0[r] = -INFINITY;
+        if (c + 32 < lo_rel || c + 32 > hi_rel) s1[r] = -INFINITY;
       }
     }
-    float mx = fmaxf(s0[0], s1[0]);
+    float mx = max3f(s0[0], s1[0], s0[1]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    for (int r = 1; r < 15; ++r) mx = max3f(mx, s1[r], s0[r + 1]);
+    mx = max3f(mx, s1[15], s1[15]);
     mx = fmaxf(mx, xor32(mx));
     const bool need = mx != -INFINITY && (m == -INFINITY || (mx - m) * g.scale_log2 > kRescaleLog2);
     if (__any(need)) {
@@ -140,23 +144,24 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const u16* __restrict__ q,
       m = mnew;
     }
     const float msc = m == -INFINITY ? 0.f : m * g.scale_log2;
-    float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], g.scale_log2, -msc));
       s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], g.scale_log2, -msc));
-      rs0 += s0[r];
-      rs1 += s1[r];
     }
-    l += rs0 + rs1;
-
+    // the row sum is taken over the bf16 P that multiplies V
+    float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int ks = 0; ks < BN / 16; ++ks) {
       const bf16x8 pop = pack_bf16(ks < 2 ? s0 : s1, ks & 1);
+      float& rs = (ks & 1) ? rs1 : rs0;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) rs = sum2_bf16(bf16x2{pop[e], pop[e + 1]}, rs);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         o[db] = mfma32(tr_operand_pad<LDV>(cV, 0, ks, 32 * db, lane), pop, o[db]);
     }
+    l += rs0 + rs1;
     // this wave's loads of the next tile are done; after the barrier every
     // wave's are, and every wave has finished reading the current stage
     wait_vmcnt<0>();
