@@ -43,7 +43,7 @@ int check_shape(int B, int S, int Skv, int Hq, int Hkv, int D, int cp, int rank,
   if (tiles >= (1LL << 31)) return DMGQA_ERR_UNSUPPORTED;
   // element offsets inside q/out/dout/dq and k/v/dk/dv are 32-bit
   if ((long long)B * Sq * Hq * D >= (1LL << 31) || (long long)B * Skv * Hkv * D >= (1LL << 31) ||
-      G >= (1 << 16))
+      G >= (1 << 15))
     return DMGQA_ERR_UNSUPPORTED;
   sh->B = B; sh->S = S; sh->Skv = Skv; sh->Hq = Hq; sh->Hkv = Hkv; sh->D = D;
   sh->cp = cp; sh->rank = rank; sh->G = G; sh->c = c; sh->Sq = (int)Sq;
@@ -65,7 +65,7 @@ int check_docs_args(const int32_t* doc_ids, const int32_t* cu, int n_docs, const
 
 // Workspace layout.
 struct Layout {
-  size_t dstart, dend, agg, Dbuf, hdr, tile_info, items, partial, total;
+  size_t dstart, dend, agg, rowstat, hdr, tile_info, items, partial, total;
   int nkt, max_split_base;
 };
 
@@ -81,7 +81,7 @@ Layout layout(const Shape& s, bool backward) {
     L.nkt = (s.Skv + kDkdvBN - 1) / kDkdvBN;
     L.max_split_base = kMaxSplitTotal / s.Hkv > 1 ? kMaxSplitTotal / s.Hkv : 1;
     const size_t ntiles = (size_t)s.B * L.nkt;
-    L.Dbuf = off; off = align_up(off + (size_t)s.B * s.Sq * s.Hq * sizeof(float));
+    L.rowstat = off; off = align_up(off + 2 * (size_t)s.B * s.Sq * s.Hq * sizeof(float));
     L.hdr = off; off = align_up(off + sizeof(SchedHeader));
     L.tile_info = off; off = align_up(off + ntiles * sizeof(int2));
     L.items = off; off = align_up(off + (ntiles + L.max_split_base) * sizeof(int2));
@@ -206,7 +206,9 @@ int docmask_gqa_attn_bwd(const void* q, const void* k, const void* v, const void
   const Geo g = make_geo(s, softmax_scale);
   const int32_t* dstart = reinterpret_cast<const int32_t*>(ws + L.dstart);
   const int32_t* dend = reinterpret_cast<const int32_t*>(ws + L.dend);
-  float* Dbuf = reinterpret_cast<float*>(ws + L.Dbuf);
+  // per query row: -lse/scale, then -D
+  float* Lbuf = reinterpret_cast<float*>(ws + L.rowstat);
+  float* Nbuf = Lbuf + (size_t)s.B * s.Sq * s.Hq;
   SchedHeader* hdr = reinterpret_cast<SchedHeader*>(ws + L.hdr);
   int2* tile_info = reinterpret_cast<int2*>(ws + L.tile_info);
   int2* items = reinterpret_cast<int2*>(ws + L.items);
@@ -219,14 +221,14 @@ int docmask_gqa_attn_bwd(const void* q, const void* k, const void* v, const void
   timing_begin(kKDq, st);
   e = launch_bwd_dq(D, static_cast<const u16*>(q), static_cast<const u16*>(k),
                     static_cast<const u16*>(v), static_cast<const u16*>(out),
-                    static_cast<const u16*>(dout), lse, dstart, static_cast<u16*>(dq), Dbuf, g,
-                    st);
+                    static_cast<const u16*>(dout), lse, dstart, static_cast<u16*>(dq), Lbuf, Nbuf,
+                    g, st);
   timing_end(kKDq, st);
   if (e != hipSuccess) return DMGQA_ERR_HIP;
   timing_begin(kKDkdv, st);
   e = launch_bwd_dkdv(D, static_cast<const u16*>(q), static_cast<const u16*>(k),
-                      static_cast<const u16*>(v), static_cast<const u16*>(dout), lse, dstart,
-                      dend, Dbuf, hdr, tile_info, items, partial, dk, dv, g, L.nkt, st);
+                      static_cast<const u16*>(v), static_cast<const u16*>(dout), Lbuf, Nbuf, dend,
+                      hdr, tile_info, items, partial, dk, dv, g, L.nkt, st);
   timing_end(kKDkdv, st);
   if (e != hipSuccess) return DMGQA_ERR_HIP;
   timing_begin(kKReduce, st);

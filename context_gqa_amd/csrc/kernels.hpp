@@ -40,12 +40,12 @@ hipError_t launch_fwd(int D, const u16* q, const u16* k, const u16* v, const int
                       u16* out, float* lse, const Geo& g, hipStream_t st);
 hipError_t launch_bwd_dq(int D, const u16* q, const u16* k, const u16* v, const u16* out,
                          const u16* dout, const float* lse, const int32_t* dstart, u16* dq,
-                         float* Dbuf, const Geo& g, hipStream_t st);
+                         float* Lbuf, float* Nbuf, const Geo& g, hipStream_t st);
 hipError_t launch_bwd_dkdv(int D, const u16* q, const u16* k, const u16* v, const u16* dout,
-                           const float* lse, const int32_t* dstart, const int32_t* dend,
-                           const float* Dbuf, SchedHeader* hdr, const int2* tile_info,
-                           const int2* items, float* partial, float* dk, float* dv, const Geo& g,
-                           int nkt, hipStream_t st);
+                           const float* Lbuf, const float* Nbuf, const int32_t* dend,
+                           SchedHeader* hdr, const int2* tile_info, const int2* items,
+                           float* partial, float* dk, float* dv, const Geo& g, int nkt,
+                           hipStream_t st);
 hipError_t launch_bwd_reduce(int D, const int2* tile_info, const float* partial, float* dk,
                              float* dv, const Geo& g, int nkt, hipStream_t st);
 
