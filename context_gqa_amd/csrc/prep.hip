@@ -188,20 +188,32 @@ __global__ __launch_bounds__(kScanThreads) void sched_dkdv(const int32_t* __rest
   long long rps = (total + max_split_base - 1) / max_split_base;
   if (rps < kMinRowsPerSplit) rps = kMinRowsPerSplit;
   rps = (rps + kDkdvBM - 1) / kDkdvBM * kDkdvBM;
-  // 2. splits per tile, prefix sums of items and of partial slots
-  int my_items = 0, my_slots = 0;
+  // 2. splits per tile: rows / rps full splits and at most one shorter
+  //    remainder (a tile no row reaches gets one empty item, which writes
+  //    its zero gradients).  Items are listed largest first, so that the
+  //    persistent workgroups, taking them in order, end close together: all
+  //    full splits in tile order, then the remainders by decreasing size
+  //    (64 size classes; order within a class is arbitrary and does not
+  //    affect results, which depend only on (tile, split)).
+  __shared__ int bucket_cnt[64], bucket_base[64];
+  if (threadIdx.x < 64) bucket_cnt[threadIdx.x] = 0;
+  __syncthreads();
+  auto remainder_class = [&](long long rem) { return 63 - (int)min(63LL, rem * 64 / rps); };
+  int my_full = 0, my_slots = 0;
   for (int x = first; x < min(first + per, ntiles); ++x) {
     const int b = x / nkt, kt = x % nkt;
     int a0, na, b0, nb;
     dkdv_tile_tokens(dend + (size_t)b * g.Skv, kt, g, a0, na, b0, nb);
     const long long rows = (long long)(na + nb) * g.G;
-    const int ns = rows == 0 ? 1 : (int)((rows + rps - 1) / rps);
-    my_items += ns;
+    const int nf = (int)(rows / rps);
+    const long long rem = rows - (long long)nf * rps;
+    const int ns = nf + ((rem > 0 || rows == 0) ? 1 : 0);
+    my_full += nf;
     my_slots += ns > 1 ? ns : 0;
+    if (rem > 0 || rows == 0) atomicAdd(&bucket_cnt[remainder_class(rem)], 1);
   }
-  // exclusive scans via the inclusive max-scan helper on prefix sums
   __shared__ int scan_i[kScanThreads], scan_s[kScanThreads];
-  scan_i[threadIdx.x] = my_items;
+  scan_i[threadIdx.x] = my_full;
   scan_s[threadIdx.x] = my_slots;
   __syncthreads();
   for (int o = 1; o < kScanThreads; o <<= 1) {
@@ -212,21 +224,47 @@ __global__ __launch_bounds__(kScanThreads) void sched_dkdv(const int32_t* __rest
     scan_s[threadIdx.x] += vs;
     __syncthreads();
   }
-  int item = scan_i[threadIdx.x] - my_items;
+  const int n_full = scan_i[kScanThreads - 1];
+  if (threadIdx.x == 0) {
+    int acc = n_full;
+    for (int c = 0; c < 64; ++c) {
+      bucket_base[c] = acc;
+      acc += bucket_cnt[c];
+      bucket_cnt[c] = 0;
+    }
+  }
+  __syncthreads();
+  int item = scan_i[threadIdx.x] - my_full;
   int slot = scan_s[threadIdx.x] - my_slots;
+  int n_items_mine = 0;
   for (int x = first; x < min(first + per, ntiles); ++x) {
     const int b = x / nkt, kt = x % nkt;
     int a0, na, b0, nb;
     dkdv_tile_tokens(dend + (size_t)b * g.Skv, kt, g, a0, na, b0, nb);
     const long long rows = (long long)(na + nb) * g.G;
-    const int ns = rows == 0 ? 1 : (int)((rows + rps - 1) / rps);
+    const int nf = (int)(rows / rps);
+    const long long rem = rows - (long long)nf * rps;
+    const bool has_rem = rem > 0 || rows == 0;
+    const int ns = nf + (has_rem ? 1 : 0);
     tile_info[x] = make_int2(ns, ns > 1 ? slot : -1);
-    for (int s = 0; s < ns; ++s) items[item + s] = make_int2(x, s);
-    item += ns;
+    for (int s = 0; s < nf; ++s) items[item + s] = make_int2(x, s);
+    item += nf;
+    if (has_rem) {
+      const int c = remainder_class(rem);
+      items[bucket_base[c] + atomicAdd(&bucket_cnt[c], 1)] = make_int2(x, nf);
+    }
+    n_items_mine += ns;
     slot += ns > 1 ? ns : 0;
   }
-  if (threadIdx.x == kScanThreads - 1) {
-    hdr->n_base_items = scan_i[kScanThreads - 1];
+  // total item count
+  scan_i[threadIdx.x] = n_items_mine;
+  __syncthreads();
+  for (int o = kScanThreads / 2; o > 0; o >>= 1) {
+    if (threadIdx.x < o) scan_i[threadIdx.x] += scan_i[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    hdr->n_base_items = scan_i[0];
     hdr->rows_per_split = (int)rps;
     hdr->n_slots_base = scan_s[kScanThreads - 1];
     hdr->counter = 0;
