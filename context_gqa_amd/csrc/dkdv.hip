@@ -25,15 +25,18 @@
 // for the fp32 result there.
 //
 // LDS stage layout (bytes): [Q tile][dO tile][-lse/scale: 64 fp32][-D: 64 fp32].
-// A tile is 64 rows x D bf16 stored chunk-major: the 16-byte chunk c
-// (elements 8c .. 8c+7) of row r sits at c * kChunkStride + 16 * r.  With the
-// 64-byte pad in kChunkStride both access patterns are free of bank
-// conflicts on the 64 four-byte banks:
-//   - ds_read_b128 of one chunk by 16 consecutive rows: 256 contiguous bytes;
-//   - ds_read_b64_tr_b16 (4 rows x 4 chunks of 8 bytes per 16 lanes, two
-//     such groups per cycle): bank = 16*(chunk%4) + 4*(row%4) + 2*half.
-// A DMA instruction moves one chunk of all 64 rows (lane = row), so each
-// lane computes one global row offset per block.
+// A tile holds 64 rows x D bf16 in groups of 4 sixteen-byte chunks (32
+// elements): group c/4 of row r occupies the 64 bytes at
+// (c/4) * 4096 + 64 * r, and inside them chunk c sits in slot
+// (c % 4) ^ ((r / 4) % 4).  On the 64 four-byte banks this makes both
+// access patterns conflict-free:
+//   - ds_read_b128 of one chunk by 16 consecutive rows: bank =
+//     16*(r%4) + 4*slot, and the slot differs across the four row quads;
+//   - ds_read_b64_tr_b16 (rows r..r+3 of a quad x 4 chunks of a group x two
+//     8-byte halves, 32 lanes a cycle): 4 rows x 4 slots x 2 halves.
+// A DMA instruction fills one chunk group of 16 rows (lane l: row 16w + l/4,
+// slot l % 4): every lane loads 16 bytes of its row from a 64-byte run, and
+// each lane keeps the same row for all of a block's instructions.
 #include "common.hpp"
 #include "dma.hpp"
 #include <stdint.h>
@@ -44,12 +47,12 @@ namespace dmgqa {
 namespace {
 
 constexpr int kBlkRows = kDkdvBM;                    // 64 query rows per LDS stage
-constexpr int kChunkStride = kBlkRows * 16 + 64;     // bytes between chunk columns
+constexpr int kGroupBytes = kBlkRows * 64;           // one chunk group of a tile
 
 template <int D>
 struct DkdvLds {
   static constexpr int kChunks = D / 8;
-  static constexpr int kTile = kChunks * kChunkStride;
+  static constexpr int kTile = kChunks / 4 * kGroupBytes;
   static constexpr int kL = 2 * kTile;               // -lse/scale per row
   static constexpr int kN = kL + kBlkRows * 4;       // -D per row
   static constexpr int kStage = kN + kBlkRows * 4;
@@ -83,12 +86,14 @@ __device__ __forceinline__ f32x4 ld_lds_f32x4(const char* p) {
 }
 
 // Operand for lane l = 32h + i holding column (32*db + i) of the rows that
-// register slot (h, e) pairs with in k-step ks (see common.hpp), from a
-// chunk-major tile; `lane_off` is the per-lane part of the address.
-__device__ __forceinline__ bf16x8 tr_chunk(const char* tile, int lane_off, int q0, int ks, int db) {
-  const char* p = tile + lane_off + db * 4 * kChunkStride + (q0 + 16 * ks) * 16;
-  const i16x4 lo = ds_read_tr(reinterpret_cast<const u16*>(p));
-  const i16x4 hi = ds_read_tr(reinterpret_cast<const u16*>(p + 8 * 16));
+// register slot (h, e) pairs with in k-step ks (see common.hpp), from a tile
+// in the grouped layout above; lane_off[hf] is the per-lane part of the
+// address of the rows 8*hf .. 8*hf+3 of the 16-row step.
+__device__ __forceinline__ bf16x8 tr_group(const char* tile, const int (&lane_off)[2], int q0,
+                                           int ks, int db) {
+  const char* p = tile + db * kGroupBytes + (q0 + 16 * ks) * 64;
+  const i16x4 lo = ds_read_tr(reinterpret_cast<const u16*>(p + lane_off[0]));
+  const i16x4 hi = ds_read_tr(reinterpret_cast<const u16*>(p + lane_off[1]));
   const bf16x4 a = __builtin_bit_cast(bf16x4, lo);
   const bf16x4 b = __builtin_bit_cast(bf16x4, hi);
   bf16x8 r;
@@ -135,11 +140,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const size_t kvstride = (size_t)g.Hkv * D;
   const float c2 = g.scale_log2;
 
-  // per-lane parts of the LDS addresses
-  const int off_b128 = h * kChunkStride + 16 * i;              // + kk * 2 * kChunkStride
+  // per-lane parts of the LDS addresses.  b128 operand (row i, chunk
+  // h + 2kk): slot (h + 2(kk&1)) ^ (i/4 % 4) = slot of even kk, ^2 for odd.
+  const int off_b[2] = {64 * i + 16 * (h ^ ((i >> 2) & 3)),
+                        64 * i + 16 * ((h ^ ((i >> 2) & 3)) ^ 2)};
+  // transposed operand: source lane s of 16-lane group grp reads row
+  // 4h + s/4 (+8 for the second half), chunk 2(grp&1) + (s&3)/2 of the
+  // group, 8-byte half s&1; the row quad index is h (+2).
   const int s16 = lane & 15, grp = lane >> 4;
-  const int off_tr = (2 * (grp & 1) + ((s16 & 3) >> 1)) * kChunkStride +
-                     (4 * (grp >> 1) + (s16 >> 2)) * 16 + 8 * (s16 & 1);
+  int off_t[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+    off_t[hf] = (4 * h + (s16 >> 2) + 8 * hf) * 64 +
+                16 * ((2 * (grp & 1) + ((s16 & 3) >> 1)) ^ ((h + 2 * hf) & 3)) + 8 * (s16 & 1);
 
   for (;;) {
     if (threadIdx.x == 0) s_item = atomicAdd(&hdr->counter, 1);
@@ -209,24 +222,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int step_ti = kBlkRows / g.G, step_hh = kBlkRows - step_ti * g.G;
     const int last_ti = (r_end - 1) / g.G, last_hh = (r_end - 1) - last_ti * g.G;
     int nx_blk = 0;
-    auto issue_block = [&](char* st) __attribute__((always_inline)) {
-      const bool ok = r_begin + nx_blk * kBlkRows + lane < r_end;
-      const int t = nx_hh + lane;
+    auto row_index = [&](int r) __attribute__((always_inline)) -> unsigned {
+      const bool ok = r_begin + nx_blk * kBlkRows + r < r_end;
+      const int t = nx_hh + r;
       const int qd = div_small(t, g);
       const int ti = ok ? nx_ti + qd : last_ti;
       const int hh = ok ? t - qd * g.G : last_hh;
       const int tok = ti < na ? a0 + ti : b0 + (ti - na);
-      const unsigned ridx = (unsigned)((b * g.Sq + tok) * g.Hq + kvh * g.G + hh);
-      const u16* qr = q + ridx * (unsigned)D;
-      const u16* orow = dout + ridx * (unsigned)D;
+      return (unsigned)((b * g.Sq + tok) * g.Hq + kvh * g.G + hh);
+    };
+    auto issue_block = [&](char* st) __attribute__((always_inline)) {
+      // tiles: wave w fills rows 16w .. 16w+15 of every chunk group
+      const int rr = 16 * wave + (lane >> 2);
+      const unsigned ridx = row_index(rr);
+      const int slot = lane & 3, xr = (rr >> 2) & 3;
+      const u16* qr = q + ridx * (unsigned)D + 8 * (slot ^ xr);
+      const u16* orow = dout + ridx * (unsigned)D + 8 * (slot ^ xr);
+      char* tq = st + 64 * 16 * wave;
 #pragma unroll
       for (int c = 0; c < NCH / 4; ++c) {
-        const int ch = wave * (NCH / 4) + c;
-        dma_lds16(qr + 8 * ch, st + ch * kChunkStride);
-        dma_lds16(orow + 8 * ch, st + Lds::kTile + ch * kChunkStride);
+        dma_lds16(qr + 32 * c, tq + c * kGroupBytes);
+        dma_lds16(orow + 32 * c, tq + Lds::kTile + c * kGroupBytes);
       }
+      // row statistics: lane = row (waves 0, 2: -lse/scale; 1, 3: -D)
+      const unsigned ridm = row_index(lane);
       const float* rs = (wave & 1) ? Nbuf : Lbuf;
-      dma_lds4(rs + ridx, st + ((wave & 1) ? Lds::kN : Lds::kL));
+      dma_lds4(rs + ridm, st + ((wave & 1) ? Lds::kN : Lds::kL));
       ++nx_blk;
       nx_ti += step_ti;
       nx_hh += step_hh;
@@ -254,10 +275,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       }
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        sc = mfma32(ld_lds_b128(st + off_b128 + kk * 2 * kChunkStride + 16 * q0), kop[kk], sc);
+        sc = mfma32(ld_lds_b128(st + (kk >> 1) * kGroupBytes + 64 * q0 + off_b[kk & 1]), kop[kk],
+                    sc);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        pc = mfma32(ld_lds_b128(st + Lds::kTile + off_b128 + kk * 2 * kChunkStride + 16 * q0),
+        pc = mfma32(ld_lds_b128(st + Lds::kTile + (kk >> 1) * kGroupBytes + 64 * q0 +
+                                off_b[kk & 1]),
                     vop[kk], pc);
 
       float p[16];
@@ -296,7 +319,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 dot = tr_chunk(tO, off_tr, q0, ks, db);
+          const bf16x8 dot = tr_group(tO, off_t, q0, ks, db);
           dva[db] = mfma32(pop[ks], dot, dva[db]);
           dva[db] = mfma32(plo[ks], dot, dva[db]);
         }
@@ -309,7 +332,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          dka[db] = mfma32(dsop[ks], tr_chunk(tQ, off_tr, q0, ks, db), dka[db]);
+          dka[db] = mfma32(dsop[ks], tr_group(tQ, off_t, q0, ks, db), dka[db]);
     };
 
     // The first sub-block of block n waits for its DMA (issued two blocks
