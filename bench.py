@@ -119,6 +119,9 @@ def main(argv=None) -> int:
     ap.add_argument("--seeds", default="0,1,2,3,4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay one captured HIP graph per seed instead of launching eagerly "
+                         "(measured slower than eager launches on ROCm 7)")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -164,28 +167,50 @@ def main(argv=None) -> int:
                          flops=useful_flops(pairs, Hq, D, cfg.backward),
                          bytes=algorithmic_bytes(case, cfg.backward)))
 
-    stream = torch.cuda.current_stream()
-
     def step(i):
+        """One forward + backward call on seed i's inputs, on the current stream."""
         r = runs[i % len(runs)]
         t, case = r["t"], r["case"]
         M.docmask_gqa_attn_fwd(t["q"], t["k"], t["v"], doc_ids=t["doc"], cp_size=cfg.cp_size,
                                cp_rank=rank, softmax_scale=case.scale, out=t["out"],
-                               lse=t["lse"], workspace=t["wsf"], stream=stream)
+                               lse=t["lse"], workspace=t["wsf"])
         if cfg.backward:
             M.docmask_gqa_attn_bwd(t["q"], t["k"], t["v"], t["out"], t["dout"], t["lse"],
                                    doc_ids=t["doc"], cp_size=cfg.cp_size, cp_rank=rank,
                                    softmax_scale=case.scale, dq=t["dq"], dk=t["dk"], dv=t["dv"],
-                                   workspace=t["wsb"], stream=stream)
+                                   workspace=t["wsb"])
 
-    for i in range(args.warmup):
+    # With --graph each seed's step is captured once into a HIP graph (the
+    # library makes no allocation, synchronisation or memset inside a call)
+    # and the timed loop replays it.
+    for i in range(max(args.warmup, len(runs))):
         step(i)
+    torch.cuda.synchronize()
+    graphs = None
+    if args.graph:
+        graphs = []
+        for j in range(len(runs)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(j)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run_step(i):
+        if graphs is None:
+            step(i)
+        else:
+            graphs[i % len(runs)].replay()
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        run_step(i)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(args.steps):
-        step(i)
+        run_step(i)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
@@ -199,7 +224,7 @@ def main(argv=None) -> int:
         reps = max(3, args.steps // len(runs))
         a.record(stream)
         for _ in range(reps):
-            step(j)
+            run_step(j)
         b.record(stream)
         torch.cuda.synchronize()
         per_seed.append(r["flops"]["total"] / (a.elapsed_time(b) / reps * 1e-3) / 1e12)
@@ -245,7 +270,8 @@ def main(argv=None) -> int:
         "config": {"workload": f"{cfg.name}: {cfg.description}", "cp_size": cfg.cp_size,
                    "cp_rank": rank, "seq_len": cfg.S, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
                    "head_dim": cfg.D, "global_batch": cfg.B, "seeds": seeds,
-                   "parallelism": "one CP rank's share on one GPU"},
+                   "parallelism": "one CP rank's share on one GPU",
+                   "launch": "hip graph per seed" if args.graph else "eager"},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "per_seed_tflops": [round(x, 2) for x in per_seed],
         "median_seed_tflops": round(float(np.median(per_seed)), 2),
