@@ -77,6 +77,77 @@ def algorithmic_bytes(case, backward: bool) -> int:
     return fwd + bwd
 
 
+COPY_CALIBRATION_BYTES = 512 << 20
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: a stored traffic figure is reported only for
+    the exact kernels it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "context_gqa_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel`, from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE measurement (profiles/traffic_<kernel>_<workload>.json,
+    written by profiles/traffic_from_pmc.py); None if there is none or the
+    kernels have changed since it was taken."""
+    path = os.path.join(TRAFFIC_DIR, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec["bytes_per_launch"]
+
+
+KERNEL_KEYS = {"fwd": "fwd_kernel", "bwd_dq": "bwd_dq_kernel", "bwd_dkdv": "bwd_dkdv_kernel"}
+
+
+def traffic_from_pmc(fetch_csv: str, write_csv: str, kernel: str, workload: str,
+                     command: str) -> dict:
+    """HBM bytes per launch of `kernel` from two rocprofv3 --pmc runs of
+    `bench.py --copy-calibration` (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch), each scaled by the same counter's reading for the
+    device-to-device copy of COPY_CALIBRATION_BYTES in the same run."""
+    import csv
+
+    def per_dispatch(path, counter):
+        ours, copies = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            name = r["Kernel_Name"]
+            if KERNEL_KEYS[kernel] in name:
+                ours.append(v)
+            elif "copy" in name.lower() and "dmgqa" not in name:
+                copies.append(v)
+        if not ours or not copies:
+            raise SystemExit(f"{path}: no {counter} rows for {kernel} or for the copy kernel")
+        return sum(ours) / len(ours), max(copies)
+
+    f_k, f_copy = per_dispatch(fetch_csv, "FETCH_SIZE")
+    w_k, w_copy = per_dispatch(write_csv, "WRITE_SIZE")
+    f_scale = COPY_CALIBRATION_BYTES / (f_copy * 1024)
+    w_scale = COPY_CALIBRATION_BYTES / (w_copy * 1024)
+    return {"kernel": kernel, "workload": workload,
+            "fetch_kib_per_launch": round(f_k, 1), "write_kib_per_launch": round(w_k, 1),
+            "copy_bytes": COPY_CALIBRATION_BYTES, "copy_fetch_kib": f_copy,
+            "copy_write_kib": w_copy, "fetch_scale": round(f_scale, 4),
+            "write_scale": round(w_scale, 4),
+            "bytes_per_launch": int(f_k * 1024 * f_scale + w_k * 1024 * w_scale),
+            "source_hash": kernel_source_hash(), "command": command}
+
+
 def cpu_baseline(runs, min_s: float = 10.0, max_s: float = 30.0) -> dict:
     """The CPU oracle (fp64 numpy, all host cores) on the same inputs: whole
     ranks' forward + backward, cycling over the seeds until at least min_s
@@ -119,10 +190,27 @@ def main(argv=None) -> int:
     ap.add_argument("--seeds", default="0,1,2,3,4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run three device-to-device copies of 512 MiB (the reference "
+                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--graph", action="store_true",
                     help="replay one captured HIP graph per seed instead of launching eagerly "
                          "(measured slower than eager launches on ROCm 7)")
+    ap.add_argument("--traffic-from-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<kernel>_<workload>.json from two "
+                         "rocprofv3 --pmc counter files and exit")
+    ap.add_argument("--traffic-kernel", default="bwd_dkdv")
+    ap.add_argument("--traffic-command", default="")
     args = ap.parse_args(argv)
+    if args.traffic_from_pmc:
+        import workloads as W
+        rec = traffic_from_pmc(*args.traffic_from_pmc, args.traffic_kernel,
+                               W.CONFIGS[args.workload].name, args.traffic_command)
+        path = os.path.join(TRAFFIC_DIR, f"traffic_{rec['kernel']}_{rec['workload']}.json")
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -249,6 +337,17 @@ def main(argv=None) -> int:
                     "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
                     "avg_launch_us": round(1e3 * tot_ms / n, 3)}
+
+    if roofline is not None:
+        roofline["traffic"] = measured_traffic(roofline["kernel"], cfg.name)
+
+    if args.copy_calibration:
+        src = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
