@@ -190,6 +190,9 @@ def main(argv=None) -> int:
     ap.add_argument("--seeds", default="0,1,2,3,4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--recompute", action="store_true",
+                    help="give the backward its minimum workspace (no dS stash: dQ recomputes "
+                         "the scores)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run three device-to-device copies of 512 MiB (the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -247,8 +250,9 @@ def main(argv=None) -> int:
         t["wsf"] = torch.empty(max(1, M.docmask_gqa_fwd_workspace_size(B, S, Skv, Hq, Hkv, D,
                                                                       cfg.cp_size)),
                                dtype=torch.uint8, device=dev)
-        t["wsb"] = torch.empty(max(1, M.docmask_gqa_bwd_workspace_size(B, S, Skv, Hq, Hkv, D,
-                                                                      cfg.cp_size)),
+        wsb_size = (M.docmask_gqa_bwd_workspace_size_min if args.recompute
+                    else M.docmask_gqa_bwd_workspace_size)
+        t["wsb"] = torch.empty(max(1, wsb_size(B, S, Skv, Hq, Hkv, D, cfg.cp_size)),
                                dtype=torch.uint8, device=dev)
         pairs = sum(allowed_pairs(l, S, cfg.cp_size, rank) for l in case.lengths)
         runs.append(dict(case=case, t=t, pairs=pairs,
@@ -370,7 +374,9 @@ def main(argv=None) -> int:
                    "cp_rank": rank, "seq_len": cfg.S, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
                    "head_dim": cfg.D, "global_batch": cfg.B, "seeds": seeds,
                    "parallelism": "one CP rank's share on one GPU",
-                   "launch": "hip graph per seed" if args.graph else "eager"},
+                   "launch": "hip graph per seed" if args.graph else "eager",
+                   "backward": "recompute (minimum workspace)" if args.recompute
+                               else "dS stash"},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "per_seed_tflops": [round(x, 2) for x in per_seed],
         "median_seed_tflops": round(float(np.median(per_seed)), 2),

@@ -34,6 +34,7 @@ _f32 = ctypes.c_float
 SIGNATURES = {
     "docmask_gqa_fwd_workspace_size": (_sz, [_i32] * 7),
     "docmask_gqa_bwd_workspace_size": (_sz, [_i32] * 7),
+    "docmask_gqa_bwd_workspace_size_min": (_sz, [_i32] * 7),
     "docmask_gqa_attn_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp,
                                             _sz, _vp]),
@@ -88,6 +89,10 @@ def docmask_gqa_fwd_workspace_size(B, S, Skv, Hq, Hkv, D, cp_size) -> int:
 
 def docmask_gqa_bwd_workspace_size(B, S, Skv, Hq, Hkv, D, cp_size) -> int:
     return int(lib().docmask_gqa_bwd_workspace_size(B, S, Skv, Hq, Hkv, D, cp_size))
+
+
+def docmask_gqa_bwd_workspace_size_min(B, S, Skv, Hq, Hkv, D, cp_size) -> int:
+    return int(lib().docmask_gqa_bwd_workspace_size_min(B, S, Skv, Hq, Hkv, D, cp_size))
 
 
 def _ptr(t) -> Optional[int]:

@@ -3,6 +3,7 @@
 // argument contract are documented in include/docmask_gqa.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -65,9 +66,31 @@ int check_docs_args(const int32_t* doc_ids, const int32_t* cu, int n_docs, const
 
 // Workspace layout.
 struct Layout {
-  size_t dstart, dend, agg, rowstat, hdr, tile_info, items, partial, total;
+  size_t dstart, dend, agg, rowstat, hdr, tile_info, items, tile_rows, partial, stash, total_min,
+      total;
   int nkt, max_split_base;
+  int stash_kvh_blocks;   // stash blocks reserved per KV head
 };
+
+// Upper bound, over all document layouts, of the dS stash blocks of one KV
+// head: a key tile starting at t0 reaches at most the local tokens with
+// positions in [t0, S), a contiguous range [tlo, thi) of local tokens, i.e.
+// query rows [tlo*G, thi*G) covered by blocks of kStashRows rows.
+long long stash_blocks_bound(const Shape& s, int nkt) {
+  const long long baseA = (long long)s.rank * s.c;
+  const long long baseB = (long long)(2 * s.cp - 1 - s.rank) * s.c;
+  long long total = 0;
+  for (int kt = 0; kt < nkt; ++kt) {
+    const long long t0 = (long long)kt * kDkdvBN;
+    const long long la = std::min<long long>(std::max<long long>(t0 - baseA, 0), s.c);
+    const long long lb = std::min<long long>(std::max<long long>(t0 - baseB, 0), s.c);
+    const long long na = s.c - la, nb = s.c - lb;
+    const long long tlo = na > 0 ? la : s.c + lb;
+    const long long thi = nb > 0 ? 2LL * s.c : la + na;
+    if (thi > tlo) total += (thi * s.G + kStashRows - 1) / kStashRows - tlo * s.G / kStashRows;
+  }
+  return total * s.B;
+}
 
 Layout layout(const Shape& s, bool backward) {
   Layout L{};
@@ -85,10 +108,22 @@ Layout layout(const Shape& s, bool backward) {
     L.hdr = off; off = align_up(off + sizeof(SchedHeader));
     L.tile_info = off; off = align_up(off + ntiles * sizeof(int2));
     L.items = off; off = align_up(off + (ntiles + L.max_split_base) * sizeof(int2));
+    L.tile_rows = off; off = align_up(off + ntiles * sizeof(int4));
     const size_t slots = 2 * (size_t)L.max_split_base * s.Hkv;
     L.partial = off; off = align_up(off + slots * 2 * kDkdvBN * s.D * sizeof(float));
+    L.total_min = off;
+    const long long blocks = stash_blocks_bound(s, L.nkt);
+    // the dK/dV kernel addresses one tile's stash with 32-bit byte offsets
+    // below 2^31 (a tile holds at most ceil(Sq*G/32) + 1 blocks)
+    const long long tile_bytes =
+        ((long long)s.Sq * s.G / kStashRows + 2) * (long long)kStashBlockBytes;
+    L.stash_kvh_blocks = blocks < (1LL << 31) && tile_bytes < (1LL << 31) ? (int)blocks : -1;
+    L.stash = off;
+    if (L.stash_kvh_blocks >= 0)
+      off = align_up(off + (size_t)blocks * s.Hkv * kStashBlockBytes);
   }
   L.total = off;
+  if (!backward) L.total_min = off;
   return L;
 }
 
@@ -144,6 +179,15 @@ size_t docmask_gqa_bwd_workspace_size(int32_t B, int32_t S, int32_t Skv, int32_t
   return layout(s, true).total;
 }
 
+size_t docmask_gqa_bwd_workspace_size_min(int32_t B, int32_t S, int32_t Skv, int32_t Hq,
+                                          int32_t Hkv, int32_t D, int32_t cp_size) {
+  Shape s;
+  if (check_shape(B, S, S, Hq, Hkv, D, cp_size, 0, &s) != DMGQA_OK) return 0;
+  s.Skv = Skv > 0 && Skv <= S ? Skv : S;
+  if (s.empty) return 0;
+  return layout(s, true).total_min;
+}
+
 int docmask_gqa_attn_fwd(const void* q, const void* k, const void* v, const int32_t* doc_ids,
                          const int32_t* cu_seqlens, int32_t n_docs, int32_t B, int32_t S,
                          int32_t Skv, int32_t Hq, int32_t Hkv, int32_t D, int32_t cp_size,
@@ -197,7 +241,10 @@ int docmask_gqa_attn_bwd(const void* q, const void* k, const void* v, const void
   rc = check_docs_args(doc_ids, cu_seqlens, n_docs, s);
   if (rc != DMGQA_OK) return rc;
   const Layout L = layout(s, true);
-  if (workspace_bytes < L.total) return DMGQA_ERR_WORKSPACE;
+  if (workspace_bytes < L.total_min) return DMGQA_ERR_WORKSPACE;
+  // With room for the dS stash the dK/dV kernel stores dS and dQ is one
+  // product per key tile; else dQ recomputes S, P and dP.
+  const bool use_stash = L.stash_kvh_blocks >= 0 && workspace_bytes >= L.total;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
@@ -212,25 +259,47 @@ int docmask_gqa_attn_bwd(const void* q, const void* k, const void* v, const void
   SchedHeader* hdr = reinterpret_cast<SchedHeader*>(ws + L.hdr);
   int2* tile_info = reinterpret_cast<int2*>(ws + L.tile_info);
   int2* items = reinterpret_cast<int2*>(ws + L.items);
+  int4* tile_rows = reinterpret_cast<int4*>(ws + L.tile_rows);
   float* partial = reinterpret_cast<float*>(ws + L.partial);
+  u16* stash = use_stash ? reinterpret_cast<u16*>(ws + L.stash) : nullptr;
+  const u16* qh = static_cast<const u16*>(q);
+  const u16* kh = static_cast<const u16*>(k);
+  const u16* vh = static_cast<const u16*>(v);
+  const u16* oh = static_cast<const u16*>(out);
+  const u16* doh = static_cast<const u16*>(dout);
 
   timing_begin(kKSched, st);
-  hipError_t e = launch_sched_dkdv(dend, g, L.nkt, L.max_split_base, hdr, tile_info, items, st);
+  hipError_t e = launch_sched_dkdv(dend, g, L.nkt, L.max_split_base, hdr, tile_info, items,
+                                   tile_rows, st);
   timing_end(kKSched, st);
   if (e != hipSuccess) return DMGQA_ERR_HIP;
-  timing_begin(kKDq, st);
-  e = launch_bwd_dq(D, static_cast<const u16*>(q), static_cast<const u16*>(k),
-                    static_cast<const u16*>(v), static_cast<const u16*>(out),
-                    static_cast<const u16*>(dout), lse, dstart, static_cast<u16*>(dq), Lbuf, Nbuf,
-                    g, st);
-  timing_end(kKDq, st);
-  if (e != hipSuccess) return DMGQA_ERR_HIP;
-  timing_begin(kKDkdv, st);
-  e = launch_bwd_dkdv(D, static_cast<const u16*>(q), static_cast<const u16*>(k),
-                      static_cast<const u16*>(v), static_cast<const u16*>(dout), Lbuf, Nbuf, dend,
-                      hdr, tile_info, items, partial, dk, dv, g, L.nkt, st);
-  timing_end(kKDkdv, st);
-  if (e != hipSuccess) return DMGQA_ERR_HIP;
+  if (use_stash) {
+    timing_begin(kKRowstat, st);
+    e = launch_rowstat(D, oh, doh, lse, Lbuf, Nbuf, g, st);
+    timing_end(kKRowstat, st);
+    if (e != hipSuccess) return DMGQA_ERR_HIP;
+    timing_begin(kKDkdv, st);
+    e = launch_bwd_dkdv(D, qh, kh, vh, doh, Lbuf, Nbuf, dend, hdr, tile_info, items, tile_rows,
+                        stash, L.stash_kvh_blocks, partial, dk, dv, g, L.nkt, st);
+    timing_end(kKDkdv, st);
+    if (e != hipSuccess) return DMGQA_ERR_HIP;
+    timing_begin(kKDq, st);
+    e = launch_bwd_dq_stash(D, kh, dstart, tile_rows, stash, L.stash_kvh_blocks,
+                            static_cast<u16*>(dq), g, L.nkt, st);
+    timing_end(kKDq, st);
+    if (e != hipSuccess) return DMGQA_ERR_HIP;
+  } else {
+    timing_begin(kKDq, st);
+    e = launch_bwd_dq(D, qh, kh, vh, oh, doh, lse, dstart, static_cast<u16*>(dq), Lbuf, Nbuf, g,
+                      st);
+    timing_end(kKDq, st);
+    if (e != hipSuccess) return DMGQA_ERR_HIP;
+    timing_begin(kKDkdv, st);
+    e = launch_bwd_dkdv(D, qh, kh, vh, doh, Lbuf, Nbuf, dend, hdr, tile_info, items, tile_rows,
+                        nullptr, 0, partial, dk, dv, g, L.nkt, st);
+    timing_end(kKDkdv, st);
+    if (e != hipSuccess) return DMGQA_ERR_HIP;
+  }
   timing_begin(kKReduce, st);
   e = launch_bwd_reduce(D, tile_info, partial, dk, dv, g, L.nkt, st);
   timing_end(kKReduce, st);

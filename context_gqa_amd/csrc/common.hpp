@@ -14,6 +14,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace dmgqa {
 
@@ -194,6 +195,16 @@ __device__ __forceinline__ int mod_g(int x, const Geo& g) {
 // never reaches the next multiple of 1/G and the high word is floor(t/G).
 __device__ __forceinline__ int div_small(int t, const Geo& g) {
   return g.G == 1 ? t : (int)__umulhi((unsigned)t, g.g_magic);
+}
+
+// f(std::integral_constant<int, I>{}) for I = 0 .. N-1, unrolled at compile
+// time (for operands that must be immediates).
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
 }
 
 // A value the caller knows is the same in every lane, as a scalar.

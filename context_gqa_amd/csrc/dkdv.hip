@@ -39,6 +39,7 @@
 // each lane keeps the same row for all of a block's instructions.
 #include "common.hpp"
 #include "dma.hpp"
+
 #include <stdint.h>
 #include "kernels.hpp"
 
@@ -62,19 +63,26 @@ struct DkdvLds {
 typedef __attribute__((address_space(3))) char lds_char;
 
 // global_load_lds_dword{,x4} issued as inline assembly: lane l's 4 / 16
-// bytes at `g` go to LDS address lds + size * l (lds wave-uniform).  The
-// compiler does not see these as LDS writes, so it adds no waits of its own
-// for them (its conservative merge of in-flight DMA state at loop heads
-// would otherwise wait for the block just issued); the kernel orders every
-// read of a stage after an explicit vmcnt wait and a barrier instead.
-__device__ __forceinline__ void dma_lds16(const void* g, char* lds) {
-  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_char*)lds);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base)
+// bytes at sbase + voff + IMM go to LDS address lds + size * l (sbase and
+// lds wave-uniform, voff a 32-bit per-lane byte offset, so only one VGPR per
+// lane carries the address).  The instruction's immediate offset is added to
+// the LDS address too, so M0 is set to lds - IMM.  The compiler does not see these as LDS
+// writes, so it adds no waits of its own for them (its conservative merge of
+// in-flight DMA state at loop heads would otherwise wait for the block just
+// issued); the kernel orders every read of a stage after an explicit vmcnt
+// wait and a barrier instead.
+template <int IMM>
+__device__ __forceinline__ void dma_lds16(const void* sbase, unsigned voff, char* lds) {
+  const unsigned m0 =
+      __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_char*)lds) - (unsigned)IMM;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(voff),
+               "s"(sbase), "s"(m0), "i"(IMM)
                : "memory");
 }
-__device__ __forceinline__ void dma_lds4(const void* g, char* lds) {
-  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_char*)lds);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(base)
+__device__ __forceinline__ void dma_lds4(const void* sbase, unsigned voff, char* lds) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_char*)lds);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(m0)
                : "memory");
 }
 
@@ -119,12 +127,19 @@ __device__ __forceinline__ void dkdv_ranges(const int32_t* dend_b, int kt, const
   b0 = g.c + lb; nb = max(0, hb - lb);
 }
 
-template <int D>
+// STASH: also store dS (bf16) for the dQ product kernel.  Each wave's
+// 32 rows x 32 keys of dS are transposed through LDS (written key-major,
+// read with the transposed read) into 16-byte chunks of one row and 8 keys
+// in the MFMA slot order; chunk (key group kq of 16, lane 32h + i) of a
+// stash block holds row i of the block and keys 16kq + 8(e/4) + 4h + e%4,
+// so the dQ kernel loads each operand with one 16-byte read per lane.
+template <int D, bool STASH>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ dout, const float* __restrict__ Lbuf, const float* __restrict__ Nbuf,
     const int32_t* __restrict__ dend, SchedHeader* __restrict__ hdr,
     const int2* __restrict__ tile_info, const int2* __restrict__ items,
+    const int4* __restrict__ tile_rows, u16* __restrict__ stash, int stash_kvh_blocks,
     float* __restrict__ partial, float* __restrict__ dk, float* __restrict__ dv, Geo g, int nkt) {
   using Lds = DkdvLds<D>;
   constexpr int BN = kDkdvBN, KK = D / 16, DB = D / 32, NCH = D / 8;
@@ -132,8 +147,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) char st1[Lds::kStage];
   __shared__ __attribute__((aligned(1024))) char st2[Lds::kStage];
   __shared__ int s_item;
+  // per-wave transpose scratch of the dS stash: [32 keys][32 rows] bf16
+  // row stride 36: the key-major writes and the transposed reads are both
+  // spread over the 64 banks
+  constexpr int kTrLd = 36;
+  __shared__ __attribute__((aligned(16))) u16 s_tr[STASH ? 4 * 32 * kTrLd : 1];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int h = lane >> 5, i = lane & 31;
   const int total = hdr->n_base_items * g.Hkv;
   const int rps = hdr->rows_per_split;
@@ -236,22 +256,67 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       const int rr = 16 * wave + (lane >> 2);
       const unsigned ridx = row_index(rr);
       const int slot = lane & 3, xr = (rr >> 2) & 3;
-      const u16* qr = q + ridx * (unsigned)D + 8 * (slot ^ xr);
-      const u16* orow = dout + ridx * (unsigned)D + 8 * (slot ^ xr);
+      // byte offset of the row's chunk (q and dout share the layout; both
+      // stay below 4 GiB, which the host checks)
+      const unsigned qoff = (ridx * (unsigned)D + 8 * (slot ^ xr)) * 2u;
       char* tq = st + 64 * 16 * wave;
-#pragma unroll
-      for (int c = 0; c < NCH / 4; ++c) {
-        dma_lds16(qr + 32 * c, tq + c * kGroupBytes);
-        dma_lds16(orow + 32 * c, tq + Lds::kTile + c * kGroupBytes);
-      }
+      static_for<NCH / 4>([&](auto c) __attribute__((always_inline)) {
+        dma_lds16<64 * decltype(c)::value>(q, qoff, tq + decltype(c)::value * kGroupBytes);
+        dma_lds16<64 * decltype(c)::value>(dout, qoff,
+                                           tq + Lds::kTile + decltype(c)::value * kGroupBytes);
+      });
       // row statistics: lane = row (waves 0, 2: -lse/scale; 1, 3: -D)
       const unsigned ridm = row_index(lane);
-      const float* rs = (wave & 1) ? Nbuf : Lbuf;
-      dma_lds4(rs + ridm, st + ((wave & 1) ? Lds::kN : Lds::kL));
+      if (wave & 1)
+        dma_lds4(Nbuf, ridm * 4u, st + Lds::kN);
+      else
+        dma_lds4(Lbuf, ridm * 4u, st + Lds::kL);
       ++nx_blk;
       nx_ti += step_ti;
       nx_hh += step_hh;
       if (nx_hh >= g.G) { nx_hh -= g.G; ++nx_ti; }
+    };
+
+    // dS stash of this item's tile: virtual row vr is query row tlo*G + vr
+    // of the KV head (the tile's rows are the contiguous local tokens
+    // [tlo, thi)); block b of the tile covers rows [32(J_lo + b), +32).
+    // Stores go through a buffer resource spanning exactly the tile's
+    // blocks: a lane whose row lies past the item's end gets an offset
+    // beyond that range, which the hardware drops (no divergent branch).
+    const int4 trow = tile_rows[x];
+    const int tr_z = uniform(trow.z), tr_x = uniform(trow.x);
+    const int tile_blocks = uniform((trow.y * g.G + kStashRows - 1) / kStashRows - trow.z);
+    __amdgpu_buffer_rsrc_t srs;
+    if constexpr (STASH)
+      srs = __builtin_amdgcn_make_buffer_rsrc(
+          stash + ((size_t)kvh * stash_kvh_blocks + uniform(trow.w)) * (kStashBlockBytes / 2), 0,
+          tile_blocks * kStashBlockBytes, 0x00020000);
+    // (1) dS to this wave's transpose scratch, key-major: lane (h, i) holds
+    // key i at rows 16ks + 4h + 0..3 and 16ks + 8 + 4h + 0..3.
+    auto stash_put = [&](const bf16x8 (&dsop)[2]) __attribute__((always_inline)) {
+      u16* T = s_tr + wave * 32 * kTrLd;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const u32x4 w = __builtin_bit_cast(u32x4, dsop[ks]);
+        *reinterpret_cast<uint2*>(T + i * kTrLd + 16 * ks + 4 * h) = uint2{w[0], w[1]};
+        *reinterpret_cast<uint2*>(T + i * kTrLd + 16 * ks + 8 + 4 * h) = uint2{w[2], w[3]};
+      }
+    };
+    // (2) transposed read: lane (h, i) gets row i, keys 16kq + 8(e/4) + 4h +
+    // e%4, stored as chunk (2*wave + kq, lane) of the row's stash block.
+    // Done after the sub-block's products, when its operands are dead.
+    auto stash_store = [&](int R) __attribute__((always_inline)) {
+      const u16* T = s_tr + wave * 32 * kTrLd;
+      const int grow = tr_x * g.G + R + i;
+      const unsigned off = R + i < r_end ? (unsigned)(((grow >> 5) - tr_z) * kStashBlockBytes +
+                                                      (32 * h + (grow & 31)) * 16 + wave * 2048)
+                                         : 0x80000000u;
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) {
+        const bf16x8 op = tr_operand_pad<kTrLd>(T, 0, kq, 0, lane);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, op), srs, off + kq * 1024,
+                                               0, 0);
+      }
     };
 
     // One sub-block of 32 rows (rows q0.. of stage st, virtual rows from R).
@@ -273,15 +338,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) { sc[4 * r4 + e] = l4[e]; pc[4 * r4 + e] = n4[e]; }
       }
+      // Each phase's LDS operands are read up front and the phases are fenced
+      // (sched_barrier), so the reads are in flight while the previous
+      // phase's products run instead of one read before each product.
+      bf16x8 qa[KK], oa[KK];
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        sc = mfma32(ld_lds_b128(st + (kk >> 1) * kGroupBytes + 64 * q0 + off_b[kk & 1]), kop[kk],
-                    sc);
+        qa[kk] = ld_lds_b128(st + (kk >> 1) * kGroupBytes + 64 * q0 + off_b[kk & 1]);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        pc = mfma32(ld_lds_b128(st + Lds::kTile + (kk >> 1) * kGroupBytes + 64 * q0 +
-                                off_b[kk & 1]),
-                    vop[kk], pc);
+        oa[kk] = ld_lds_b128(st + Lds::kTile + (kk >> 1) * kGroupBytes + 64 * q0 + off_b[kk & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) sc = mfma32(qa[kk], kop[kk], sc);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) pc = mfma32(oa[kk], vop[kk], pc);
 
       float p[16];
 #pragma unroll
@@ -315,24 +387,37 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         }
       const char* tQ = st;
       const char* tO = st + Lds::kTile;
+      bf16x8 dot[2][DB];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) dot[ks][db] = tr_group(tO, off_t, q0, ks, db);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 dot = tr_group(tO, off_t, q0, ks, db);
-          dva[db] = mfma32(pop[ks], dot, dva[db]);
-          dva[db] = mfma32(plo[ks], dot, dva[db]);
+          dva[db] = mfma32(pop[ks], dot[ks][db], dva[db]);
+          dva[db] = mfma32(plo[ks], dot[ks][db], dva[db]);
         }
       bf16x8 dsop[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) dsop[ks][e] = (__bf16)(p[8 * ks + e] * pc[8 * ks + e]);
+      if constexpr (STASH) stash_put(dsop);
+      bf16x8 qt[2][DB];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) qt[ks][db] = tr_group(tQ, off_t, q0, ks, db);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          dka[db] = mfma32(dsop[ks], tr_group(tQ, off_t, q0, ks, db), dka[db]);
+          dka[db] = mfma32(dsop[ks], qt[ks][db], dka[db]);
+      if constexpr (STASH) stash_store(R);
     };
 
     // The first sub-block of block n waits for its DMA (issued two blocks
@@ -413,14 +498,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 hipError_t launch_bwd_dkdv(int D, const u16* q, const u16* k, const u16* v, const u16* dout,
                            const float* Lbuf, const float* Nbuf, const int32_t* dend,
                            SchedHeader* hdr, const int2* tile_info, const int2* items,
+                           const int4* tile_rows, u16* stash, int stash_kvh_blocks,
                            float* partial, float* dk, float* dv, const Geo& g, int nkt,
                            hipStream_t st) {
-  if (D == 128)
-    bwd_dkdv_kernel<128><<<kDkdvGrid, 256, 0, st>>>(q, k, v, dout, Lbuf, Nbuf, dend, hdr,
-                                                    tile_info, items, partial, dk, dv, g, nkt);
-  else
-    bwd_dkdv_kernel<64><<<kDkdvGrid, 256, 0, st>>>(q, k, v, dout, Lbuf, Nbuf, dend, hdr,
-                                                   tile_info, items, partial, dk, dv, g, nkt);
+#define DMGQA_DKDV(DD, SS)                                                                   \
+  bwd_dkdv_kernel<DD, SS><<<kDkdvGrid, 256, 0, st>>>(q, k, v, dout, Lbuf, Nbuf, dend, hdr,   \
+                                                     tile_info, items, tile_rows, stash,     \
+                                                     stash_kvh_blocks, partial, dk, dv, g, nkt)
+  if (D == 128) {
+    if (stash) DMGQA_DKDV(128, true); else DMGQA_DKDV(128, false);
+  } else {
+    if (stash) DMGQA_DKDV(64, true); else DMGQA_DKDV(64, false);
+  }
+#undef DMGQA_DKDV
   return hipGetLastError();
 }
 

@@ -1,0 +1,243 @@
+// dQ of document-masked causal GQA attention from the dS stash, and the
+// per-row statistics the dK/dV kernel needs.
+//
+// dQ = scale * dS K ("Training Infrastructure and Systems", "FlashAttention:
+// never write the score matrix" for the recomputation it replaces; the chain
+// rule as in the other backward kernels).  The dK/dV kernel, which computes
+// dS for every (query row, key) pair it visits, stores it as bf16 in stash
+// blocks of 32 query rows x 128 keys; this kernel is then a plain product
+// per KV head: for each 32-row block of query rows, the sum over the key
+// tiles that reach it of dS_block K_tile.  Without the stash, dQ has to
+// recompute S, P and dP (three products instead of one).
+#include "common.hpp"
+#include "dma.hpp"
+#include "kernels.hpp"
+#include "qtile.hpp"
+
+namespace dmgqa {
+
+namespace {
+
+// K tile of 128 keys in LDS: two halves of 64 keys, each in groups of four
+// 16-byte chunks (32 elements): group c/4 of key row r at (c/4)*4096 + 64*r,
+// chunk c in slot (c % 4) ^ ((r / 4) % 4) -- conflict-free for the
+// transposed reads (4 rows x 4 slots x two 8-byte halves per 32 lanes).
+constexpr int kHalfRows = 64;
+constexpr int kGroupBytes = kHalfRows * 64;
+
+template <int D>
+struct KTile {
+  static constexpr int kHalf = D / 32 * kGroupBytes;   // bytes of one 64-key half
+  static constexpr int kBytes = 2 * kHalf;
+};
+
+// K^T operand (lane 32h + i: column d = 32 db + i, keys of k-step ks of the
+// half in the MFMA slot order) from a half tile.
+__device__ __forceinline__ bf16x8 kt_operand(const char* half, const int (&off)[2], int ks,
+                                             int db) {
+  const char* p = half + db * kGroupBytes + 16 * ks * 64;
+  const i16x4 lo = ds_read_tr(reinterpret_cast<const u16*>(p + off[0]));
+  const i16x4 hi = ds_read_tr(reinterpret_cast<const u16*>(p + off[1]));
+  const bf16x4 a = __builtin_bit_cast(bf16x4, lo);
+  const bf16x4 b = __builtin_bit_cast(bf16x4, hi);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+}  // namespace
+
+// Per query row: -lse/scale (start value of the S accumulators of the dK/dV
+// kernel, so that P = exp2(scale*log2e * S)) and -D, D = <dO, O> (start
+// value of its dP accumulators, so that dS = P * dP).  D/8 lanes per row,
+// one 16-byte chunk of out and dout each.
+template <int D>
+__global__ __launch_bounds__(256) void rowstat_kernel(const u16* __restrict__ out,
+                                                      const u16* __restrict__ dout,
+                                                      const float* __restrict__ lse,
+                                                      float* __restrict__ Lbuf,
+                                                      float* __restrict__ Nbuf, int nrows,
+                                                      float inv_scale) {
+  constexpr int kLanes = D / 8;
+  const int row = blockIdx.x * (256 / kLanes) + (threadIdx.x / kLanes);
+  const int j = threadIdx.x % kLanes;
+  const int rr = min(row, nrows - 1);
+  const bf16x8 o = ld_bf16x8(out + (size_t)rr * D + 8 * j);
+  const bf16x8 d = ld_bf16x8(dout + (size_t)rr * D + 8 * j);
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)d[e], acc);
+#pragma unroll
+  for (int o2 = kLanes / 2; o2 > 0; o2 >>= 1) acc += __shfl_xor(acc, o2, kLanes);
+  if (j == 0 && row < nrows) {
+    Nbuf[row] = -acc;
+    Lbuf[row] = -lse[row] * inv_scale;
+  }
+}
+
+// One workgroup = 4 stash blocks (128 query rows of one KV head): wave w
+// owns block J = 4*qb + w.  Key tiles of 128 are those reaching any of the
+// 128 rows; their K tiles stream through two LDS stages (DMA one tile
+// ahead), and the wave's dS operands for the next tile are loaded into
+// registers one tile ahead.  Rows of a block outside the tile's reach hold
+// no stash data and are zeroed.
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
+    const u16* __restrict__ k, const int32_t* __restrict__ dstart,
+    const int4* __restrict__ tile_rows, const u16* __restrict__ stash, int stash_kvh_blocks,
+    u16* __restrict__ dq, Geo g, int nkt) {
+  using KT = KTile<D>;
+  constexpr int DB = D / 32, NCH = D / 8, BN = kDkdvBN;
+  __shared__ __attribute__((aligned(1024))) char sk0[KT::kBytes];
+  __shared__ __attribute__((aligned(1024))) char sk1[KT::kBytes];
+
+  const int nrows = g.Sq * g.G;
+  const int nqb = (nrows + 127) / 128;
+  const int nbg = g.B * g.Hkv;
+  const int qb = nqb - 1 - (int)(blockIdx.x / nbg);     // heavy (late) row blocks first
+  const int bg = blockIdx.x % nbg;
+  const int b = bg / g.Hkv, kvh = bg % g.Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, i = lane & 31;
+  const int J = 4 * qb + wave;                 // this wave's 32-row block
+  const int grow = 32 * J + i;                 // this lane's query row (in the KV head)
+
+  // transposed-read offsets (row quad index h, +2 for the second half)
+  const int s16 = lane & 15, grp = lane >> 4;
+  int off_t[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+    off_t[hf] = (4 * h + (s16 >> 2) + 8 * hf) * 64 +
+                16 * ((2 * (grp & 1) + ((s16 & 3) >> 1)) ^ ((h + 2 * hf) & 3)) + 8 * (s16 & 1);
+
+  const int32_t* ds = dstart + (size_t)b * g.Skv;
+  const QTileKeys kr = qtile_keys<128, BN>(128 * qb, ds, g);
+  const int ntiles = kr.na + kr.nb;
+  const size_t kvstride = (size_t)g.Hkv * D;
+  const u16* kbase = k + (size_t)b * g.Skv * kvstride + (size_t)kvh * D;
+  const int4* trow_b = tile_rows + (size_t)b * nkt;
+  const u16* stash_h = stash + (size_t)kvh * stash_kvh_blocks * (kStashBlockBytes / 2);
+
+  // K tile DMA: wave w fills key rows 16w .. 16w+15 of both halves
+  const int kr_row = 16 * wave + (lane >> 2);
+  const int slot = lane & 3, xr = (kr_row >> 2) & 3;
+  auto issue = [&](int it, char* st) __attribute__((always_inline)) {
+    const int kt = it < kr.na ? kr.a0 + it : kr.b0 + (it - kr.na);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int key = min(kt * BN + 64 * hf + kr_row, g.Skv - 1);
+      const u16* src = kbase + (size_t)key * kvstride + 8 * (slot ^ xr);
+      char* dst = st + hf * KT::kHalf + 64 * 16 * wave;
+#pragma unroll
+      for (int c = 0; c < NCH / 4; ++c)
+        dma16(src + 32 * c, reinterpret_cast<u16*>(dst + c * kGroupBytes));
+    }
+  };
+  // dS operands of this wave's block for tile `it`, loaded one tile ahead
+  // of their use.  `have`: the tile's stash holds block J; `part`: some rows
+  // of the block lie outside the tile's reach (their stash rows are never
+  // written and are replaced by zeros at use); `ok`: this lane's row does not.
+  struct DsOps {
+    u32x4 op[8];
+    bool have, part, ok;
+  };
+  auto load_ds = [&](int it, DsOps& d) __attribute__((always_inline)) {
+    const int kt = it < kr.na ? kr.a0 + it : kr.b0 + (it - kr.na);
+    const int4 tr = trow_b[kt];
+    const int nblk = tr.y > tr.x ? (tr.y * g.G + kStashRows - 1) / kStashRows - tr.z : 0;
+    const int rel = J - tr.z;
+    d.have = rel >= 0 && rel < nblk;
+    d.part = !(tr.x * g.G <= 32 * J && 32 * J + 32 <= tr.y * g.G);
+    d.ok = grow >= tr.x * g.G && grow < tr.y * g.G;
+    if (d.have) {
+      const u16* src = stash_h + (size_t)(tr.w + rel) * (kStashBlockBytes / 2) + lane * 8;
+#pragma unroll
+      for (int kq = 0; kq < 8; ++kq) d.op[kq] = *reinterpret_cast<const u32x4*>(src + kq * 512);
+    }
+  };
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = zero16();
+
+  // One barrier per key tile: wait for this tile's K and dS (issued during
+  // the previous tile), barrier (every wave's K loads are in and every wave
+  // is done with the previous tile), start the next tile's K and dS loads,
+  // multiply.
+  auto step = [&](int it, const char* cur, char* nxt, DsOps& dc, DsOps& dn)
+                  __attribute__((always_inline)) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (it + 1 < ntiles) {
+      issue(it + 1, nxt);
+      load_ds(it + 1, dn);
+    }
+    if (dc.have) {
+      if (dc.part && !dc.ok) {
+#pragma unroll
+        for (int kq = 0; kq < 8; ++kq) dc.op[kq] = u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            acc[db] = mfma32(kt_operand(cur + hf * KT::kHalf, off_t, ks, db),
+                             __builtin_bit_cast(bf16x8, dc.op[4 * hf + ks]), acc[db]);
+    }
+  };
+  if (ntiles > 0) {
+    DsOps dA, dB;
+    issue(0, sk0);
+    load_ds(0, dA);
+    for (int it = 0; it < ntiles; it += 2) {
+      step(it, sk0, sk1, dA, dB);
+      if (it + 1 < ntiles) step(it + 1, sk1, sk0, dB, dA);
+    }
+  }
+
+  if (grow < nrows) {
+    const int tok = grow / g.G, hh = grow - tok * g.G;
+    u16* orow = dq + (((size_t)b * g.Sq + tok) * g.Hq + kvh * g.G + hh) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[db][4 * r4 + e] * g.scale);
+        *reinterpret_cast<uint2*>(orow + 32 * db + 8 * r4 + 4 * h) = __builtin_bit_cast(uint2, w);
+      }
+  }
+}
+
+hipError_t launch_rowstat(int D, const u16* out, const u16* dout, const float* lse, float* Lbuf,
+                          float* Nbuf, const Geo& g, hipStream_t st) {
+  const int nrows = g.B * g.Sq * g.Hq;
+  const int rows_per_block = 256 / (D / 8);
+  const unsigned grid = (unsigned)((nrows + rows_per_block - 1) / rows_per_block);
+  if (D == 128)
+    rowstat_kernel<128><<<grid, 256, 0, st>>>(out, dout, lse, Lbuf, Nbuf, nrows, 1.f / g.scale);
+  else
+    rowstat_kernel<64><<<grid, 256, 0, st>>>(out, dout, lse, Lbuf, Nbuf, nrows, 1.f / g.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_stash(int D, const u16* k, const int32_t* dstart, const int4* tile_rows,
+                               const u16* stash, int stash_kvh_blocks, u16* dq, const Geo& g,
+                               int nkt, hipStream_t st) {
+  const int nqb = (g.Sq * g.G + 127) / 128;
+  const unsigned grid = (unsigned)nqb * g.B * g.Hkv;
+  if (D == 128)
+    bwd_dq_stash_kernel<128><<<grid, 256, 0, st>>>(k, dstart, tile_rows, stash, stash_kvh_blocks,
+                                                   dq, g, nkt);
+  else
+    bwd_dq_stash_kernel<64><<<grid, 256, 0, st>>>(k, dstart, tile_rows, stash, stash_kvh_blocks,
+                                                  dq, g, nkt);
+  return hipGetLastError();
+}
+
+}  // namespace dmgqa

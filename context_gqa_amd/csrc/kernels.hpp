@@ -21,6 +21,10 @@ constexpr int kDkdvBM = 64;
 constexpr int kMinRowsPerSplit = 512;
 constexpr int kMaxSplitTotal = 512;
 constexpr int kDkdvGrid = 256;  // persistent workgroups of the dK/dV kernel
+// dS stash: blocks of kStashRows query rows (aligned within each KV head's
+// row index tok*G + head) x kDkdvBN keys of one key tile, bf16.
+constexpr int kStashRows = 32;
+constexpr int kStashBlockBytes = kStashRows * kDkdvBN * 2;
 
 struct SchedHeader {
   int n_base_items;    // work items per KV head
@@ -35,7 +39,8 @@ hipError_t launch_prep_docs(const int32_t* doc, int B, int S, int Skv, int32_t* 
 hipError_t launch_prep_cu(const int32_t* cu, int n_docs, int Skv, int32_t* dstart, int32_t* dend,
                           hipStream_t st);
 hipError_t launch_sched_dkdv(const int32_t* dend, const Geo& g, int nkt, int max_split_base,
-                             SchedHeader* hdr, int2* tile_info, int2* items, hipStream_t st);
+                             SchedHeader* hdr, int2* tile_info, int2* items, int4* tile_rows,
+                             hipStream_t st);
 hipError_t launch_fwd(int D, const u16* q, const u16* k, const u16* v, const int32_t* dstart,
                       u16* out, float* lse, const Geo& g, hipStream_t st);
 hipError_t launch_bwd_dq(int D, const u16* q, const u16* k, const u16* v, const u16* out,
@@ -44,14 +49,20 @@ hipError_t launch_bwd_dq(int D, const u16* q, const u16* k, const u16* v, const 
 hipError_t launch_bwd_dkdv(int D, const u16* q, const u16* k, const u16* v, const u16* dout,
                            const float* Lbuf, const float* Nbuf, const int32_t* dend,
                            SchedHeader* hdr, const int2* tile_info, const int2* items,
+                           const int4* tile_rows, u16* stash, int stash_kvh_blocks,
                            float* partial, float* dk, float* dv, const Geo& g, int nkt,
                            hipStream_t st);
+hipError_t launch_rowstat(int D, const u16* out, const u16* dout, const float* lse, float* Lbuf,
+                          float* Nbuf, const Geo& g, hipStream_t st);
+hipError_t launch_bwd_dq_stash(int D, const u16* k, const int32_t* dstart, const int4* tile_rows,
+                               const u16* stash, int stash_kvh_blocks, u16* dq, const Geo& g,
+                               int nkt, hipStream_t st);
 hipError_t launch_bwd_reduce(int D, const int2* tile_info, const float* partial, float* dk,
                              float* dv, const Geo& g, int nkt, hipStream_t st);
 
 // Kernel timing (benchmark use): when enabled, each launch below is
 // bracketed by HIP events recorded on the launch stream.
-enum KernelId { kKPrep = 0, kKFwd, kKSched, kKDq, kKDkdv, kKReduce, kNumKernels };
+enum KernelId { kKPrep = 0, kKFwd, kKSched, kKDq, kKDkdv, kKReduce, kKRowstat, kNumKernels };
 void timing_begin(int kernel, hipStream_t st);
 void timing_end(int kernel, hipStream_t st);
 

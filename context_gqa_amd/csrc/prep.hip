@@ -157,6 +157,17 @@ __device__ void dkdv_tile_tokens(const int32_t* dend_b, int kt, const Geo& g, in
   token_ranges(t0, pe, g, a0, na, b0, nb);
 }
 
+// Stash blocks (kStashRows query rows x kDkdvBN keys of dS) of a key tile:
+// the tile reaches one contiguous range of local tokens [tlo, thi) (when it
+// reaches both chunks the first part runs to the end of the rank's first
+// chunk and the second starts at the beginning of the second), i.e. the
+// query rows [tlo*G, thi*G), which the blocks cover aligned to kStashRows.
+__device__ __forceinline__ int stash_blocks(int a0, int na, int b0, int nb, const Geo& g) {
+  const int tlo = na > 0 ? a0 : b0, thi = nb > 0 ? b0 + nb : a0 + na;
+  if (thi <= tlo) return 0;
+  return (thi * g.G + kStashRows - 1) / kStashRows - tlo * g.G / kStashRows;
+}
+
 // One block.  For every (batch, key tile): the number of query rows (local
 // tokens x group heads) that reach it; then a split of those rows into
 // pieces of `rows_per_split` (chosen so the total stays under kMaxSplitBase),
@@ -165,7 +176,8 @@ __global__ __launch_bounds__(kScanThreads) void sched_dkdv(const int32_t* __rest
                                                            int nkt, int max_split_base,
                                                            SchedHeader* __restrict__ hdr,
                                                            int2* __restrict__ tile_info,
-                                                           int2* __restrict__ items) {
+                                                           int2* __restrict__ items,
+                                                           int4* __restrict__ tile_rows) {
   __shared__ int sh[32];
   __shared__ long long red[16];
   const int ntiles = g.B * nkt;
@@ -199,7 +211,7 @@ __global__ __launch_bounds__(kScanThreads) void sched_dkdv(const int32_t* __rest
   if (threadIdx.x < 64) bucket_cnt[threadIdx.x] = 0;
   __syncthreads();
   auto remainder_class = [&](long long rem) { return 63 - (int)min(63LL, rem * 64 / rps); };
-  int my_full = 0, my_slots = 0;
+  int my_full = 0, my_slots = 0, my_blocks = 0;
   for (int x = first; x < min(first + per, ntiles); ++x) {
     const int b = x / nkt, kt = x % nkt;
     int a0, na, b0, nb;
@@ -210,18 +222,22 @@ __global__ __launch_bounds__(kScanThreads) void sched_dkdv(const int32_t* __rest
     const int ns = nf + ((rem > 0 || rows == 0) ? 1 : 0);
     my_full += nf;
     my_slots += ns > 1 ? ns : 0;
+    my_blocks += stash_blocks(a0, na, b0, nb, g);
     if (rem > 0 || rows == 0) atomicAdd(&bucket_cnt[remainder_class(rem)], 1);
   }
-  __shared__ int scan_i[kScanThreads], scan_s[kScanThreads];
+  __shared__ int scan_i[kScanThreads], scan_s[kScanThreads], scan_b[kScanThreads];
   scan_i[threadIdx.x] = my_full;
   scan_s[threadIdx.x] = my_slots;
+  scan_b[threadIdx.x] = my_blocks;
   __syncthreads();
   for (int o = 1; o < kScanThreads; o <<= 1) {
     int vi = threadIdx.x >= o ? scan_i[threadIdx.x - o] : 0;
     int vs = threadIdx.x >= o ? scan_s[threadIdx.x - o] : 0;
+    int vb = threadIdx.x >= o ? scan_b[threadIdx.x - o] : 0;
     __syncthreads();
     scan_i[threadIdx.x] += vi;
     scan_s[threadIdx.x] += vs;
+    scan_b[threadIdx.x] += vb;
     __syncthreads();
   }
   const int n_full = scan_i[kScanThreads - 1];
@@ -236,6 +252,7 @@ __global__ __launch_bounds__(kScanThreads) void sched_dkdv(const int32_t* __rest
   __syncthreads();
   int item = scan_i[threadIdx.x] - my_full;
   int slot = scan_s[threadIdx.x] - my_slots;
+  int sblk = scan_b[threadIdx.x] - my_blocks;
   int n_items_mine = 0;
   for (int x = first; x < min(first + per, ntiles); ++x) {
     const int b = x / nkt, kt = x % nkt;
@@ -247,6 +264,11 @@ __global__ __launch_bounds__(kScanThreads) void sched_dkdv(const int32_t* __rest
     const bool has_rem = rem > 0 || rows == 0;
     const int ns = nf + (has_rem ? 1 : 0);
     tile_info[x] = make_int2(ns, ns > 1 ? slot : -1);
+    {
+      const int tlo = na > 0 ? a0 : b0, thi = nb > 0 ? b0 + nb : a0 + na;
+      tile_rows[x] = make_int4(tlo, thi, tlo * g.G / kStashRows, sblk);
+      sblk += stash_blocks(a0, na, b0, nb, g);
+    }
     for (int s = 0; s < nf; ++s) items[item + s] = make_int2(x, s);
     item += nf;
     if (has_rem) {
@@ -292,8 +314,10 @@ hipError_t launch_prep_cu(const int32_t* cu, int n_docs, int Skv, int32_t* dstar
 }
 
 hipError_t launch_sched_dkdv(const int32_t* dend, const Geo& g, int nkt, int max_split_base,
-                             SchedHeader* hdr, int2* tile_info, int2* items, hipStream_t st) {
-  sched_dkdv<<<1, kScanThreads, 0, st>>>(dend, g, nkt, max_split_base, hdr, tile_info, items);
+                             SchedHeader* hdr, int2* tile_info, int2* items, int4* tile_rows,
+                             hipStream_t st) {
+  sched_dkdv<<<1, kScanThreads, 0, st>>>(dend, g, nkt, max_split_base, hdr, tile_info, items,
+                                         tile_rows);
   return hipGetLastError();
 }
 

@@ -76,7 +76,8 @@ enum {
                                   or zero softmax_scale, negative sizes */
   DMGQA_ERR_UNSUPPORTED = -2,  /* D not in {64, 128}; cu_seqlens with B > 1;
                                   sizes whose element offsets overflow */
-  DMGQA_ERR_WORKSPACE = -3,    /* workspace_bytes below the required size */
+  DMGQA_ERR_WORKSPACE = -3,    /* workspace_bytes below the required size
+                                  (for the backward: below the minimum) */
   DMGQA_ERR_HIP = -4           /* a HIP launch or runtime call failed */
 };
 
@@ -86,10 +87,24 @@ size_t docmask_gqa_fwd_workspace_size(int32_t B, int32_t S, int32_t Skv,
                                       int32_t Hq, int32_t Hkv, int32_t D,
                                       int32_t cp_size);
 
-/* Bytes of workspace the backward call needs. */
+/* Bytes of workspace for the fastest backward.  Besides the scheduling
+ * arrays it reserves a stash for dS in bf16 (blocks of 32 query rows x 128
+ * keys, for every key tile and the query rows that may reach it): the dK/dV
+ * kernel stores dS there and dQ = scale * dS K becomes one product per key
+ * tile instead of recomputing the scores.  The size is an upper bound over
+ * all document layouts (at most about Sq * Hq * Skv bytes; the layouts of a
+ * real batch use a fraction of it) and depends only on the sizes. */
 size_t docmask_gqa_bwd_workspace_size(int32_t B, int32_t S, int32_t Skv,
                                       int32_t Hq, int32_t Hkv, int32_t D,
                                       int32_t cp_size);
+
+/* Smallest workspace the backward accepts: without the dS stash, dQ
+ * recomputes the scores, P and dP (slower, same results up to rounding
+ * order).  Callers that cannot spare the stash pass any size from this one
+ * up to, but not including, docmask_gqa_bwd_workspace_size(). */
+size_t docmask_gqa_bwd_workspace_size_min(int32_t B, int32_t S, int32_t Skv,
+                                          int32_t Hq, int32_t Hkv, int32_t D,
+                                          int32_t cp_size);
 
 /* Forward: out = softmax(scale * q k^T, masked) v and lse for the rank's
  * local rows.  Exactly one of doc_ids / cu_seqlens is non-NULL; n_docs is

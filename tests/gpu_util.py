@@ -34,8 +34,17 @@ def gpu_fwd(case: W.Case, d, use_cu=False):
                                   cp_rank=case.rank, softmax_scale=case.scale, **kw)
 
 
-def gpu_bwd(case: W.Case, d, out, lse, use_cu=False):
+def gpu_bwd(case: W.Case, d, out, lse, use_cu=False, ws="stash"):
+    """ws = "stash": the workspace the library asks for (dS stash path);
+    "recompute": the minimum workspace (dQ recomputes S, P and dP)."""
     kw = {"cu_seqlens": d["cu_seqlens"]} if use_cu else {"doc_ids": d["doc_ids"]}
+    if ws == "recompute":
+        B, Sq, Hq, D = case.q.shape
+        n = M.docmask_gqa_bwd_workspace_size_min(B, Sq * case.cfg.cp_size, case.Skv, Hq,
+                                                 case.cfg.Hkv, D, case.cfg.cp_size)
+        kw["workspace"] = torch.empty(max(n, 1), dtype=torch.uint8, device=d["q"].device)
+    else:
+        assert ws == "stash", ws
     return M.docmask_gqa_attn_bwd(d["q"], d["k"], d["v"], out, d["dout"], lse,
                                   cp_size=case.cfg.cp_size, cp_rank=case.rank,
                                   softmax_scale=case.scale, **kw)

@@ -46,6 +46,17 @@ def test_workspace_sizes():
     assert f(1, 8192, 8192, 16, 1, 96, 1) == 0           # unsupported D
     # independent of the document layout, monotone in the key length
     assert f(1, 131072, 102400, 16, 1, 128, 16) <= f(1, 131072, 131072, 16, 1, 128, 16)
+    # the minimum backward workspace (no dS stash) is below the full one and
+    # above the forward's; both are 0 for the same invalid shapes
+    bm = M.docmask_gqa_bwd_workspace_size_min
+    for shape in ((1, 8192, 8192, 16, 1, 128, 1), (1, 131072, 131072, 16, 1, 128, 16),
+                  (2, 4096, 4096, 32, 8, 64, 2)):
+        assert f(*shape) < bm(*shape) < b(*shape)
+    assert bm(1, 8190, 8190, 16, 1, 128, 4) == 0 and bm(1, 8192, 8192, 16, 3, 128, 1) == 0
+    # the stash reservation is a worst case over document layouts: with one
+    # key tile of 128 and 128 query rows it holds all 128 x 128 bf16 scores
+    one_tile = (1, 128, 128, 1, 1, 128, 1)
+    assert b(*one_tile) - bm(*one_tile) >= 128 * 128 * 2
 
 
 class _Buf:

@@ -58,14 +58,15 @@ def _small_case(cfg, seed, rank, lengths, Skv):
     return W.make_case(cfg, seed, rank, Skv=Skv, lengths=lengths)
 
 
+@pytest.mark.parametrize("ws", ["stash", "recompute"])
 @pytest.mark.parametrize("cid,cfg,seed,rank,lengths,Skv", SMALL, ids=[c[0] for c in SMALL])
-def test_small_full_oracle(cid, cfg, seed, rank, lengths, Skv):
+def test_small_full_oracle(cid, cfg, seed, rank, lengths, Skv, ws):
     case = _small_case(cfg, seed, rank, lengths, Skv)
-    say(f"[{cid}] B={case.cfg.B} S={case.cfg.S} cp={case.cfg.cp_size} rank={rank} "
+    say(f"[{cid} {ws}] B={case.cfg.B} S={case.cfg.S} cp={case.cfg.cp_size} rank={rank} "
         f"Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} Skv={case.Skv}")
     d = dev(case)
     out, lse = gpu_fwd(case, d)
-    dq, dk, dv = gpu_bwd(case, d, out, lse)
+    dq, dk, dv = gpu_bwd(case, d, out, lse, ws=ws)
     torch.cuda.synchronize()
     rdq, rdk, rdv, rout, rlse = oracle.attn_bwd(case.q, case.k, case.v, case.dout, case.doc_ids,
                                                 case.cfg.cp_size, rank, case.scale,
@@ -117,8 +118,11 @@ def test_empty_inputs():
 
 # ----------------------------------------------------------- full sizes
 
-FULL = [("llama8b", 0), ("tp405b", 0), ("long_cp", 0), ("long_cp", 7)] + \
-       [("short_docs", r) for r in range(4)] + [("single_doc", r) for r in range(4)]
+FULL = [("llama8b", 0, "stash"), ("tp405b", 0, "stash"), ("long_cp", 0, "stash"),
+        ("long_cp", 7, "stash")] + \
+       [("short_docs", r, "stash") for r in range(4)] + \
+       [("single_doc", r, "stash") for r in range(4)] + \
+       [("tp405b", 0, "recompute"), ("long_cp", 7, "recompute"), ("single_doc", 3, "recompute")]
 
 _full_cache = {}
 
@@ -173,15 +177,15 @@ def anchors_budget(case):
     return 3 * 128
 
 
-@pytest.mark.parametrize("name,rank", FULL, ids=[f"{n}_r{r}" for n, r in FULL])
-def test_full_size_sampled(name, rank):
+@pytest.mark.parametrize("name,rank,ws", FULL, ids=[f"{n}_r{r}_{w}" for n, r, w in FULL])
+def test_full_size_sampled(name, rank, ws):
     cfg = W.CONFIGS[name]
     case = W.make_case(cfg, 0, rank, full=_full_tensors(name, 0))
-    say(f"[{name} rank {rank}] S={cfg.S} cp={cfg.cp_size} Hq={cfg.Hq} Hkv={cfg.Hkv} "
+    say(f"[{name} rank {rank} {ws}] S={cfg.S} cp={cfg.cp_size} Hq={cfg.Hq} Hkv={cfg.Hkv} "
         f"D={cfg.D} Skv={case.Skv} docs={len(case.lengths[0])}")
     d = dev(case)
     out, lse = gpu_fwd(case, d)
-    dq, dk, dv = gpu_bwd(case, d, out, lse)
+    dq, dk, dv = gpu_bwd(case, d, out, lse, ws=ws)
     torch.cuda.synchronize()
     for nm, t in (("out", out), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
         assert torch.isfinite(t.float()).all(), nm
