@@ -97,7 +97,7 @@ def kernel_source_hash() -> str:
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel`, from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE measurement (profiles/traffic_<kernel>_<workload>.json,
-    written by profiles/traffic_from_pmc.py); None if there is none or the
+    written by `bench.py --traffic-from-pmc`); None if there is none or the
     kernels have changed since it was taken."""
     path = os.path.join(TRAFFIC_DIR, f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):

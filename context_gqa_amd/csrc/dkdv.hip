@@ -10,15 +10,25 @@
 // where the rows are the (token, query head) pairs of the KV head's group
 // that may attend to the key (GQA: the group's heads share the key).
 //
-// Work item: 128 keys of one KV head (wave w owns keys t0 + 32w .. +31) x a
-// slice of the query rows that reach them.  Rows are streamed through LDS in
-// blocks of 64 (3 stages, filled by global->LDS DMA two blocks ahead) and
-// processed in sub-blocks of 32.  Per sub-block and wave:
-//   S_j = Q_j K^T and dP_j = dO_j V^T  (MFMA; the accumulators start from
-//       -lse/scale and -D, so P = exp2(scale*log2e * S_j) and dS = P * dP_j
+// Work item: 128 keys of one KV head x a slice of the query rows that reach
+// them.  Eight waves (two per SIMD, so one wave's vector work runs under the
+// other's matrix work) each own 16 keys, t0 + 16w .. +15, and use
+// 16x16x32 MFMAs.  Rows are streamed through LDS in blocks of 64 (a ring of
+// 4 stages, filled by global->LDS DMA two blocks ahead, the DMA
+// instructions spread over the sub-blocks) and processed in sub-blocks of
+// 32.  Per sub-block and wave:
+//   S = Q K^T and dP = dO V^T      (MFMA; the accumulators start from
+//       -lse/scale and -D, so P = exp2(scale*log2e * S) and dS = P * dP
 //       take one multiply each)
-//   P, dS and their bf16 operands        (VALU, next to independent MFMAs)
-//   dV += P^T dO_j, dK += dS^T Q_j       (MFMA, transposed LDS reads)
+//   P, dS and their bf16 operands  (VALU)
+//   dV += P^T dO, dK += dS^T Q     (MFMA, transposed LDS reads)
+//
+// Lane layout (lane l = 16*g4 + j): the S / dP tiles are C[row][key] with
+// key = j; lane group g4 holds the rows 16t + 4*pi(g4) + r (t = 0, 1,
+// r = 0..3), pi swapping the two bits of g4.  Those 8 values are the A
+// operand (P^T, dS^T: key j, k-slot 8*g4 + e <-> row 16(e/4) + 4*pi(g4) +
+// e%4) of the dV / dK products with no data movement; pi puts the two lane
+// groups of each 32-lane half on row quads whose LDS slots do not collide.
 //
 // P enters dV as a bf16 hi + lo pair (16 significant bits): dV sums P over
 // every row of the group, and one bf16 rounding of P is not accurate enough
@@ -28,15 +38,17 @@
 // A tile holds 64 rows x D bf16 in groups of 4 sixteen-byte chunks (32
 // elements): group c/4 of row r occupies the 64 bytes at
 // (c/4) * 4096 + 64 * r, and inside them chunk c sits in slot
-// (c % 4) ^ ((r / 4) % 4).  On the 64 four-byte banks this makes both
-// access patterns conflict-free:
-//   - ds_read_b128 of one chunk by 16 consecutive rows: bank =
-//     16*(r%4) + 4*slot, and the slot differs across the four row quads;
-//   - ds_read_b64_tr_b16 (rows r..r+3 of a quad x 4 chunks of a group x two
-//     8-byte halves, 32 lanes a cycle): 4 rows x 4 slots x 2 halves.
-// A DMA instruction fills one chunk group of 16 rows (lane l: row 16w + l/4,
-// slot l % 4): every lane loads 16 bytes of its row from a 64-byte run, and
-// each lane keeps the same row for all of a block's instructions.
+// (c % 4) ^ ((r / 4) % 4).  On the 64 four-byte banks both access patterns
+// are conflict-free:
+//   - ds_read_b128 of one chunk by 16 rows (any order of 16 aligned rows):
+//     bank = 16*(r%4) + 4*slot, and the slot differs across the row quads;
+//   - ds_read_b64_tr_b16 (per 16-lane group: 4 rows of a quad x 2 chunks x
+//     two 8-byte halves; the two groups of a 32-lane half read quads whose
+//     XOR key differs by 2, so their slot pairs are disjoint).
+// A DMA instruction fills one chunk group of 16 rows (lane l: row
+// 16*(w%4) + l/4, slot l % 4): every lane loads 16 bytes of its row from a
+// 64-byte run, and each lane keeps the same row for all of a block's
+// instructions.
 #include "common.hpp"
 #include "dma.hpp"
 
@@ -49,6 +61,8 @@ namespace {
 
 constexpr int kBlkRows = kDkdvBM;                    // 64 query rows per LDS stage
 constexpr int kGroupBytes = kBlkRows * 64;           // one chunk group of a tile
+constexpr int kWaves = 8;
+constexpr int kWaveKeys = kDkdvBN / kWaves;          // 16 keys per wave
 
 template <int D>
 struct DkdvLds {
@@ -57,7 +71,9 @@ struct DkdvLds {
   static constexpr int kL = 2 * kTile;               // -lse/scale per row
   static constexpr int kN = kL + kBlkRows * 4;       // -D per row
   static constexpr int kStage = kN + kBlkRows * 4;
-  static constexpr int kDmaPerWave = kChunks / 2 + 1;  // per block: Q, dO share + one row stat
+  // DMA instructions per block and wave: D/64 chunk groups each of Q and
+  // dO, and one row-statistics load (16 lanes)
+  static constexpr int kDmaPerWave = 2 * (D / 64) + 1;
 };
 
 typedef __attribute__((address_space(3))) char lds_char;
@@ -66,11 +82,11 @@ typedef __attribute__((address_space(3))) char lds_char;
 // bytes at sbase + voff + IMM go to LDS address lds + size * l (sbase and
 // lds wave-uniform, voff a 32-bit per-lane byte offset, so only one VGPR per
 // lane carries the address).  The instruction's immediate offset is added to
-// the LDS address too, so M0 is set to lds - IMM.  The compiler does not see these as LDS
-// writes, so it adds no waits of its own for them (its conservative merge of
-// in-flight DMA state at loop heads would otherwise wait for the block just
-// issued); the kernel orders every read of a stage after an explicit vmcnt
-// wait and a barrier instead.
+// the LDS address too, so M0 is set to lds - IMM.  The compiler does not see
+// these as LDS writes, so it adds no waits of its own for them (its
+// conservative merge of in-flight DMA state at loop heads would otherwise
+// wait for the block just issued); the kernel orders every read of a stage
+// after an explicit vmcnt wait and a barrier instead.
 template <int IMM>
 __device__ __forceinline__ void dma_lds16(const void* sbase, unsigned voff, char* lds) {
   const unsigned m0 =
@@ -93,15 +109,16 @@ __device__ __forceinline__ f32x4 ld_lds_f32x4(const char* p) {
   return *reinterpret_cast<const f32x4*>(p);
 }
 
-// Operand for lane l = 32h + i holding column (32*db + i) of the rows that
-// register slot (h, e) pairs with in k-step ks (see common.hpp), from a tile
-// in the grouped layout above; lane_off[hf] is the per-lane part of the
-// address of the rows 8*hf .. 8*hf+3 of the 16-row step.
-__device__ __forceinline__ bf16x8 tr_group(const char* tile, const int (&lane_off)[2], int q0,
-                                           int ks, int db) {
-  const char* p = tile + db * kGroupBytes + (q0 + 16 * ks) * 64;
-  const i16x4 lo = ds_read_tr(reinterpret_cast<const u16*>(p + lane_off[0]));
-  const i16x4 hi = ds_read_tr(reinterpret_cast<const u16*>(p + lane_off[1]));
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// B operand of 32 rows x 16 columns from a tile in the grouped layout: two
+// transposed reads, at p (rows 4*pi(g4) + 0..3 of the sub-block) and 16
+// rows further.
+__device__ __forceinline__ bf16x8 tr_pair(const char* p) {
+  const i16x4 lo = ds_read_tr(reinterpret_cast<const u16*>(p));
+  const i16x4 hi = ds_read_tr(reinterpret_cast<const u16*>(p + 16 * 64));
   const bf16x4 a = __builtin_bit_cast(bf16x4, lo);
   const bf16x4 b = __builtin_bit_cast(bf16x4, hi);
   bf16x8 r;
@@ -128,13 +145,13 @@ __device__ __forceinline__ void dkdv_ranges(const int32_t* dend_b, int kt, const
 }
 
 // STASH: also store dS (bf16) for the dQ product kernel.  Each wave's
-// 32 rows x 32 keys of dS are transposed through LDS (written key-major,
-// read with the transposed read) into 16-byte chunks of one row and 8 keys
-// in the MFMA slot order; chunk (key group kq of 16, lane 32h + i) of a
-// stash block holds row i of the block and keys 16kq + 8(e/4) + 4h + e%4,
-// so the dQ kernel loads each operand with one 16-byte read per lane.
+// 32 rows x 16 keys of dS are transposed through LDS (written key-major,
+// read with the transposed read) into one 16-byte chunk per lane: chunk
+// (key group w, lane 32h + i) of a stash block holds row i of the block and
+// keys 16w + 8(e/4) + 4h + e%4, so the dQ kernel loads each operand with
+// one 16-byte read per lane.
 template <int D, bool STASH>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ dout, const float* __restrict__ Lbuf, const float* __restrict__ Nbuf,
     const int32_t* __restrict__ dend, SchedHeader* __restrict__ hdr,
@@ -142,37 +159,35 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int4* __restrict__ tile_rows, u16* __restrict__ stash, int stash_kvh_blocks,
     float* __restrict__ partial, float* __restrict__ dk, float* __restrict__ dv, Geo g, int nkt) {
   using Lds = DkdvLds<D>;
-  constexpr int BN = kDkdvBN, KK = D / 16, DB = D / 32, NCH = D / 8;
-  __shared__ __attribute__((aligned(1024))) char st0[Lds::kStage];
-  __shared__ __attribute__((aligned(1024))) char st1[Lds::kStage];
-  __shared__ __attribute__((aligned(1024))) char st2[Lds::kStage];
+  constexpr int BN = kDkdvBN, KS = D / 32, ND = D / 16;
+  // ring of 4 stages (kStage is a multiple of 256 bytes)
+  static_assert(Lds::kStage % 256 == 0, "stage alignment");
+  __shared__ __attribute__((aligned(1024))) char stg[4 * Lds::kStage];
   __shared__ int s_item;
-  // per-wave transpose scratch of the dS stash: [32 keys][32 rows] bf16
-  // row stride 36: the key-major writes and the transposed reads are both
-  // spread over the 64 banks
-  constexpr int kTrLd = 36;
-  __shared__ __attribute__((aligned(16))) u16 s_tr[STASH ? 4 * 32 * kTrLd : 1];
+  // per-wave transpose scratch of the dS stash: [16 keys][32 rows] bf16,
+  // row stride 40
+  constexpr int kTrLd = 40;
+  __shared__ __attribute__((aligned(16))) u16 s_tr[STASH ? kWaves * kWaveKeys * kTrLd : 1];
 
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-  const int h = lane >> 5, i = lane & 31;
+  const int g4 = lane >> 4, j = lane & 15;
+  const int pg = ((g4 & 1) << 1) | (g4 >> 1);   // row quad of lane group g4
   const int total = hdr->n_base_items * g.Hkv;
   const int rps = hdr->rows_per_split;
   const size_t kvstride = (size_t)g.Hkv * D;
   const float c2 = g.scale_log2;
 
-  // per-lane parts of the LDS addresses.  b128 operand (row i, chunk
-  // h + 2kk): slot (h + 2(kk&1)) ^ (i/4 % 4) = slot of even kk, ^2 for odd.
-  const int off_b[2] = {64 * i + 16 * (h ^ ((i >> 2) & 3)),
-                        64 * i + 16 * ((h ^ ((i >> 2) & 3)) ^ 2)};
-  // transposed operand: source lane s of 16-lane group grp reads row
-  // 4h + s/4 (+8 for the second half), chunk 2(grp&1) + (s&3)/2 of the
-  // group, 8-byte half s&1; the row quad index is h (+2).
-  const int s16 = lane & 15, grp = lane >> 4;
+  // b128 operand (A of S = Q K^T): lane l reads row sigma(j) = 4*pi(j/4) +
+  // j%4 of a 16-row step, chunk 4ks + g4 (slot g4 ^ pi(j/4)).
+  const int pj = (((j >> 2) & 1) << 1) | (j >> 3);
+  const int off_b = 64 * (4 * pj + (j & 3)) + 16 * (g4 ^ pj);
+  // transposed operand (B of dV, dK) for d tile nd: source lane j of group
+  // g4 reads row 4*pg + j/4 (+16), chunk 2(nd&1) + (j&3)/2 of chunk group
+  // nd/2, 8-byte half j&1.
   int off_t[2];
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
-    off_t[hf] = (4 * h + (s16 >> 2) + 8 * hf) * 64 +
-                16 * ((2 * (grp & 1) + ((s16 & 3) >> 1)) ^ ((h + 2 * hf) & 3)) + 8 * (s16 & 1);
+  for (int par = 0; par < 2; ++par)
+    off_t[par] = 64 * (4 * pg + (j >> 2)) + 16 * ((2 * par + ((j & 3) >> 1)) ^ pg) + 8 * (j & 1);
 
   for (;;) {
     if (threadIdx.x == 0) s_item = atomicAdd(&hdr->counter, 1);
@@ -194,16 +209,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int nsb = r_end > r_begin ? (r_end - r_begin + 31) / 32 : 0;
     const int nblk = (nsb + 1) / 2;
 
-    // this lane's key and its K / V operands
-    const int key = t0 + wave * 32 + i;
+    // this lane's key and its K / V operands (B of S = Q K^T, dP = dO V^T:
+    // lane l holds key j, elements 32ks + 8*g4 .. +7)
+    const int key = t0 + wave * kWaveKeys + j;
     const int kc = min(key, g.Skv - 1);
     const u16* krow = k + ((size_t)b * g.Skv + kc) * kvstride + (size_t)kvh * D;
     const u16* vrow = v + ((size_t)b * g.Skv + kc) * kvstride + (size_t)kvh * D;
-    bf16x8 kop[KK], vop[KK];
+    bf16x8 kop[KS], vop[KS];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      kop[kk] = ld_bf16x8(krow + 8 * h + 16 * kk);
-      vop[kk] = ld_bf16x8(vrow + 8 * h + 16 * kk);
+    for (int ks = 0; ks < KS; ++ks) {
+      kop[ks] = ld_bf16x8(krow + 32 * ks + 8 * g4);
+      vop[ks] = ld_bf16x8(vrow + 32 * ks + 8 * g4);
     }
 
     // Rows allowed for this key: local tokens with position in
@@ -224,12 +240,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         vr_hi = min(max(ti_hi * g.G, r_begin), r_end);
       }
     }
-    const int w_lo = __builtin_amdgcn_readlane(vr_lo, 31);
+    const int w_lo = __builtin_amdgcn_readlane(vr_lo, kWaveKeys - 1);
     const int w_hi = __builtin_amdgcn_readlane(vr_hi, 0);
 
-    f32x16 dka[DB], dva[DB];
+    f32x4 dka[ND], dva[ND];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) { dka[db] = zero16(); dva[db] = zero16(); }
+    for (int nd = 0; nd < ND; ++nd) {
+      dka[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dva[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     // Row bookkeeping of the next block to load: virtual row nx_vr0 =
     // nx_ti * G + nx_hh (uniform), advanced by kBlkRows per block.  Every
@@ -251,30 +270,49 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       const int tok = ti < na ? a0 + ti : b0 + (ti - na);
       return (unsigned)((b * g.Sq + tok) * g.Hq + kvh * g.G + hh);
     };
-    auto issue_block = [&](char* st) __attribute__((always_inline)) {
-      // tiles: wave w fills rows 16w .. 16w+15 of every chunk group
-      const int rr = 16 * wave + (lane >> 2);
+    // DMA of one block, in two parts so that its instructions can be spread
+    // over the block's two sub-blocks: prep_block computes this lane's row
+    // offsets and advances the row bookkeeping, issue_q starts Q and the row
+    // statistics, issue_o dO.
+    unsigned nx_qoff = 0, nx_ridm = 0;
+    auto prep_block = [&]() __attribute__((always_inline)) {
+      // tiles: wave w fills rows 16(w%4) .. +15 of chunk groups w/4 + 2m
+      const int rq = wave & 3, c0 = wave >> 2;
+      const int rr = 16 * rq + (lane >> 2);
       const unsigned ridx = row_index(rr);
       const int slot = lane & 3, xr = (rr >> 2) & 3;
       // byte offset of the row's chunk (q and dout share the layout; both
       // stay below 4 GiB, which the host checks)
-      const unsigned qoff = (ridx * (unsigned)D + 8 * (slot ^ xr)) * 2u;
-      char* tq = st + 64 * 16 * wave;
-      static_for<NCH / 4>([&](auto c) __attribute__((always_inline)) {
-        dma_lds16<64 * decltype(c)::value>(q, qoff, tq + decltype(c)::value * kGroupBytes);
-        dma_lds16<64 * decltype(c)::value>(dout, qoff,
-                                           tq + Lds::kTile + decltype(c)::value * kGroupBytes);
-      });
-      // row statistics: lane = row (waves 0, 2: -lse/scale; 1, 3: -D)
-      const unsigned ridm = row_index(lane);
-      if (wave & 1)
-        dma_lds4(Nbuf, ridm * 4u, st + Lds::kN);
-      else
-        dma_lds4(Lbuf, ridm * 4u, st + Lds::kL);
+      nx_qoff = (ridx * (unsigned)D + 32 * c0 + 8 * (slot ^ xr)) * 2u;
+      nx_ridm = row_index(16 * rq + (lane & 15));
       ++nx_blk;
       nx_ti += step_ti;
       nx_hh += step_hh;
       if (nx_hh >= g.G) { nx_hh -= g.G; ++nx_ti; }
+    };
+    auto issue_q = [&](char* st) __attribute__((always_inline)) {
+      const int rq = wave & 3, c0 = wave >> 2;
+      char* tq = st + 64 * 16 * rq + c0 * kGroupBytes;
+      static_for<D / 64>([&](auto m) __attribute__((always_inline)) {
+        constexpr int M = decltype(m)::value;
+        dma_lds16<128 * M>(q, nx_qoff, tq + 2 * M * kGroupBytes);
+      });
+      // row statistics, lanes 0..15: rows 16(w%4) + lane; waves 0-3 load
+      // -lse/scale, waves 4-7 -D
+      if (lane < 16) {
+        if (wave < 4)
+          dma_lds4(Lbuf, nx_ridm * 4u, st + Lds::kL + 64 * rq);
+        else
+          dma_lds4(Nbuf, nx_ridm * 4u, st + Lds::kN + 64 * rq);
+      }
+    };
+    auto issue_o = [&](char* st) __attribute__((always_inline)) {
+      const int rq = wave & 3, c0 = wave >> 2;
+      char* tq = st + Lds::kTile + 64 * 16 * rq + c0 * kGroupBytes;
+      static_for<D / 64>([&](auto m) __attribute__((always_inline)) {
+        constexpr int M = decltype(m)::value;
+        dma_lds16<128 * M>(dout, nx_qoff, tq + 2 * M * kGroupBytes);
+      });
     };
 
     // dS stash of this item's tile: virtual row vr is query row tlo*G + vr
@@ -291,181 +329,160 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       srs = __builtin_amdgcn_make_buffer_rsrc(
           stash + ((size_t)kvh * stash_kvh_blocks + uniform(trow.w)) * (kStashBlockBytes / 2), 0,
           tile_blocks * kStashBlockBytes, 0x00020000);
-    // (1) dS to this wave's transpose scratch, key-major: lane (h, i) holds
-    // key i at rows 16ks + 4h + 0..3 and 16ks + 8 + 4h + 0..3.
-    auto stash_put = [&](const bf16x8 (&dsop)[2]) __attribute__((always_inline)) {
-      u16* T = s_tr + wave * 32 * kTrLd;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const u32x4 w = __builtin_bit_cast(u32x4, dsop[ks]);
-        *reinterpret_cast<uint2*>(T + i * kTrLd + 16 * ks + 4 * h) = uint2{w[0], w[1]};
-        *reinterpret_cast<uint2*>(T + i * kTrLd + 16 * ks + 8 + 4 * h) = uint2{w[2], w[3]};
-      }
+    // (1) dS to this wave's transpose scratch, key-major: lane (g4, j) holds
+    // key j at rows 16t + 4*pg + 0..3.
+    auto stash_put = [&](const bf16x8& dsop) __attribute__((always_inline)) {
+      u16* T = s_tr + wave * kWaveKeys * kTrLd;
+      const u32x4 w4 = __builtin_bit_cast(u32x4, dsop);
+      *reinterpret_cast<uint2*>(T + j * kTrLd + 4 * pg) = uint2{w4[0], w4[1]};
+      *reinterpret_cast<uint2*>(T + j * kTrLd + 16 + 4 * pg) = uint2{w4[2], w4[3]};
     };
-    // (2) transposed read: lane (h, i) gets row i, keys 16kq + 8(e/4) + 4h +
-    // e%4, stored as chunk (2*wave + kq, lane) of the row's stash block.
-    // Done after the sub-block's products, when its operands are dead.
+    // (2) transposed read: lane (h, i) gets row i, keys 8(e/4) + 4h + e%4
+    // of the wave's 16, stored as chunk (w, lane) of the row's stash block.
     auto stash_store = [&](int R) __attribute__((always_inline)) {
-      const u16* T = s_tr + wave * 32 * kTrLd;
+      const u16* T = s_tr + wave * kWaveKeys * kTrLd;
+      const int i = lane & 31, h = lane >> 5;
       const int grow = tr_x * g.G + R + i;
       const unsigned off = R + i < r_end ? (unsigned)(((grow >> 5) - tr_z) * kStashBlockBytes +
-                                                      (32 * h + (grow & 31)) * 16 + wave * 2048)
+                                                      wave * 1024 + (32 * h + (grow & 31)) * 16)
                                          : 0x80000000u;
-#pragma unroll
-      for (int kq = 0; kq < 2; ++kq) {
-        const bf16x8 op = tr_operand_pad<kTrLd>(T, 0, kq, 0, lane);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, op), srs, off + kq * 1024,
-                                               0, 0);
-      }
+      const bf16x8 op = tr_operand_pad<kTrLd>(T, 0, 0, 0, lane);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, op), srs, off, 0, 0);
     };
 
-    // One sub-block of 32 rows (rows q0.. of stage st, virtual rows from R).
-    // Program order puts vector work next to matrix work it does not depend
-    // on: P = exp2(..) and its operands while the dP chain runs, dS and its
-    // operand while the dV products run.
-    auto body = [&](auto masked, const char* st, int q0, int R) __attribute__((always_inline)) {
-      // keeps the compiler from hoisting the loads both variants share above
-      // the branch that picks the variant (which would make them all live at once)
-      if constexpr (decltype(masked)::value)
-        asm volatile("; masked sub-block" ::: "memory");
-      else
-        asm volatile("; full sub-block" ::: "memory");
-      f32x16 sc, pc;
+    // S = Q K^T and dP = dO V^T of one sub-block (rows q0.. of stage st):
+    // the accumulators start at -lse/scale and -D of their rows.
+    auto sdp = [&](const char* st, int q0, f32x4 (&sc)[2], f32x4 (&pc)[2])
+                   __attribute__((always_inline)) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 l4 = ld_lds_f32x4(st + Lds::kL + 4 * (q0 + 8 * r4 + 4 * h));
-        const f32x4 n4 = ld_lds_f32x4(st + Lds::kN + 4 * (q0 + 8 * r4 + 4 * h));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { sc[4 * r4 + e] = l4[e]; pc[4 * r4 + e] = n4[e]; }
+      for (int t = 0; t < 2; ++t) {
+        sc[t] = ld_lds_f32x4(st + Lds::kL + 4 * (q0 + 16 * t + 4 * pg));
+        pc[t] = ld_lds_f32x4(st + Lds::kN + 4 * (q0 + 16 * t + 4 * pg));
       }
-      // Each phase's LDS operands are read up front and the phases are fenced
-      // (sched_barrier), so the reads are in flight while the previous
-      // phase's products run instead of one read before each product.
-      bf16x8 qa[KK], oa[KK];
+      bf16x8 qa[2][KS], oa[2][KS];
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        qa[kk] = ld_lds_b128(st + (kk >> 1) * kGroupBytes + 64 * q0 + off_b[kk & 1]);
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        oa[kk] = ld_lds_b128(st + Lds::kTile + (kk >> 1) * kGroupBytes + 64 * q0 + off_b[kk & 1]);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int ks = 0; ks < KS; ++ks) {
+          qa[t][ks] = ld_lds_b128(st + ks * kGroupBytes + 64 * (q0 + 16 * t) + off_b);
+          oa[t][ks] = ld_lds_b128(st + Lds::kTile + ks * kGroupBytes + 64 * (q0 + 16 * t) + off_b);
+        }
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) sc = mfma32(qa[kk], kop[kk], sc);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) pc = mfma32(oa[kk], vop[kk], pc);
+        for (int t = 0; t < 2; ++t) sc[t] = mfma16(qa[t][ks], kop[ks], sc[t]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) pc[t] = mfma16(oa[t][ks], vop[ks], pc[t]);
+    };
 
-      float p[16];
+    // The rest of a sub-block (virtual rows from R, rows q0.. of stage st)
+    // from its S and dP: P, dV += P^T dO, dS, dK += dS^T Q.
+    auto rest = [&](auto masked, const char* st, int q0, int R, const f32x4 (&sc)[2],
+                    const f32x4 (&pc)[2]) __attribute__((always_inline)) {
+      // p[4t + r]: row 16t + 4*pg + r of the sub-block, key j
+      float p[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(sc[r] * c2);
+      for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(sc[e >> 2][e & 3] * c2);
       if constexpr (decltype(masked)::value) {
-        // register r holds virtual row R + 4h + cr, cr = 8*(r/4) + r%4
-        const int lo_rel = vr_lo - R - 4 * h;
+        const int lo_rel = vr_lo - R - 4 * pg;
         const unsigned span = (unsigned)max(vr_hi - vr_lo, 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int cr = 8 * (r >> 2) + (r & 3);
-          if ((unsigned)(cr - lo_rel) >= span) p[r] = 0.f;
+        for (int e = 0; e < 8; ++e) {
+          const int cr = 16 * (e >> 2) + (e & 3);
+          if ((unsigned)(cr - lo_rel) >= span) p[e] = 0.f;
         }
       }
       // hi = bf16(P) (round to nearest even, one conversion per pair), lo =
       // bf16(P - hi), with hi widened back to fp32 by a shift / mask
-      bf16x8 pop[2], plo[2];
+      bf16x8 pop, plo;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = p[e], p1 = p[e + 1];
+        const bf16x2 hp = {(__bf16)p0, (__bf16)p1};
+        const unsigned hw = __builtin_bit_cast(unsigned, hp);
+        const float h0 = __builtin_bit_cast(float, hw << 16);
+        const float h1 = __builtin_bit_cast(float, hw & 0xffff0000u);
+        pop[e] = hp[0];
+        pop[e + 1] = hp[1];
+        plo[e] = (__bf16)(p0 - h0);
+        plo[e + 1] = (__bf16)(p1 - h1);
+      }
+      const char* tQ = st + 64 * q0;
+      const char* tO = st + Lds::kTile + 64 * q0;
+      bf16x8 dot[ND];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = p[8 * ks + e], p1 = p[8 * ks + e + 1];
-          const bf16x2 hp = {(__bf16)p0, (__bf16)p1};
-          const unsigned hw = __builtin_bit_cast(unsigned, hp);
-          const float h0 = __builtin_bit_cast(float, hw << 16);
-          const float h1 = __builtin_bit_cast(float, hw & 0xffff0000u);
-          pop[ks][e] = hp[0];
-          pop[ks][e + 1] = hp[1];
-          plo[ks][e] = (__bf16)(p0 - h0);
-          plo[ks][e + 1] = (__bf16)(p1 - h1);
-        }
-      const char* tQ = st;
-      const char* tO = st + Lds::kTile;
-      bf16x8 dot[2][DB];
+      for (int nd = 0; nd < ND; ++nd) dot[nd] = tr_pair(tO + (nd >> 1) * kGroupBytes + off_t[nd & 1]);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int nd = 0; nd < ND; ++nd) {
+        dva[nd] = mfma16(pop, dot[nd], dva[nd]);
+        dva[nd] = mfma16(plo, dot[nd], dva[nd]);
+      }
+      bf16x8 dsop;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) dot[ks][db] = tr_group(tO, off_t, q0, ks, db);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          dva[db] = mfma32(pop[ks], dot[ks][db], dva[db]);
-          dva[db] = mfma32(plo[ks], dot[ks][db], dva[db]);
-        }
-      bf16x8 dsop[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dsop[ks][e] = (__bf16)(p[8 * ks + e] * pc[8 * ks + e]);
+      for (int e = 0; e < 8; ++e) dsop[e] = (__bf16)(p[e] * pc[e >> 2][e & 3]);
       if constexpr (STASH) stash_put(dsop);
-      bf16x8 qt[2][DB];
+      bf16x8 qt[ND];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int nd = 0; nd < ND; ++nd) qt[nd] = tr_pair(tQ + (nd >> 1) * kGroupBytes + off_t[nd & 1]);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) qt[ks][db] = tr_group(tQ, off_t, q0, ks, db);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          dka[db] = mfma32(dsop[ks], qt[ks][db], dka[db]);
+      for (int nd = 0; nd < ND; ++nd) dka[nd] = mfma16(dsop, qt[nd], dka[nd]);
       if constexpr (STASH) stash_store(R);
     };
 
-    // The first sub-block of block n waits for its DMA (issued two blocks
-    // earlier; only block n+1's may still be in flight), then - past the
-    // barrier, which also retires every read of block n-1 - starts the DMA
-    // of block n+2 into block n-1's stage.  K/V operands and the key bounds
-    // must have arrived before the DMA stream starts, so that no wait inside
-    // the loop has to count them.
-    wait_vmcnt<0>();
-    if (nblk > 0) {
-      issue_block(st0);
-      issue_block(st1);
-    }
-    int j = 0;
-    auto step = [&](const char* st, int q0, char* dst, auto first) __attribute__((always_inline)) {
-      if constexpr (decltype(first)::value) {
-        wait_vmcnt<Lds::kDmaPerWave>();
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        issue_block(dst);
-      }
-      const int R = r_begin + 32 * j;
-      if (w_lo <= R && R + 32 <= w_hi)
-        body(std::false_type{}, st, q0, R);
-      else
-        body(std::true_type{}, st, q0, R);
-      ++j;
+    // Sub-block j lives in stage (j/2) % 4 at row 32*(j%2).  Block n+2's
+    // DMA is issued during block n, after the barrier that opens it (Q and
+    // row statistics in its first sub-block, dO in its second); that
+    // barrier also guarantees every wave has finished block n-1.  Every
+    // wait counts one block's instructions: block n's DMA must be done,
+    // block n+1's may be in flight.  A last block with a single sub-block
+    // skips the dO part; no wait follows it.
+    auto stage = [&](int blk) __attribute__((always_inline)) -> char* {
+      return stg + (blk & 3) * Lds::kStage;
     };
-    while (j < nsb) {
-      step(st0, 0, st2, std::true_type{});
-      if (j >= nsb) break;
-      step(st0, 32, st2, std::false_type{});
-      if (j >= nsb) break;
-      step(st1, 0, st0, std::true_type{});
-      if (j >= nsb) break;
-      step(st1, 32, st0, std::false_type{});
-      if (j >= nsb) break;
-      step(st2, 0, st1, std::true_type{});
-      if (j >= nsb) break;
-      step(st2, 32, st1, std::false_type{});
+    wait_vmcnt<0>();
+    if (nsb > 0) {
+      prep_block();
+      issue_q(stage(0));
+      issue_o(stage(0));
+      prep_block();
+      issue_q(stage(1));
+      issue_o(stage(1));
+    }
+    for (int jb = 0; 2 * jb < nsb; ++jb) {
+      wait_vmcnt<Lds::kDmaPerWave>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      prep_block();
+      const char* st = stage(jb);
+      char* nx = stage(jb + 2);
+      auto sub_block = [&](auto second) __attribute__((always_inline)) {
+        constexpr int h2 = decltype(second)::value ? 1 : 0;
+        const int R = r_begin + 64 * jb + 32 * h2;
+        f32x4 sc[2], pc[2];
+        sdp(st, 32 * h2, sc, pc);
+        // DMA instructions of a later block, while the products run
+        if constexpr (h2 == 0)
+          issue_q(nx);
+        else
+          issue_o(nx);
+        if (w_lo <= R && R + 32 <= w_hi)
+          rest(std::false_type{}, st, 32 * h2, R, sc, pc);
+        else
+          rest(std::true_type{}, st, 32 * h2, R, sc, pc);
+      };
+      sub_block(std::false_type{});
+      if (2 * jb + 1 < nsb) sub_block(std::true_type{});
     }
 
     // No DMA (including the re-loads past the item's end) may still be
     // writing LDS once the item is done.
     wait_vmcnt<0>();
 
-    // Write this wave's 32 keys: directly (dK scaled) if the tile was not
-    // split, else to the item's partial-sum slot.
+    // Write this wave's 16 keys: directly (dK scaled) if the tile was not
+    // split, else to the item's partial-sum slot.  Register r of d tile nd
+    // holds key 16w + 4*g4 + r, element 16nd + j.
     const int2 info = tile_info[x];
     const bool split_tile = info.x > 1;
     float* dst_k;
@@ -483,13 +500,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     }
     const float kscale = split_tile ? 1.f : g.scale;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int nd = 0; nd < ND; ++nd)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kvloc = wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      for (int r = 0; r < 4; ++r) {
+        const int kvloc = wave * kWaveKeys + 4 * g4 + r;
         if (split_tile || t0 + kvloc < g.Skv) {
-          dst_k[(size_t)kvloc * rstride + 32 * db + i] = dka[db][r] * kscale;
-          dst_v[(size_t)kvloc * rstride + 32 * db + i] = dva[db][r];
+          dst_k[(size_t)kvloc * rstride + 16 * nd + j] = dka[nd][r] * kscale;
+          dst_v[(size_t)kvloc * rstride + 16 * nd + j] = dva[nd][r];
         }
       }
   }
@@ -501,10 +518,10 @@ hipError_t launch_bwd_dkdv(int D, const u16* q, const u16* k, const u16* v, cons
                            const int4* tile_rows, u16* stash, int stash_kvh_blocks,
                            float* partial, float* dk, float* dv, const Geo& g, int nkt,
                            hipStream_t st) {
-#define DMGQA_DKDV(DD, SS)                                                                   \
-  bwd_dkdv_kernel<DD, SS><<<kDkdvGrid, 256, 0, st>>>(q, k, v, dout, Lbuf, Nbuf, dend, hdr,   \
-                                                     tile_info, items, tile_rows, stash,     \
-                                                     stash_kvh_blocks, partial, dk, dv, g, nkt)
+#define DMGQA_DKDV(DD, SS)                                                                  \
+  bwd_dkdv_kernel<DD, SS><<<kDkdvGrid, kWaves * 64, 0, st>>>(                               \
+      q, k, v, dout, Lbuf, Nbuf, dend, hdr, tile_info, items, tile_rows, stash,             \
+      stash_kvh_blocks, partial, dk, dv, g, nkt)
   if (D == 128) {
     if (stash) DMGQA_DKDV(128, true); else DMGQA_DKDV(128, false);
   } else {
