@@ -268,15 +268,12 @@ int docmask_gqa_attn_bwd(const void* q, const void* k, const void* v, const void
   const u16* oh = static_cast<const u16*>(out);
   const u16* doh = static_cast<const u16*>(dout);
 
-  timing_begin(kKSched, st);
-  hipError_t e = launch_sched_dkdv(dend, g, L.nkt, L.max_split_base, hdr, tile_info, items,
-                                   tile_rows, st);
-  timing_end(kKSched, st);
-  if (e != hipSuccess) return DMGQA_ERR_HIP;
+  hipError_t e;
   if (use_stash) {
-    timing_begin(kKRowstat, st);
-    e = launch_rowstat(D, oh, doh, lse, Lbuf, Nbuf, g, st);
-    timing_end(kKRowstat, st);
+    timing_begin(kKSchedRowstat, st);
+    e = launch_sched_rowstat(D, dend, g, L.nkt, L.max_split_base, hdr, tile_info, items,
+                             tile_rows, oh, doh, lse, Lbuf, Nbuf, st);
+    timing_end(kKSchedRowstat, st);
     if (e != hipSuccess) return DMGQA_ERR_HIP;
     timing_begin(kKDkdv, st);
     e = launch_bwd_dkdv(D, qh, kh, vh, doh, Lbuf, Nbuf, dend, hdr, tile_info, items, tile_rows,
@@ -289,6 +286,11 @@ int docmask_gqa_attn_bwd(const void* q, const void* k, const void* v, const void
     timing_end(kKDq, st);
     if (e != hipSuccess) return DMGQA_ERR_HIP;
   } else {
+    timing_begin(kKSched, st);
+    e = launch_sched_dkdv(dend, g, L.nkt, L.max_split_base, hdr, tile_info, items, tile_rows,
+                          st);
+    timing_end(kKSched, st);
+    if (e != hipSuccess) return DMGQA_ERR_HIP;
     timing_begin(kKDq, st);
     e = launch_bwd_dq(D, qh, kh, vh, oh, doh, lse, dstart, static_cast<u16*>(dq), Lbuf, Nbuf, g,
                       st);

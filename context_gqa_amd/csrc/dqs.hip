@@ -48,34 +48,6 @@ __device__ __forceinline__ bf16x8 kt_operand(const char* half, const int (&off)[
 
 }  // namespace
 
-// Per query row: -lse/scale (start value of the S accumulators of the dK/dV
-// kernel, so that P = exp2(scale*log2e * S)) and -D, D = <dO, O> (start
-// value of its dP accumulators, so that dS = P * dP).  D/8 lanes per row,
-// one 16-byte chunk of out and dout each.
-template <int D>
-__global__ __launch_bounds__(256) void rowstat_kernel(const u16* __restrict__ out,
-                                                      const u16* __restrict__ dout,
-                                                      const float* __restrict__ lse,
-                                                      float* __restrict__ Lbuf,
-                                                      float* __restrict__ Nbuf, int nrows,
-                                                      float inv_scale) {
-  constexpr int kLanes = D / 8;
-  const int row = blockIdx.x * (256 / kLanes) + (threadIdx.x / kLanes);
-  const int j = threadIdx.x % kLanes;
-  const int rr = min(row, nrows - 1);
-  const bf16x8 o = ld_bf16x8(out + (size_t)rr * D + 8 * j);
-  const bf16x8 d = ld_bf16x8(dout + (size_t)rr * D + 8 * j);
-  float acc = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)d[e], acc);
-#pragma unroll
-  for (int o2 = kLanes / 2; o2 > 0; o2 >>= 1) acc += __shfl_xor(acc, o2, kLanes);
-  if (j == 0 && row < nrows) {
-    Nbuf[row] = -acc;
-    Lbuf[row] = -lse[row] * inv_scale;
-  }
-}
-
 // One workgroup = 4 stash blocks (128 query rows of one KV head): wave w
 // owns block J = 4*qb + w.  Key tiles of 128 are those reaching any of the
 // 128 rows; their K tiles stream through two LDS stages (DMA one tile
@@ -212,18 +184,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
         *reinterpret_cast<uint2*>(orow + 32 * db + 8 * r4 + 4 * h) = __builtin_bit_cast(uint2, w);
       }
   }
-}
-
-hipError_t launch_rowstat(int D, const u16* out, const u16* dout, const float* lse, float* Lbuf,
-                          float* Nbuf, const Geo& g, hipStream_t st) {
-  const int nrows = g.B * g.Sq * g.Hq;
-  const int rows_per_block = 256 / (D / 8);
-  const unsigned grid = (unsigned)((nrows + rows_per_block - 1) / rows_per_block);
-  if (D == 128)
-    rowstat_kernel<128><<<grid, 256, 0, st>>>(out, dout, lse, Lbuf, Nbuf, nrows, 1.f / g.scale);
-  else
-    rowstat_kernel<64><<<grid, 256, 0, st>>>(out, dout, lse, Lbuf, Nbuf, nrows, 1.f / g.scale);
-  return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq_stash(int D, const u16* k, const int32_t* dstart, const int4* tile_rows,

@@ -52,8 +52,11 @@ hipError_t launch_bwd_dkdv(int D, const u16* q, const u16* k, const u16* v, cons
                            const int4* tile_rows, u16* stash, int stash_kvh_blocks,
                            float* partial, float* dk, float* dv, const Geo& g, int nkt,
                            hipStream_t st);
-hipError_t launch_rowstat(int D, const u16* out, const u16* dout, const float* lse, float* Lbuf,
-                          float* Nbuf, const Geo& g, hipStream_t st);
+// Schedule (one block) and per-row statistics (stash path) in one launch.
+hipError_t launch_sched_rowstat(int D, const int32_t* dend, const Geo& g, int nkt,
+                                int max_split_base, SchedHeader* hdr, int2* tile_info,
+                                int2* items, int4* tile_rows, const u16* out, const u16* dout,
+                                const float* lse, float* Lbuf, float* Nbuf, hipStream_t st);
 hipError_t launch_bwd_dq_stash(int D, const u16* k, const int32_t* dstart, const int4* tile_rows,
                                const u16* stash, int stash_kvh_blocks, u16* dq, const Geo& g,
                                int nkt, hipStream_t st);
@@ -62,7 +65,7 @@ hipError_t launch_bwd_reduce(int D, const int2* tile_info, const float* partial,
 
 // Kernel timing (benchmark use): when enabled, each launch below is
 // bracketed by HIP events recorded on the launch stream.
-enum KernelId { kKPrep = 0, kKFwd, kKSched, kKDq, kKDkdv, kKReduce, kKRowstat, kNumKernels };
+enum KernelId { kKPrep = 0, kKFwd, kKSched, kKDq, kKDkdv, kKReduce, kKSchedRowstat, kNumKernels };
 void timing_begin(int kernel, hipStream_t st);
 void timing_end(int kernel, hipStream_t st);
 

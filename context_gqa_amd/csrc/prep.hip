@@ -168,16 +168,14 @@ __device__ __forceinline__ int stash_blocks(int a0, int na, int b0, int nb, cons
   return (thi * g.G + kStashRows - 1) / kStashRows - tlo * g.G / kStashRows;
 }
 
-// One block.  For every (batch, key tile): the number of query rows (local
-// tokens x group heads) that reach it; then a split of those rows into
-// pieces of `rows_per_split` (chosen so the total stays under kMaxSplitBase),
-// the work-item list and the partial-sum slots.
-__global__ __launch_bounds__(kScanThreads) void sched_dkdv(const int32_t* __restrict__ dend, Geo g,
-                                                           int nkt, int max_split_base,
-                                                           SchedHeader* __restrict__ hdr,
-                                                           int2* __restrict__ tile_info,
-                                                           int2* __restrict__ items,
-                                                           int4* __restrict__ tile_rows) {
+// One block (kScanThreads threads).  For every (batch, key tile): the
+// number of query rows (local tokens x group heads) that reach it; then a
+// split of those rows into pieces of `rows_per_split` (chosen so the total
+// stays under kMaxSplitBase), the work-item list and the partial-sum slots.
+__device__ void sched_body(const int32_t* __restrict__ dend, const Geo& g, int nkt,
+                           int max_split_base, SchedHeader* __restrict__ hdr,
+                           int2* __restrict__ tile_info, int2* __restrict__ items,
+                           int4* __restrict__ tile_rows) {
   __shared__ int sh[32];
   __shared__ long long red[16];
   const int ntiles = g.B * nkt;
@@ -294,6 +292,56 @@ __global__ __launch_bounds__(kScanThreads) void sched_dkdv(const int32_t* __rest
   (void)sh;
 }
 
+__global__ __launch_bounds__(kScanThreads) void sched_dkdv(const int32_t* __restrict__ dend, Geo g,
+                                                           int nkt, int max_split_base,
+                                                           SchedHeader* __restrict__ hdr,
+                                                           int2* __restrict__ tile_info,
+                                                           int2* __restrict__ items,
+                                                           int4* __restrict__ tile_rows) {
+  sched_body(dend, g, nkt, max_split_base, hdr, tile_info, items, tile_rows);
+}
+
+// Per query row: -lse/scale (start value of the S accumulators of the dK/dV
+// kernel, so that P = exp2(scale*log2e * S)) and -D, D = <dO, O> (start
+// value of its dP accumulators, so that dS = P * dP).  D/8 lanes per row,
+// one 16-byte chunk of out and dout each; `blk` indexes groups of
+// kScanThreads / (D/8) rows.
+template <int D>
+__device__ void rowstat_rows(const u16* __restrict__ out, const u16* __restrict__ dout,
+                             const float* __restrict__ lse, float* __restrict__ Lbuf,
+                             float* __restrict__ Nbuf, int nrows, float inv_scale, int blk) {
+  constexpr int kLanes = D / 8;
+  const int row = blk * (kScanThreads / kLanes) + (int)(threadIdx.x / kLanes);
+  const int j = threadIdx.x % kLanes;
+  const int rr = min(row, nrows - 1);
+  const bf16x8 o = ld_bf16x8(out + (size_t)rr * D + 8 * j);
+  const bf16x8 d = ld_bf16x8(dout + (size_t)rr * D + 8 * j);
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)d[e], acc);
+#pragma unroll
+  for (int o2 = kLanes / 2; o2 > 0; o2 >>= 1) acc += __shfl_xor(acc, o2, kLanes);
+  if (j == 0 && row < nrows) {
+    Nbuf[row] = -acc;
+    Lbuf[row] = -lse[row] * inv_scale;
+  }
+}
+
+// The schedule (block 0) and the row statistics (the other blocks) in one
+// launch: the single-block schedule then runs beside the row statistics.
+template <int D>
+__global__ __launch_bounds__(kScanThreads) void sched_rowstat(
+    const int32_t* __restrict__ dend, Geo g, int nkt, int max_split_base,
+    SchedHeader* __restrict__ hdr, int2* __restrict__ tile_info, int2* __restrict__ items,
+    int4* __restrict__ tile_rows, const u16* __restrict__ out, const u16* __restrict__ dout,
+    const float* __restrict__ lse, float* __restrict__ Lbuf, float* __restrict__ Nbuf) {
+  if (blockIdx.x == 0)
+    sched_body(dend, g, nkt, max_split_base, hdr, tile_info, items, tile_rows);
+  else
+    rowstat_rows<D>(out, dout, lse, Lbuf, Nbuf, g.B * g.Sq * g.Hq, 1.f / g.scale,
+                    (int)blockIdx.x - 1);
+}
+
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_prep_docs(const int32_t* doc, int B, int S, int Skv, int32_t* dstart,
@@ -318,6 +366,24 @@ hipError_t launch_sched_dkdv(const int32_t* dend, const Geo& g, int nkt, int max
                              hipStream_t st) {
   sched_dkdv<<<1, kScanThreads, 0, st>>>(dend, g, nkt, max_split_base, hdr, tile_info, items,
                                          tile_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_sched_rowstat(int D, const int32_t* dend, const Geo& g, int nkt,
+                                int max_split_base, SchedHeader* hdr, int2* tile_info,
+                                int2* items, int4* tile_rows, const u16* out, const u16* dout,
+                                const float* lse, float* Lbuf, float* Nbuf, hipStream_t st) {
+  const int nrows = g.B * g.Sq * g.Hq;
+  const int rows_per_block = kScanThreads / (D / 8);
+  const unsigned grid = 1u + (unsigned)((nrows + rows_per_block - 1) / rows_per_block);
+  if (D == 128)
+    sched_rowstat<128><<<grid, kScanThreads, 0, st>>>(dend, g, nkt, max_split_base, hdr,
+                                                      tile_info, items, tile_rows, out, dout,
+                                                      lse, Lbuf, Nbuf);
+  else
+    sched_rowstat<64><<<grid, kScanThreads, 0, st>>>(dend, g, nkt, max_split_base, hdr,
+                                                     tile_info, items, tile_rows, out, dout,
+                                                     lse, Lbuf, Nbuf);
   return hipGetLastError();
 }
 

@@ -27,7 +27,7 @@ size_t g_used = 0;
 int g_open[kNumKernels];
 
 const char* kNames[kNumKernels] = {"prep", "fwd", "sched_dkdv", "bwd_dq", "bwd_dkdv",
-                                   "bwd_reduce", "rowstat"};
+                                   "bwd_reduce", "sched_rowstat"};
 
 hipEvent_t take_event() {
   if (g_used == g_pool.size()) {
