@@ -1,5 +1,4 @@
-// dQ of document-masked causal GQA attention from the dS stash, and the
-// per-row statistics the dK/dV kernel needs.
+// dQ of document-masked causal GQA attention from the dS stash.
 //
 // dQ = scale * dS K ("Training Infrastructure and Systems", "FlashAttention:
 // never write the score matrix" for the recomputation it replaces; the chain
@@ -46,13 +45,28 @@ __device__ __forceinline__ bf16x8 kt_operand(const char* half, const int (&off)[
   return r;
 }
 
+typedef __attribute__((address_space(3))) char lds_char;
+
+// global_load_lds_dwordx4 as inline assembly: lane l's 16 bytes at
+// sbase + voff + IMM go to LDS address lds + 16 * l (sbase, lds
+// wave-uniform).  The immediate offset moves the LDS address too, so M0 is
+// lds - IMM.
+template <int IMM>
+__device__ __forceinline__ void dma_asm16(const void* sbase, unsigned voff, char* lds) {
+  const unsigned m0 =
+      __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_char*)lds) - (unsigned)IMM;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(voff),
+               "s"(sbase), "s"(m0), "i"(IMM)
+               : "memory");
+}
+
 }  // namespace
 
 // One workgroup = 4 stash blocks (128 query rows of one KV head): wave w
 // owns block J = 4*qb + w.  Key tiles of 128 are those reaching any of the
 // 128 rows; their K tiles stream through two LDS stages (DMA one tile
-// ahead), and the wave's dS operands for the next tile are loaded into
-// registers one tile ahead.  Rows of a block outside the tile's reach hold
+// ahead), and the wave's dS operands are loaded into registers two tiles
+// ahead.  Rows of a block outside the tile's reach hold
 // no stash data and are zeroed.
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
@@ -70,7 +84,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
   const int qb = nqb - 1 - (int)(blockIdx.x / nbg);     // heavy (late) row blocks first
   const int bg = blockIdx.x % nbg;
   const int b = bg / g.Hkv, kvh = bg % g.Hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int h = lane >> 5, i = lane & 31;
   const int J = 4 * qb + wave;                 // this wave's 32-row block
   const int grow = 32 * J + i;                 // this lane's query row (in the KV head)
@@ -91,63 +105,94 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
   const int4* trow_b = tile_rows + (size_t)b * nkt;
   const u16* stash_h = stash + (size_t)kvh * stash_kvh_blocks * (kStashBlockBytes / 2);
 
-  // K tile DMA: wave w fills key rows 16w .. 16w+15 of both halves
+  // K tile DMA: wave w fills key rows 16w .. 16w+15 of both halves (lane
+  // l: row 16w + l/4, slot l%4), as assembly with a scalar base and a 32-bit
+  // per-lane offset (K below 2^31 elements, which the host checks), so the
+  // compiler adds no waits of its own for these LDS writes.
   const int kr_row = 16 * wave + (lane >> 2);
-  const int slot = lane & 3, xr = (kr_row >> 2) & 3;
+  const unsigned coff = 8 * ((lane & 3) ^ ((kr_row >> 2) & 3));
+  // per-lane byte offsets of the two halves' rows within a full tile
+  const unsigned koff[2] = {((unsigned)kr_row * (unsigned)kvstride + coff) * 2u,
+                            ((unsigned)(kr_row + 64) * (unsigned)kvstride + coff) * 2u};
   auto issue = [&](int it, char* st) __attribute__((always_inline)) {
-    const int kt = it < kr.na ? kr.a0 + it : kr.b0 + (it - kr.na);
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int key = min(kt * BN + 64 * hf + kr_row, g.Skv - 1);
-      const u16* src = kbase + (size_t)key * kvstride + 8 * (slot ^ xr);
+    const int kt = uniform(it < kr.na ? kr.a0 + it : kr.b0 + (it - kr.na));
+    // the tile's rows as a scalar base; a tile running past the last key
+    // clamps its rows per lane
+    const u16* tb = kbase + (size_t)kt * BN * kvstride;
+    const bool partial = kt * BN + BN > g.Skv;
+    auto half = [&](int hf, unsigned off) __attribute__((always_inline)) {
       char* dst = st + hf * KT::kHalf + 64 * 16 * wave;
+      static_for<NCH / 4>([&](auto cc) __attribute__((always_inline)) {
+        constexpr int C = decltype(cc)::value;
+        dma_asm16<64 * C>(tb, off, dst + C * kGroupBytes);
+      });
+    };
+    if (!partial) {
+      half(0, koff[0]);
+      half(1, koff[1]);
+    } else {
 #pragma unroll
-      for (int c = 0; c < NCH / 4; ++c)
-        dma16(src + 32 * c, reinterpret_cast<u16*>(dst + c * kGroupBytes));
+      for (int hf = 0; hf < 2; ++hf) {
+        const int key = min(64 * hf + kr_row, g.Skv - 1 - kt * BN);
+        half(hf, ((unsigned)key * (unsigned)kvstride + coff) * 2u);
+      }
     }
   };
-  // dS operands of this wave's block for tile `it`, loaded one tile ahead
+  // dS operands of this wave's block for tile `it`, loaded two tiles ahead
   // of their use.  `have`: the tile's stash holds block J; `part`: some rows
   // of the block lie outside the tile's reach (their stash rows are never
   // written and are replaced by zeros at use); `ok`: this lane's row does not.
+  // Past the last tile the loads still happen (from this head's first stash
+  // block, never used), so every step issues the same number of them.
   struct DsOps {
     u32x4 op[8];
-    bool have, part, ok;
+    int4 tr;     // the tile's row range (tile_rows entry)
+    bool in;     // a tile of this workgroup (not a load past the last)
   };
   auto load_ds = [&](int it, DsOps& d) __attribute__((always_inline)) {
-    const int kt = it < kr.na ? kr.a0 + it : kr.b0 + (it - kr.na);
+    const int x = min(it, ntiles - 1);
+    const int kt = uniform(x < kr.na ? kr.a0 + x : kr.b0 + (x - kr.na));
     const int4 tr = trow_b[kt];
+    d.tr = tr;
+    d.in = it < ntiles;
     const int nblk = tr.y > tr.x ? (tr.y * g.G + kStashRows - 1) / kStashRows - tr.z : 0;
     const int rel = J - tr.z;
-    d.have = rel >= 0 && rel < nblk;
-    d.part = !(tr.x * g.G <= 32 * J && 32 * J + 32 <= tr.y * g.G);
-    d.ok = grow >= tr.x * g.G && grow < tr.y * g.G;
-    if (d.have) {
-      const u16* src = stash_h + (size_t)(tr.w + rel) * (kStashBlockBytes / 2) + lane * 8;
+    const bool have = d.in && rel >= 0 && rel < nblk;
+    // one block through a buffer resource (wave-uniform base) and a fixed
+    // per-lane offset
+    const u16* blk = stash_h + (have ? (size_t)(tr.w + rel) * (kStashBlockBytes / 2) : 0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u16*>(blk), 0, kStashBlockBytes, 0x00020000);
 #pragma unroll
-      for (int kq = 0; kq < 8; ++kq) d.op[kq] = *reinterpret_cast<const u32x4*>(src + kq * 512);
-    }
+    for (int kq = 0; kq < 8; ++kq)
+      d.op[kq] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + kq * 1024, 0, 0));
   };
-
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = zero16();
 
-  // One barrier per key tile: wait for this tile's K and dS (issued during
-  // the previous tile), barrier (every wave's K loads are in and every wave
-  // is done with the previous tile), start the next tile's K and dS loads,
-  // multiply.
+  // One barrier per key tile.  Issue order: K(it+1) DMA, then dS(it+2)
+  // loads, so when tile it starts only the 8 dS loads of tile it+1 may be
+  // outstanding: wait for the rest (tile it's K and dS), barrier (every
+  // wave's K loads are in and every wave is done with tile it-1, whose
+  // stage the next DMA refills), start the next loads, multiply.
   auto step = [&](int it, const char* cur, char* nxt, DsOps& dc, DsOps& dn)
                   __attribute__((always_inline)) {
-    wait_vmcnt<0>();
+    wait_vmcnt<8>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (it + 1 < ntiles) {
-      issue(it + 1, nxt);
-      load_ds(it + 1, dn);
-    }
-    if (dc.have) {
-      if (dc.part && !dc.ok) {
+    if (it + 1 < ntiles) issue(it + 1, nxt);
+    load_ds(it + 2, dn);
+    const int4 tr = dc.tr;
+    const int nblk = tr.y > tr.x ? (tr.y * g.G + kStashRows - 1) / kStashRows - tr.z : 0;
+    const int rel = J - tr.z;
+    const bool have = dc.in && rel >= 0 && rel < nblk;
+    // rows of the block outside the tile's reach: never written, zeroed here
+    const bool part = !(tr.x * g.G <= 32 * J && 32 * J + 32 <= tr.y * g.G);
+    const bool ok = grow >= tr.x * g.G && grow < tr.y * g.G;
+    if (have) {
+      if (part && !ok) {
 #pragma unroll
         for (int kq = 0; kq < 8; ++kq) dc.op[kq] = u32x4{0u, 0u, 0u, 0u};
       }
@@ -162,13 +207,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
     }
   };
   if (ntiles > 0) {
-    DsOps dA, dB;
+    DsOps d0, d1, d2;
     issue(0, sk0);
-    load_ds(0, dA);
-    for (int it = 0; it < ntiles; it += 2) {
-      step(it, sk0, sk1, dA, dB);
-      if (it + 1 < ntiles) step(it + 1, sk1, sk0, dB, dA);
+    load_ds(0, d0);
+    load_ds(1, d1);
+    // K stages alternate with the tile index, dS register sets cycle by 3
+    for (int it = 0; it < ntiles; it += 6) {
+      step(it, sk0, sk1, d0, d2);
+      if (it + 1 >= ntiles) break;
+      step(it + 1, sk1, sk0, d1, d0);
+      if (it + 2 >= ntiles) break;
+      step(it + 2, sk0, sk1, d2, d1);
+      if (it + 3 >= ntiles) break;
+      step(it + 3, sk1, sk0, d0, d2);
+      if (it + 4 >= ntiles) break;
+      step(it + 4, sk0, sk1, d1, d0);
+      if (it + 5 >= ntiles) break;
+      step(it + 5, sk1, sk0, d2, d1);
     }
+    wait_vmcnt<0>();
   }
 
   if (grow < nrows) {
