@@ -9,12 +9,21 @@
 // exp(scale*(m_old - m_new)), rescales the running output by the same factor
 // and adds P V.  At the end it writes out = O / l and lse = scale*m + ln l.
 //
-// Layout on gfx950: 4 waves x 32 query rows; rows are (token, head-in-group)
-// pairs of one KV head, so one K/V tile in LDS serves all G query heads
-// sharing it (GQA).  Scores are held as S^T = K Q^T so that each lane owns
-// one query row (two lanes per row, 16 keys each): the row max and sum need
-// one cross-lane exchange.  P V is computed as O^T = V^T P^T with V read
-// from LDS by transposed reads.
+// Layout on gfx950: 4 waves x 32 query rows, two workgroups per CU; rows
+// are (token, head-in-group) pairs of one KV head, so one K/V tile in LDS
+// serves all G query heads sharing it (GQA).
+// Scores are held as S^T = K Q^T so that each lane owns one query row (two
+// lanes per row, 16 keys each): the row max and sum need one cross-lane
+// exchange.  P V is computed as O^T = V^T P^T with V read from LDS by
+// transposed reads.
+//
+// K/V tiles (64 keys) stream through 2 LDS stages, filled by global->LDS
+// DMA one tile ahead.  A tile holds 64 rows x D bf16 in groups
+// of 4 sixteen-byte chunks: group c/4 of row r occupies the 64 bytes at
+// (c/4) * 4096 + 64 * r, chunk c in slot (c % 4) ^ ((r / 4) % 4), so the
+// 128-bit reads of K (32 rows of one chunk per 32-lane half) and the
+// transposed reads of V (4 rows x 4 slots x 2 halves) are conflict-free on
+// the 64 banks, and a DMA instruction moves 64 contiguous bytes of 16 rows.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "qtile.hpp"
@@ -22,29 +31,69 @@
 
 namespace dmgqa {
 
+namespace {
+
+constexpr int kRows = kFwdBM;             // query rows per workgroup
+constexpr int kWaves = kRows / 32;
+constexpr int kGroupBytes = kFwdBN * 64;  // one chunk group of a 64-row tile
+
+typedef __attribute__((address_space(3))) char lds_char;
+
 // Lazy rescaling: the running maximum used as the exponent reference is only
 // raised when a row's new maximum exceeds it by more than 2^kRescaleLog2 (in
 // exp2 units); otherwise P may reach 2^kRescaleLog2, which bf16 and fp32
 // represent exactly as well as values below 1.  out = O / l is unchanged.
 constexpr float kRescaleLog2 = 8.f;
 
+// global_load_lds_dwordx4 as inline assembly: lane l's 16 bytes at
+// sbase + voff + IMM go to LDS address lds + 16 * l (sbase, lds
+// wave-uniform; voff a 32-bit per-lane byte offset).  The immediate offset
+// moves the LDS address too, so M0 is lds - IMM.  Written as assembly so the
+// compiler adds no waits of its own for these LDS writes; every read of a
+// stage follows an explicit vmcnt wait and a barrier.
+template <int IMM>
+__device__ __forceinline__ void dma_lds16(const void* sbase, unsigned voff, char* lds) {
+  const unsigned m0 =
+      __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_char*)lds) - (unsigned)IMM;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(voff),
+               "s"(sbase), "s"(m0), "i"(IMM)
+               : "memory");
+}
+
+__device__ __forceinline__ bf16x8 ld_lds_b128(const char* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// MFMA operand holding, for lane l = 32h + i, column 32*db + i of the tile
+// rows that register slot (h, e) pairs with in k-step ks (rows 16ks +
+// 8(e/4) + 4h + e%4), from a tile in the grouped layout; lane_off[hf] is the
+// per-lane part of the address of rows 8*hf .. 8*hf+3 of the 16-row step.
+__device__ __forceinline__ bf16x8 tr_group(const char* tile, const int (&lane_off)[2], int ks,
+                                           int db) {
+  const char* p = tile + db * kGroupBytes + 16 * ks * 64;
+  const i16x4 lo = ds_read_tr(reinterpret_cast<const u16*>(p + lane_off[0]));
+  const i16x4 hi = ds_read_tr(reinterpret_cast<const u16*>(p + lane_off[1]));
+  const bf16x4 a = __builtin_bit_cast(bf16x4, lo);
+  const bf16x4 b = __builtin_bit_cast(bf16x4, hi);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+}  // namespace
+
 template <int D>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(const u16* __restrict__ q,
-                                                     const u16* __restrict__ k,
-                                                     const u16* __restrict__ v,
-                                                     const int32_t* __restrict__ dstart,
-                                                     u16* __restrict__ out,
-                                                     float* __restrict__ lse, Geo g) {
-  constexpr int BM = kFwdBM, BN = kFwdBN, KK = D / 16, DB = D / 32;
-  // Padded layouts, each conflict-free for its one access pattern on the
-  // 64-bank LDS: K is read by ds_read_b128 (16 consecutive rows, one chunk)
-  // -> row stride D + 8; V by ds_read_b64_tr_b16 (4 rows x 4 chunks) -> row
-  // stride D + 32.  Two stages, each its own array (see dma.hpp).
-  constexpr int LDK = D + 8, LDV = D + 32;
-  __shared__ __attribute__((aligned(1024))) u16 sK0[BN * LDK];
-  __shared__ __attribute__((aligned(1024))) u16 sK1[BN * LDK];
-  __shared__ __attribute__((aligned(1024))) u16 sV0[BN * LDV];
-  __shared__ __attribute__((aligned(1024))) u16 sV1[BN * LDV];
+__global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict__ q,
+                                                          const u16* __restrict__ k,
+                                                          const u16* __restrict__ v,
+                                                          const int32_t* __restrict__ dstart,
+                                                          u16* __restrict__ out,
+                                                          float* __restrict__ lse, Geo g) {
+  constexpr int BM = kRows, BN = kFwdBN, KK = D / 16, DB = D / 32;
+  constexpr int kTile = D / 32 * kGroupBytes;   // bytes of a K (or V) tile
+  constexpr int kStage = 2 * kTile;
+  __shared__ __attribute__((aligned(1024))) char stg[2 * kStage];
 
   const int nrows = g.Sq * g.G;
   const int nt = (nrows + BM - 1) / BM;
@@ -53,7 +102,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const u16* __restrict__ q,
   const int tile = nt - 1 - (int)(blockIdx.x / nbg);
   const int bg = blockIdx.x % nbg;
   const int b = bg / g.Hkv, kvh = bg % g.Hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int h = lane >> 5, i = lane & 31;
 
   const int row0 = tile * BM;
@@ -79,34 +128,62 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const u16* __restrict__ q,
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = zero16();
 
+  // K operand (A of S^T = K Q^T): lane (h, i) reads row i (and 32 + i),
+  // chunk h + 2kk: slot (h + 2(kk&1)) ^ (i/4 % 4).
+  const int off_b[2] = {64 * i + 16 * (h ^ ((i >> 2) & 3)),
+                        64 * i + 16 * ((h ^ ((i >> 2) & 3)) ^ 2)};
+  // V operand (transposed reads): source lane s of 16-lane group grp reads
+  // row 4h + s/4 (+8 for the second half), chunk 2(grp&1) + (s&3)/2 of the
+  // group, 8-byte half s&1; the row quad index is h (+2).
+  const int s16 = lane & 15, grp = lane >> 4;
+  int off_t[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+    off_t[hf] = (4 * h + (s16 >> 2) + 8 * hf) * 64 +
+                16 * ((2 * (grp & 1) + ((s16 & 3) >> 1)) ^ ((h + 2 * hf) & 3)) + 8 * (s16 & 1);
+
+  // DMA: wave w fills rows 16(w%4) .. +15 of chunk groups w/4 + 2m of the K
+  // and V tiles (lane l: row 16(w%4) + l/4, slot l%4).  Every tile index
+  // past the last re-loads the last tile, so each wave issues the same
+  // number of instructions per tile and every wait is a plain vmcnt.
   const size_t kvstride = (size_t)g.Hkv * D;
   const u16* kbase = k + (size_t)b * g.Skv * kvstride + (size_t)kvh * D;
   const u16* vbase = v + (size_t)b * g.Skv * kvstride + (size_t)kvh * D;
-  PadTileDma<BN, D, LDK, 4> dmak;
-  PadTileDma<BN, D, LDV, 4> dmav;
-  dmak.init((unsigned)kvstride, wave, lane);
-  dmav.init((unsigned)kvstride, wave, lane);
-  auto issue = [&](int it, u16* dK, u16* dV) __attribute__((always_inline)) {
-    const int t0 = uniform((it < kr.na ? kr.a0 + it : kr.b0 + (it - kr.na)) * BN);
-    dmak.issue(kbase, (unsigned)kvstride, t0, g.Skv - 1, dK, wave, lane);
-    dmav.issue(vbase, (unsigned)kvstride, t0, g.Skv - 1, dV, wave, lane);
+  const int drow = 16 * wave + (lane >> 2);
+  const unsigned coff = 8 * ((lane & 3) ^ ((drow >> 2) & 3));
+  auto tile_start = [&](int it) __attribute__((always_inline)) {
+    const int x = min(it, ntiles - 1);
+    return uniform((x < kr.na ? kr.a0 + x : kr.b0 + (x - kr.na)) * BN);
   };
-  issue(0, sK0, sV0);
-  wait_vmcnt<0>();
-  __builtin_amdgcn_s_barrier();
+  // byte offset of this lane's row chunk from the batch / head base (K and
+  // V share the layout; the host keeps each tensor below 2^31 elements)
+  auto dma_off = [&](int it) __attribute__((always_inline)) {
+    const int key = min(tile_start(it) + drow, g.Skv - 1);
+    return ((unsigned)key * (unsigned)kvstride + coff) * 2u;
+  };
+  auto issue_k = [&](unsigned off, char* st) __attribute__((always_inline)) {
+    static_for<D / 32>([&](auto cc) __attribute__((always_inline)) {
+      constexpr int C = decltype(cc)::value;
+      dma_lds16<64 * C>(kbase, off, st + 64 * 16 * wave + C * kGroupBytes);
+    });
+  };
+  auto issue_v = [&](unsigned off, char* st) __attribute__((always_inline)) {
+    static_for<D / 32>([&](auto cc) __attribute__((always_inline)) {
+      constexpr int C = decltype(cc)::value;
+      dma_lds16<64 * C>(vbase, off, st + kTile + 64 * 16 * wave + C * kGroupBytes);
+    });
+  };
 
-  auto step = [&](int it, const u16* cK, const u16* cV, u16* nK, u16* nV)
-                  __attribute__((always_inline)) {
-    const int t0 = (it < kr.na ? kr.a0 + it : kr.b0 + (it - kr.na)) * BN;
-    if (it + 1 < ntiles) issue(it + 1, nK, nV);
-
+  auto step = [&](int it, const char* cK, auto&& mid) __attribute__((always_inline)) {
+    const char* cV = cK + kTile;
+    const int t0 = tile_start(it);
     // K operands for all k-steps are read up front (2*KK LDS reads in
     // flight), so LDS latency overlaps the MFMA chain.
     bf16x8 kf0[KK], kf1[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      kf0[kk] = lds_bf16x8(&cK[i * LDK + 8 * h + 16 * kk]);
-      kf1[kk] = lds_bf16x8(&cK[(32 + i) * LDK + 8 * h + 16 * kk]);
+      kf0[kk] = ld_lds_b128(cK + (kk >> 1) * kGroupBytes + off_b[kk & 1]);
+      kf1[kk] = ld_lds_b128(cK + (kk >> 1) * kGroupBytes + 32 * 64 + off_b[kk & 1]);
     }
     f32x16 s0 = zero16(), s1 = zero16();
 #pragma unroll
@@ -115,6 +192,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const u16* __restrict__ q,
       s1 = mfma32(kf1[kk], qop[kk], s1);
     }
     sched_reads_ahead<2 * KK, KK, 2>();
+    // the next tile's V DMA, while the score products run
+    mid();
     const bool full = kr.max_lo <= t0 && t0 + BN - 1 <= kr.min_pos;
     if (!full) {
       // allowed keys lo..pos relative to this lane's first key t0 + 4h;
@@ -158,18 +237,37 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const u16* __restrict__ q,
 #pragma unroll
       for (int e = 0; e < 8; e += 2) rs = sum2_bf16(bf16x2{pop[e], pop[e + 1]}, rs);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        o[db] = mfma32(tr_operand_pad<LDV>(cV, 0, ks, 32 * db, lane), pop, o[db]);
+      for (int db = 0; db < DB; ++db) o[db] = mfma32(tr_group(cV, off_t, ks, db), pop, o[db]);
     }
     l += rs0 + rs1;
-    // this wave's loads of the next tile are done; after the barrier every
-    // wave's are, and every wave has finished reading the current stage
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
   };
-  for (int it = 0; it < ntiles; it += 2) {
-    step(it, sK0, sV0, sK1, sV1);
-    if (it + 1 < ntiles) step(it + 1, sK1, sV1, sK0, sV0);
+
+  // Two stages: before tile it, wait for its DMA, barrier (every wave's
+  // DMA of tile it is in, and every wave has finished tile it-1, whose
+  // stage is refilled next), start tile it+1's K DMA, compute (tile it+1's
+  // V DMA is issued once the score products are under way).
+  if (ntiles > 0) {
+    char* sA = stg;
+    char* sB = stg + kStage;
+    {
+      const unsigned off0 = dma_off(0);
+      issue_k(off0, sA);
+      issue_v(off0, sA);
+    }
+    for (int it = 0; it < ntiles; ++it) {
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const bool more = it + 1 < ntiles;
+      const unsigned offn = dma_off(it + 1);
+      if (more) issue_k(offn, sB);
+      step(it, sA, [&]() __attribute__((always_inline)) {
+        if (more) issue_v(offn, sB);
+      });
+      char* t = sA;
+      sA = sB;
+      sB = t;
+    }
   }
 
   const float lt = l + xor32(l);
@@ -191,12 +289,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const u16* __restrict__ q,
 
 hipError_t launch_fwd(int D, const u16* q, const u16* k, const u16* v, const int32_t* dstart,
                       u16* out, float* lse, const Geo& g, hipStream_t st) {
-  const int nt = (g.Sq * g.G + kFwdBM - 1) / kFwdBM;
+  const int nt = (g.Sq * g.G + kRows - 1) / kRows;
   const unsigned grid = (unsigned)nt * g.B * g.Hkv;
   if (D == 128)
-    fwd_kernel<128><<<grid, 256, 0, st>>>(q, k, v, dstart, out, lse, g);
+    fwd_kernel<128><<<grid, kWaves * 64, 0, st>>>(q, k, v, dstart, out, lse, g);
   else
-    fwd_kernel<64><<<grid, 256, 0, st>>>(q, k, v, dstart, out, lse, g);
+    fwd_kernel<64><<<grid, kWaves * 64, 0, st>>>(q, k, v, dstart, out, lse, g);
   return hipGetLastError();
 }
 
