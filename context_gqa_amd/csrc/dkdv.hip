@@ -339,6 +339,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     };
     // (2) transposed read: lane (h, i) gets row i, keys 8(e/4) + 4h + e%4
     // of the wave's 16, stored as chunk (w, lane) of the row's stash block.
+    // Done one sub-block later (and once after the last), between the next
+    // sub-block's score products and its own (1), so the scratch is read
+    // before it is written again.
     auto stash_store = [&](int R) __attribute__((always_inline)) {
       const u16* T = s_tr + wave * kWaveKeys * kTrLd;
       const int i = lane & 31, h = lane >> 5;
@@ -428,7 +431,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       for (int nd = 0; nd < ND; ++nd) qt[nd] = tr_pair(tQ + (nd >> 1) * kGroupBytes + off_t[nd & 1]);
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) dka[nd] = mfma16(dsop, qt[nd], dka[nd]);
-      if constexpr (STASH) stash_store(R);
     };
 
     // Sub-block j lives in stage (j/2) % 4 at row 32*(j%2).  Block n+2's
@@ -467,6 +469,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
           issue_q(nx);
         else
           issue_o(nx);
+        // the previous sub-block's dS to the stash, now that its transposed
+        // read has the score products to hide behind
+        if constexpr (STASH)
+          if (R > r_begin) stash_store(R - 32);
         if (w_lo <= R && R + 32 <= w_hi)
           rest(std::false_type{}, st, 32 * h2, R, sc, pc);
         else
@@ -475,6 +481,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       sub_block(std::false_type{});
       if (2 * jb + 1 < nsb) sub_block(std::true_type{});
     }
+    if constexpr (STASH)
+      if (nsb > 0) stash_store(r_begin + 32 * (nsb - 1));
 
     // No DMA (including the re-loads past the item's end) may still be
     // writing LDS once the item is done.
