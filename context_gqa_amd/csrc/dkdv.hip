@@ -24,11 +24,9 @@
 //   dV += P^T dO, dK += dS^T Q     (MFMA, transposed LDS reads)
 //
 // Lane layout (lane l = 16*g4 + j): the S / dP tiles are C[row][key] with
-// key = j; lane group g4 holds the rows 16t + 4*pi(g4) + r (t = 0, 1,
-// r = 0..3), pi swapping the two bits of g4.  Those 8 values are the A
-// operand (P^T, dS^T: key j, k-slot 8*g4 + e <-> row 16(e/4) + 4*pi(g4) +
-// e%4) of the dV / dK products with no data movement; pi puts the two lane
-// groups of each 32-lane half on row quads whose LDS slots do not collide.
+// key = j; lane group g4 holds the rows 16t + 4*g4 + r (t = 0, 1, r = 0..3).
+// Those 8 values are the A operand (P^T, dS^T: key j, k-slot 8*g4 + e <->
+// row 16(e/4) + 4*g4 + e%4) of the dV / dK products with no data movement.
 //
 // P enters dV as a bf16 hi + lo pair (16 significant bits): dV sums P over
 // every row of the group, and one bf16 rounding of P is not accurate enough
@@ -38,13 +36,15 @@
 // A tile holds 64 rows x D bf16 in groups of 4 sixteen-byte chunks (32
 // elements): group c/4 of row r occupies the 64 bytes at
 // (c/4) * 4096 + 64 * r, and inside them chunk c sits in slot
-// (c % 4) ^ ((r / 4) % 4).  On the 64 four-byte banks both access patterns
-// are conflict-free:
-//   - ds_read_b128 of one chunk by 16 rows (any order of 16 aligned rows):
-//     bank = 16*(r%4) + 4*slot, and the slot differs across the row quads;
-//   - ds_read_b64_tr_b16 (per 16-lane group: 4 rows of a quad x 2 chunks x
-//     two 8-byte halves; the two groups of a 32-lane half read quads whose
-//     XOR key differs by 2, so their slot pairs are disjoint).
+// (c % 4) ^ f(r), f(r) = 2 * ((r / 4) % 2).  Both read patterns of the
+// kernel are conflict-free with this f (SQ_LDS_BANK_CONFLICT 0, measured
+// over the 256 slot functions linear in the row's low four bits):
+//   - ds_read_b128 of the S / dP operands: each 16-lane group reads one
+//     chunk of 16 consecutive rows, the four groups four chunks;
+//   - ds_read_b64_tr_b16 of the dV / dK operands: each 16-lane group reads
+//     4 rows of a quad x 2 chunks x two 8-byte halves.
+// (The earlier f(r) = (r / 4) % 4 left the first pattern 2-way
+// conflicting.)
 // A DMA instruction fills one chunk group of 16 rows (lane l: row
 // 16*(w%4) + l/4, slot l % 4): every lane loads 16 bytes of its row from a
 // 64-byte run, and each lane keeps the same row for all of a block's
@@ -114,8 +114,8 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 
 // B operand of 32 rows x 16 columns from a tile in the grouped layout: two
-// transposed reads, at p (rows 4*pi(g4) + 0..3 of the sub-block) and 16
-// rows further.
+// transposed reads, at p (rows 4*g4 + 0..3 of the sub-block) and 16 rows
+// further.
 __device__ __forceinline__ bf16x8 tr_pair(const char* p) {
   const i16x4 lo = ds_read_tr(reinterpret_cast<const u16*>(p));
   const i16x4 hi = ds_read_tr(reinterpret_cast<const u16*>(p + 16 * 64));
@@ -171,23 +171,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int g4 = lane >> 4, j = lane & 15;
-  const int pg = ((g4 & 1) << 1) | (g4 >> 1);   // row quad of lane group g4
   const int total = hdr->n_base_items * g.Hkv;
   const int rps = hdr->rows_per_split;
   const size_t kvstride = (size_t)g.Hkv * D;
   const float c2 = g.scale_log2;
 
-  // b128 operand (A of S = Q K^T): lane l reads row sigma(j) = 4*pi(j/4) +
-  // j%4 of a 16-row step, chunk 4ks + g4 (slot g4 ^ pi(j/4)).
-  const int pj = (((j >> 2) & 1) << 1) | (j >> 3);
-  const int off_b = 64 * (4 * pj + (j & 3)) + 16 * (g4 ^ pj);
+  // b128 operand (A of S = Q K^T): lane l reads row j of a 16-row step,
+  // chunk 4ks + g4 (slot g4 ^ f(j); f depends on row bit 2 only, so the
+  // 16-row steps all share these offsets).
+  const int off_b = 64 * j + 16 * (g4 ^ (((j >> 2) & 1) << 1));
   // transposed operand (B of dV, dK) for d tile nd: source lane j of group
-  // g4 reads row 4*pg + j/4 (+16), chunk 2(nd&1) + (j&3)/2 of chunk group
-  // nd/2, 8-byte half j&1.
+  // g4 reads row 4*g4 + j/4 (+16), chunk 2(nd&1) + (j&3)/2 of chunk group
+  // nd/2, 8-byte half j&1 (f of those rows is 2*(g4 % 2)).
   int off_t[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par)
-    off_t[par] = 64 * (4 * pg + (j >> 2)) + 16 * ((2 * par + ((j & 3) >> 1)) ^ pg) + 8 * (j & 1);
+    off_t[par] = 64 * (4 * g4 + (j >> 2)) + 16 * ((2 * par + ((j & 3) >> 1)) ^ ((g4 & 1) << 1)) +
+                 8 * (j & 1);
 
   for (;;) {
     if (threadIdx.x == 0) s_item = atomicAdd(&hdr->counter, 1);
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       const int rq = wave & 3, c0 = wave >> 2;
       const int rr = 16 * rq + (lane >> 2);
       const unsigned ridx = row_index(rr);
-      const int slot = lane & 3, xr = (rr >> 2) & 3;
+      const int slot = lane & 3, xr = ((rr >> 2) & 1) << 1;
       // byte offset of the row's chunk (q and dout share the layout; both
       // stay below 4 GiB, which the host checks)
       nx_qoff = (ridx * (unsigned)D + 32 * c0 + 8 * (slot ^ xr)) * 2u;
@@ -330,12 +330,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
           stash + ((size_t)kvh * stash_kvh_blocks + uniform(trow.w)) * (kStashBlockBytes / 2), 0,
           tile_blocks * kStashBlockBytes, 0x00020000);
     // (1) dS to this wave's transpose scratch, key-major: lane (g4, j) holds
-    // key j at rows 16t + 4*pg + 0..3.
+    // key j at rows 16t + 4*g4 + 0..3.
     auto stash_put = [&](const bf16x8& dsop) __attribute__((always_inline)) {
       u16* T = s_tr + wave * kWaveKeys * kTrLd;
       const u32x4 w4 = __builtin_bit_cast(u32x4, dsop);
-      *reinterpret_cast<uint2*>(T + j * kTrLd + 4 * pg) = uint2{w4[0], w4[1]};
-      *reinterpret_cast<uint2*>(T + j * kTrLd + 16 + 4 * pg) = uint2{w4[2], w4[3]};
+      *reinterpret_cast<uint2*>(T + j * kTrLd + 4 * g4) = uint2{w4[0], w4[1]};
+      *reinterpret_cast<uint2*>(T + j * kTrLd + 16 + 4 * g4) = uint2{w4[2], w4[3]};
     };
     // (2) transposed read: lane (h, i) gets row i, keys 8(e/4) + 4h + e%4
     // of the wave's 16, stored as chunk (w, lane) of the row's stash block.
@@ -359,8 +359,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
                    __attribute__((always_inline)) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        sc[t] = ld_lds_f32x4(st + Lds::kL + 4 * (q0 + 16 * t + 4 * pg));
-        pc[t] = ld_lds_f32x4(st + Lds::kN + 4 * (q0 + 16 * t + 4 * pg));
+        sc[t] = ld_lds_f32x4(st + Lds::kL + 4 * (q0 + 16 * t + 4 * g4));
+        pc[t] = ld_lds_f32x4(st + Lds::kN + 4 * (q0 + 16 * t + 4 * g4));
       }
       bf16x8 qa[2][KS], oa[2][KS];
 #pragma unroll
@@ -384,12 +384,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     // from its S and dP: P, dV += P^T dO, dS, dK += dS^T Q.
     auto rest = [&](auto masked, const char* st, int q0, int R, const f32x4 (&sc)[2],
                     const f32x4 (&pc)[2]) __attribute__((always_inline)) {
-      // p[4t + r]: row 16t + 4*pg + r of the sub-block, key j
+      // p[4t + r]: row 16t + 4*g4 + r of the sub-block, key j
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(sc[e >> 2][e & 3] * c2);
       if constexpr (decltype(masked)::value) {
-        const int lo_rel = vr_lo - R - 4 * pg;
+        const int lo_rel = vr_lo - R - 4 * g4;
         const unsigned span = (unsigned)max(vr_hi - vr_lo, 0);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
