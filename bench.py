@@ -250,6 +250,8 @@ def main(argv=None) -> int:
         t["wsf"] = torch.empty(max(1, M.docmask_gqa_fwd_workspace_size(B, S, Skv, Hq, Hkv, D,
                                                                       cfg.cp_size)),
                                dtype=torch.uint8, device=dev)
+        t["bounds"] = torch.empty(M.docmask_gqa_doc_bounds_size(B, S, Skv) // 4,
+                                  dtype=torch.int32, device=dev)
         wsb_size = (M.docmask_gqa_bwd_workspace_size_min if args.recompute
                     else M.docmask_gqa_bwd_workspace_size)
         t["wsb"] = torch.empty(max(1, wsb_size(B, S, Skv, Hq, Hkv, D, cfg.cp_size)),
@@ -260,17 +262,21 @@ def main(argv=None) -> int:
                          bytes=algorithmic_bytes(case, cfg.backward)))
 
     def step(i):
-        """One forward + backward call on seed i's inputs, on the current stream."""
+        """One step on seed i's inputs, on the current stream: the document
+        bounds of the batch (computed from doc_ids in every step), then the
+        forward and the backward, both reading them."""
         r = runs[i % len(runs)]
         t, case = r["t"], r["case"]
-        M.docmask_gqa_attn_fwd(t["q"], t["k"], t["v"], doc_ids=t["doc"], cp_size=cfg.cp_size,
-                               cp_rank=rank, softmax_scale=case.scale, out=t["out"],
-                               lse=t["lse"], workspace=t["wsf"])
+        M.docmask_gqa_doc_bounds(t["doc"], B=case.cfg.B, S=cfg.S, Skv=case.Skv,
+                                 out=t["bounds"])
+        M.docmask_gqa_attn_fwd(t["q"], t["k"], t["v"], cp_size=cfg.cp_size, cp_rank=rank,
+                               softmax_scale=case.scale, out=t["out"], lse=t["lse"],
+                               workspace=t["wsf"], bounds=t["bounds"])
         if cfg.backward:
             M.docmask_gqa_attn_bwd(t["q"], t["k"], t["v"], t["out"], t["dout"], t["lse"],
-                                   doc_ids=t["doc"], cp_size=cfg.cp_size, cp_rank=rank,
-                                   softmax_scale=case.scale, dq=t["dq"], dk=t["dk"], dv=t["dv"],
-                                   workspace=t["wsb"])
+                                   cp_size=cfg.cp_size, cp_rank=rank, softmax_scale=case.scale,
+                                   dq=t["dq"], dk=t["dk"], dv=t["dv"], workspace=t["wsb"],
+                                   bounds=t["bounds"])
 
     # With --graph each seed's step is captured once into a HIP graph (the
     # library makes no allocation, synchronisation or memset inside a call)
@@ -376,7 +382,9 @@ def main(argv=None) -> int:
                    "parallelism": "one CP rank's share on one GPU",
                    "launch": "hip graph per seed" if args.graph else "eager",
                    "backward": "recompute (minimum workspace)" if args.recompute
-                               else "dS stash"},
+                               else "dS stash",
+                   "masking": "document bounds from doc_ids once per step, read by the "
+                              "forward and the backward"},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "per_seed_tflops": [round(x, 2) for x in per_seed],
         "median_seed_tflops": round(float(np.median(per_seed)), 2),

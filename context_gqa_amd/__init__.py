@@ -5,7 +5,7 @@ from .binding import (  # noqa: F401
     DMGQA_ERR_HIP, DMGQA_ERR_INVALID_ARG, DMGQA_ERR_UNSUPPORTED, DMGQA_ERR_WORKSPACE,
     DMGQA_OK, LIB_PATH, SIGNATURES, DocmaskGQAError, docmask_gqa_attn_bwd,
     docmask_gqa_attn_fwd, docmask_gqa_bwd_workspace_size, docmask_gqa_bwd_workspace_size_min,
-    docmask_gqa_check_cu_seqlens,
+    docmask_gqa_check_cu_seqlens, docmask_gqa_doc_bounds, docmask_gqa_doc_bounds_size,
     docmask_gqa_check_docs, docmask_gqa_fwd_workspace_size, docmask_gqa_status_string,
     docmask_gqa_version, lib, status_string, docmask_gqa_timing_enable,
     docmask_gqa_kernel_times,

@@ -41,6 +41,14 @@ SIGNATURES = {
     "docmask_gqa_attn_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                             _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                             _vp, _vp, _vp, _sz, _vp]),
+    "docmask_gqa_attn_fwd_bounds": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                                   _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp,
+                                                   _sz, _vp]),
+    "docmask_gqa_attn_bwd_bounds": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                                   _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                   _f32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "docmask_gqa_doc_bounds_size": (_sz, [_i32] * 3),
+    "docmask_gqa_doc_bounds": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "docmask_gqa_check_docs": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
     "docmask_gqa_check_cu_seqlens": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
     "docmask_gqa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -121,6 +129,15 @@ def _need(t, name, dtype, ndim):
     return t
 
 
+def _bounds_ok(bounds, doc_ids, cu_seqlens, B, S, Skv):
+    import torch
+    if doc_ids is not None or cu_seqlens is not None:
+        raise ValueError("pass either bounds or doc_ids / cu_seqlens")
+    _need(bounds, "bounds", torch.int32, 1)
+    if bounds.numel() * 4 < docmask_gqa_doc_bounds_size(B, S, Skv):
+        raise ValueError("bounds is smaller than docmask_gqa_doc_bounds_size(B, S, Skv)")
+
+
 def _docs(doc_ids, cu_seqlens, B, S):
     import torch
     if (doc_ids is None) == (cu_seqlens is None):
@@ -134,12 +151,37 @@ def _docs(doc_ids, cu_seqlens, B, S):
     return None, cu_seqlens, cu_seqlens.numel() - 1
 
 
+def docmask_gqa_doc_bounds_size(B, S, Skv) -> int:
+    return int(lib().docmask_gqa_doc_bounds_size(B, S, Skv))
+
+
+def docmask_gqa_doc_bounds(doc_ids=None, cu_seqlens=None, *, B: int, S: int, Skv: int,
+                           out=None, stream=None):
+    """Document bounds [2, B, Skv] int32 (first position of each key's
+    document, one past its last), followed by scratch, as one int32 buffer
+    for the attention calls' `bounds=` argument."""
+    import torch
+    doc_ids, cu_seqlens, n_docs = _docs(doc_ids, cu_seqlens, B, S)
+    need = docmask_gqa_doc_bounds_size(B, S, Skv)
+    dev = (doc_ids if doc_ids is not None else cu_seqlens).device
+    if out is None:
+        out = torch.empty(max(need // 4, 1), dtype=torch.int32, device=dev)
+    _need(out, "bounds", torch.int32, 1)
+    rc = lib().docmask_gqa_doc_bounds(_ptr(doc_ids), _ptr(cu_seqlens), n_docs, B, S, Skv,
+                                      _ptr(out), out.numel() * 4, _stream(stream))
+    if rc != DMGQA_OK:
+        raise DocmaskGQAError(rc, "docmask_gqa_doc_bounds")
+    return out
+
+
 def docmask_gqa_attn_fwd(q, k, v, doc_ids=None, cu_seqlens=None, *, cp_size: int,
                          cp_rank: int, softmax_scale: Optional[float] = None, out=None,
-                         lse=None, workspace=None, stream=None) -> Tuple["object", "object"]:
+                         lse=None, workspace=None, stream=None,
+                         bounds=None) -> Tuple["object", "object"]:
     """out [B,Sq,Hq,D] bf16 and lse [B,Sq,Hq] fp32 of the rank's local rows.
     q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] bf16; doc_ids [B,S] or cu_seqlens
-    [n_docs+1] int32 with S = Sq * cp_size."""
+    [n_docs+1] int32 with S = Sq * cp_size, or bounds from
+    docmask_gqa_doc_bounds."""
     import torch
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 4)
@@ -149,7 +191,10 @@ def docmask_gqa_attn_fwd(q, k, v, doc_ids=None, cu_seqlens=None, *, cp_size: int
     if tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != D:
         raise ValueError("k and v must be [B, Skv, Hkv, D] matching q")
     S = Sq * cp_size
-    doc_ids, cu_seqlens, n_docs = _docs(doc_ids, cu_seqlens, B, S)
+    if bounds is None:
+        doc_ids, cu_seqlens, n_docs = _docs(doc_ids, cu_seqlens, B, S)
+    else:
+        _bounds_ok(bounds, doc_ids, cu_seqlens, B, S, Skv)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -161,10 +206,16 @@ def docmask_gqa_attn_fwd(q, k, v, doc_ids=None, cu_seqlens=None, *, cp_size: int
     need = docmask_gqa_fwd_workspace_size(B, S, Skv, Hq, Hkv, D, cp_size)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    rc = lib().docmask_gqa_attn_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(doc_ids), _ptr(cu_seqlens), n_docs, B, S, Skv, Hq,
-        Hkv, D, cp_size, cp_rank, float(softmax_scale), _ptr(out), _ptr(lse),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if bounds is None:
+        rc = lib().docmask_gqa_attn_fwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(doc_ids), _ptr(cu_seqlens), n_docs, B, S, Skv, Hq,
+            Hkv, D, cp_size, cp_rank, float(softmax_scale), _ptr(out), _ptr(lse),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    else:
+        rc = lib().docmask_gqa_attn_fwd_bounds(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(bounds), B, S, Skv, Hq, Hkv, D, cp_size, cp_rank,
+            float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
     if rc != DMGQA_OK:
         raise DocmaskGQAError(rc, "docmask_gqa_attn_fwd")
     return out, lse
@@ -172,8 +223,9 @@ def docmask_gqa_attn_fwd(q, k, v, doc_ids=None, cu_seqlens=None, *, cp_size: int
 
 def docmask_gqa_attn_bwd(q, k, v, out, dout, lse, doc_ids=None, cu_seqlens=None, *,
                          cp_size: int, cp_rank: int, softmax_scale: Optional[float] = None,
-                         dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """dq [B,Sq,Hq,D] bf16, dk/dv [B,Skv,Hkv,D] fp32."""
+                         dq=None, dk=None, dv=None, workspace=None, stream=None, bounds=None):
+    """dq [B,Sq,Hq,D] bf16, dk/dv [B,Skv,Hkv,D] fp32.  Masking by doc_ids /
+    cu_seqlens, or by bounds from docmask_gqa_doc_bounds."""
     import torch
     for t, n in ((q, "q"), (out, "out"), (dout, "dout")):
         _need(t, n, torch.bfloat16, 4)
@@ -187,7 +239,10 @@ def docmask_gqa_attn_bwd(q, k, v, out, dout, lse, doc_ids=None, cu_seqlens=None,
     if tuple(v.shape) != tuple(k.shape):
         raise ValueError("k and v must match")
     S = Sq * cp_size
-    doc_ids, cu_seqlens, n_docs = _docs(doc_ids, cu_seqlens, B, S)
+    if bounds is None:
+        doc_ids, cu_seqlens, n_docs = _docs(doc_ids, cu_seqlens, B, S)
+    else:
+        _bounds_ok(bounds, doc_ids, cu_seqlens, B, S, Skv)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if dq is None:
@@ -202,11 +257,18 @@ def docmask_gqa_attn_bwd(q, k, v, out, dout, lse, doc_ids=None, cu_seqlens=None,
     need = docmask_gqa_bwd_workspace_size(B, S, Skv, Hq, Hkv, D, cp_size)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    rc = lib().docmask_gqa_attn_bwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(doc_ids),
-        _ptr(cu_seqlens), n_docs, B, S, Skv, Hq, Hkv, D, cp_size, cp_rank,
-        float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream))
+    if bounds is None:
+        rc = lib().docmask_gqa_attn_bwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(doc_ids),
+            _ptr(cu_seqlens), n_docs, B, S, Skv, Hq, Hkv, D, cp_size, cp_rank,
+            float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    else:
+        rc = lib().docmask_gqa_attn_bwd_bounds(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(bounds), B, S,
+            Skv, Hq, Hkv, D, cp_size, cp_rank, float(softmax_scale), _ptr(dq), _ptr(dk),
+            _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(stream))
     if rc != DMGQA_OK:
         raise DocmaskGQAError(rc, "docmask_gqa_attn_bwd")
     return dq, dk, dv

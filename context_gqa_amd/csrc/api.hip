@@ -140,15 +140,77 @@ Geo make_geo(const Shape& s, float scale) {
   return g;
 }
 
-int prep(const int32_t* doc_ids, const int32_t* cu, int n_docs, const Shape& s, char* ws,
-         const Layout& L, hipStream_t st) {
-  int32_t* dstart = reinterpret_cast<int32_t*>(ws + L.dstart);
-  int32_t* dend = reinterpret_cast<int32_t*>(ws + L.dend);
+// Document bounds dstart, dend [B, Skv] (agg: the scan's block aggregates,
+// 2 * B * ceil(Skv / 1024) ints; unused with cu_seqlens).
+int prep_bounds(const int32_t* doc_ids, const int32_t* cu, int n_docs, int B, int S, int Skv,
+                int32_t* dstart, int32_t* dend, int32_t* agg, hipStream_t st) {
   timing_begin(kKPrep, st);
-  hipError_t e = doc_ids ? launch_prep_docs(doc_ids, s.B, s.S, s.Skv, dstart, dend,
-                                            reinterpret_cast<int32_t*>(ws + L.agg), st)
-                         : launch_prep_cu(cu, n_docs, s.Skv, dstart, dend, st);
+  hipError_t e = doc_ids ? launch_prep_docs(doc_ids, B, S, Skv, dstart, dend, agg, st)
+                         : launch_prep_cu(cu, n_docs, Skv, dstart, dend, st);
   timing_end(kKPrep, st);
+  return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
+}
+
+// Bounds for one call: from the caller's precomputed array, or computed into
+// the workspace.
+int call_bounds(const int32_t* doc_ids, const int32_t* cu, int n_docs, const int32_t* bounds,
+                const Shape& s, char* ws, const Layout& L, hipStream_t st,
+                const int32_t** dstart, const int32_t** dend) {
+  if (bounds) {
+    *dstart = bounds;
+    *dend = bounds + (size_t)s.B * s.Skv;
+    return DMGQA_OK;
+  }
+  int32_t* ds = reinterpret_cast<int32_t*>(ws + L.dstart);
+  int32_t* de = reinterpret_cast<int32_t*>(ws + L.dend);
+  *dstart = ds;
+  *dend = de;
+  return prep_bounds(doc_ids, cu, n_docs, s.B, s.S, s.Skv, ds, de,
+                     reinterpret_cast<int32_t*>(ws + L.agg), st);
+}
+
+// Masking arguments: document ids / offsets, or a bounds array (exactly one
+// form).
+int check_mask_args(const int32_t* doc_ids, const int32_t* cu, int n_docs, const int32_t* bounds,
+                    const Shape& s) {
+  if (bounds) {
+    if (doc_ids || cu || !aligned(bounds, 4)) return DMGQA_ERR_INVALID_ARG;
+    return DMGQA_OK;
+  }
+  return check_docs_args(doc_ids, cu, n_docs, s);
+}
+
+int fwd_impl(const void* q, const void* k, const void* v, const int32_t* doc_ids,
+             const int32_t* cu_seqlens, int32_t n_docs, const int32_t* bounds, int32_t B,
+             int32_t S, int32_t Skv, int32_t Hq, int32_t Hkv, int32_t D, int32_t cp_size,
+             int32_t cp_rank, float softmax_scale, void* out, float* lse, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  Shape s;
+  int rc = check_shape(B, S, Skv, Hq, Hkv, D, cp_size, cp_rank, &s);
+  if (rc != DMGQA_OK) return rc;
+  if (!std::isfinite(softmax_scale) || softmax_scale == 0.f) return DMGQA_ERR_INVALID_ARG;
+  if (s.empty) return DMGQA_OK;
+  if (!q || !k || !v || !out || !lse || !workspace) return DMGQA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, 16))
+    return DMGQA_ERR_INVALID_ARG;
+  rc = check_mask_args(doc_ids, cu_seqlens, n_docs, bounds, s);
+  if (rc != DMGQA_OK) return rc;
+  const Layout L = layout(s, false);
+  if (workspace_bytes < L.total) return DMGQA_ERR_WORKSPACE;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int32_t* dstart;
+  const int32_t* dend;
+  rc = call_bounds(doc_ids, cu_seqlens, n_docs, bounds, s, ws, L, st, &dstart, &dend);
+  if (rc != DMGQA_OK) return rc;
+  const Geo g = make_geo(s, softmax_scale);
+  timing_begin(kKFwd, st);
+  hipError_t e = launch_fwd(D, static_cast<const u16*>(q), static_cast<const u16*>(k),
+                            static_cast<const u16*>(v), dstart, static_cast<u16*>(out), lse, g,
+                            st);
+  timing_end(kKFwd, st);
   return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
 }
 
@@ -193,40 +255,30 @@ int docmask_gqa_attn_fwd(const void* q, const void* k, const void* v, const int3
                          int32_t Skv, int32_t Hq, int32_t Hkv, int32_t D, int32_t cp_size,
                          int32_t cp_rank, float softmax_scale, void* out, float* lse,
                          void* workspace, size_t workspace_bytes, void* stream) {
-  Shape s;
-  int rc = check_shape(B, S, Skv, Hq, Hkv, D, cp_size, cp_rank, &s);
-  if (rc != DMGQA_OK) return rc;
-  if (!std::isfinite(softmax_scale) || softmax_scale == 0.f) return DMGQA_ERR_INVALID_ARG;
-  if (s.empty) return DMGQA_OK;
-  if (!q || !k || !v || !out || !lse || !workspace) return DMGQA_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-      !aligned(lse, 4) || !aligned(workspace, 16))
-    return DMGQA_ERR_INVALID_ARG;
-  rc = check_docs_args(doc_ids, cu_seqlens, n_docs, s);
-  if (rc != DMGQA_OK) return rc;
-  const Layout L = layout(s, false);
-  if (workspace_bytes < L.total) return DMGQA_ERR_WORKSPACE;
-
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  rc = prep(doc_ids, cu_seqlens, n_docs, s, ws, L, st);
-  if (rc != DMGQA_OK) return rc;
-  const Geo g = make_geo(s, softmax_scale);
-  timing_begin(kKFwd, st);
-  hipError_t e = launch_fwd(D, static_cast<const u16*>(q), static_cast<const u16*>(k),
-                            static_cast<const u16*>(v),
-                            reinterpret_cast<const int32_t*>(ws + L.dstart),
-                            static_cast<u16*>(out), lse, g, st);
-  timing_end(kKFwd, st);
-  return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
+  return fwd_impl(q, k, v, doc_ids, cu_seqlens, n_docs, nullptr, B, S, Skv, Hq, Hkv, D, cp_size,
+                  cp_rank, softmax_scale, out, lse, workspace, workspace_bytes, stream);
 }
 
-int docmask_gqa_attn_bwd(const void* q, const void* k, const void* v, const void* out,
-                         const void* dout, const float* lse, const int32_t* doc_ids,
-                         const int32_t* cu_seqlens, int32_t n_docs, int32_t B, int32_t S,
-                         int32_t Skv, int32_t Hq, int32_t Hkv, int32_t D, int32_t cp_size,
-                         int32_t cp_rank, float softmax_scale, void* dq, float* dk, float* dv,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+int docmask_gqa_attn_fwd_bounds(const void* q, const void* k, const void* v,
+                                const int32_t* bounds, int32_t B, int32_t S, int32_t Skv,
+                                int32_t Hq, int32_t Hkv, int32_t D, int32_t cp_size,
+                                int32_t cp_rank, float softmax_scale, void* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!bounds) return DMGQA_ERR_INVALID_ARG;
+  return fwd_impl(q, k, v, nullptr, nullptr, 0, bounds, B, S, Skv, Hq, Hkv, D, cp_size, cp_rank,
+                  softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace dmgqa {
+namespace {
+
+int bwd_impl(const void* q, const void* k, const void* v, const void* out, const void* dout,
+             const float* lse, const int32_t* doc_ids, const int32_t* cu_seqlens, int32_t n_docs,
+             const int32_t* bounds, int32_t B, int32_t S, int32_t Skv, int32_t Hq, int32_t Hkv,
+             int32_t D, int32_t cp_size, int32_t cp_rank, float softmax_scale, void* dq,
+             float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream) {
   Shape s;
   int rc = check_shape(B, S, Skv, Hq, Hkv, D, cp_size, cp_rank, &s);
   if (rc != DMGQA_OK) return rc;
@@ -238,7 +290,7 @@ int docmask_gqa_attn_bwd(const void* q, const void* k, const void* v, const void
       !aligned(dout, 16) || !aligned(dq, 16) || !aligned(lse, 4) || !aligned(dk, 16) ||
       !aligned(dv, 16) || !aligned(workspace, 16))
     return DMGQA_ERR_INVALID_ARG;
-  rc = check_docs_args(doc_ids, cu_seqlens, n_docs, s);
+  rc = check_mask_args(doc_ids, cu_seqlens, n_docs, bounds, s);
   if (rc != DMGQA_OK) return rc;
   const Layout L = layout(s, true);
   if (workspace_bytes < L.total_min) return DMGQA_ERR_WORKSPACE;
@@ -248,11 +300,11 @@ int docmask_gqa_attn_bwd(const void* q, const void* k, const void* v, const void
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  rc = prep(doc_ids, cu_seqlens, n_docs, s, ws, L, st);
+  const int32_t* dstart;
+  const int32_t* dend;
+  rc = call_bounds(doc_ids, cu_seqlens, n_docs, bounds, s, ws, L, st, &dstart, &dend);
   if (rc != DMGQA_OK) return rc;
   const Geo g = make_geo(s, softmax_scale);
-  const int32_t* dstart = reinterpret_cast<const int32_t*>(ws + L.dstart);
-  const int32_t* dend = reinterpret_cast<const int32_t*>(ws + L.dend);
   // per query row: -lse/scale, then -D
   float* Lbuf = reinterpret_cast<float*>(ws + L.rowstat);
   float* Nbuf = Lbuf + (size_t)s.B * s.Sq * s.Hq;
@@ -306,6 +358,61 @@ int docmask_gqa_attn_bwd(const void* q, const void* k, const void* v, const void
   e = launch_bwd_reduce(D, tile_info, partial, dk, dv, g, L.nkt, st);
   timing_end(kKReduce, st);
   return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace dmgqa
+
+extern "C" {
+
+int docmask_gqa_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                         const void* dout, const float* lse, const int32_t* doc_ids,
+                         const int32_t* cu_seqlens, int32_t n_docs, int32_t B, int32_t S,
+                         int32_t Skv, int32_t Hq, int32_t Hkv, int32_t D, int32_t cp_size,
+                         int32_t cp_rank, float softmax_scale, void* dq, float* dk, float* dv,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(q, k, v, out, dout, lse, doc_ids, cu_seqlens, n_docs, nullptr, B, S, Skv, Hq,
+                  Hkv, D, cp_size, cp_rank, softmax_scale, dq, dk, dv, workspace,
+                  workspace_bytes, stream);
+}
+
+int docmask_gqa_attn_bwd_bounds(const void* q, const void* k, const void* v, const void* out,
+                                const void* dout, const float* lse, const int32_t* bounds,
+                                int32_t B, int32_t S, int32_t Skv, int32_t Hq, int32_t Hkv,
+                                int32_t D, int32_t cp_size, int32_t cp_rank,
+                                float softmax_scale, void* dq, float* dk, float* dv,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!bounds) return DMGQA_ERR_INVALID_ARG;
+  return bwd_impl(q, k, v, out, dout, lse, nullptr, nullptr, 0, bounds, B, S, Skv, Hq, Hkv, D,
+                  cp_size, cp_rank, softmax_scale, dq, dk, dv, workspace, workspace_bytes,
+                  stream);
+}
+
+size_t docmask_gqa_doc_bounds_size(int32_t B, int32_t S, int32_t Skv) {
+  if (B <= 0 || S <= 0 || Skv <= 0 || Skv > S) return 0;
+  const size_t nblk = ((size_t)Skv + 1023) / 1024;
+  return (2 * (size_t)B * Skv + 2 * (size_t)B * nblk) * sizeof(int32_t);
+}
+
+int docmask_gqa_doc_bounds(const int32_t* doc_ids, const int32_t* cu_seqlens, int32_t n_docs,
+                           int32_t B, int32_t S, int32_t Skv, int32_t* bounds,
+                           size_t bounds_bytes, void* stream) {
+  if (B < 0 || S < 0 || Skv < 0 || Skv > S) return DMGQA_ERR_INVALID_ARG;
+  if (B == 0 || Skv == 0) return DMGQA_OK;
+  if ((long long)B * S >= (1LL << 31)) return DMGQA_ERR_UNSUPPORTED;
+  if ((doc_ids == nullptr) == (cu_seqlens == nullptr)) return DMGQA_ERR_INVALID_ARG;
+  if (doc_ids && !aligned(doc_ids, 4)) return DMGQA_ERR_INVALID_ARG;
+  if (cu_seqlens) {
+    if (B > 1) return DMGQA_ERR_UNSUPPORTED;
+    if (n_docs < 1 || n_docs > S || !aligned(cu_seqlens, 4)) return DMGQA_ERR_INVALID_ARG;
+  }
+  if (!bounds || !aligned(bounds, 4)) return DMGQA_ERR_INVALID_ARG;
+  if (bounds_bytes < docmask_gqa_doc_bounds_size(B, S, Skv)) return DMGQA_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  int32_t* dstart = bounds;
+  int32_t* dend = bounds + (size_t)B * Skv;
+  return prep_bounds(doc_ids, cu_seqlens, n_docs, B, S, Skv, dstart, dend,
+                     bounds + 2 * (size_t)B * Skv, st);
 }
 
 int docmask_gqa_check_docs(const int32_t* doc_ids, int32_t B, int32_t S, void* stream) {

@@ -129,6 +129,45 @@ int docmask_gqa_attn_bwd(const void* q, const void* k, const void* v,
                          float* dk, float* dv, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Document bounds of every key position, for callers that run several
+ * calls on the same batch (the forward and the backward of every layer):
+ *   bounds[0][b][t] = first position of t's document,
+ *   bounds[1][b][t] = one past its last position, capped at Skv,
+ * int32 [2, B, Skv] at the start of `bounds`, followed by scratch.  With the
+ * causal mask, query position p may attend to keys bounds[0][b][p] .. p
+ * (the document mask of "Paper notes: The Llama 3 Herd of Models", "Two
+ * architectural choices", as an interval per position).  Exactly one of
+ * doc_ids / cu_seqlens, as for the attention calls.  The caller allocates
+ * `bounds` (docmask_gqa_doc_bounds_size bytes, 4-byte aligned) and keeps it
+ * while later calls read it; the call is asynchronous on `stream`.
+ * docmask_gqa_doc_bounds_size returns 0 for invalid sizes. */
+size_t docmask_gqa_doc_bounds_size(int32_t B, int32_t S, int32_t Skv);
+int docmask_gqa_doc_bounds(const int32_t* doc_ids, const int32_t* cu_seqlens,
+                           int32_t n_docs, int32_t B, int32_t S, int32_t Skv,
+                           int32_t* bounds, size_t bounds_bytes, void* stream);
+
+/* The forward and backward with the masking given as a bounds array from
+ * docmask_gqa_doc_bounds (same B, S and Skv; its writes ordered before
+ * these calls) instead of doc_ids / cu_seqlens; everything else as in
+ * docmask_gqa_attn_fwd / docmask_gqa_attn_bwd, with the same workspace
+ * sizes.  The bounds are not validated against the sizes beyond alignment:
+ * a bounds array of other sizes is undefined behaviour. */
+int docmask_gqa_attn_fwd_bounds(const void* q, const void* k, const void* v,
+                                const int32_t* bounds, int32_t B, int32_t S,
+                                int32_t Skv, int32_t Hq, int32_t Hkv, int32_t D,
+                                int32_t cp_size, int32_t cp_rank,
+                                float softmax_scale, void* out, float* lse,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+int docmask_gqa_attn_bwd_bounds(const void* q, const void* k, const void* v,
+                                const void* out, const void* dout,
+                                const float* lse, const int32_t* bounds,
+                                int32_t B, int32_t S, int32_t Skv, int32_t Hq,
+                                int32_t Hkv, int32_t D, int32_t cp_size,
+                                int32_t cp_rank, float softmax_scale, void* dq,
+                                float* dk, float* dv, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Debug check of the document-id precondition.  Copies doc_ids [B, S] to the
  * host, synchronising `stream`.  Returns 0 if every id forms one contiguous
  * run in each batch row, 1 if some id reappears after a different id,

@@ -159,3 +159,51 @@ def test_binding_requires_device_tensors():
     with pytest.raises(TypeError):
         M.docmask_gqa_attn_fwd(q.float(), k, k, doc_ids=torch.zeros(1, 512, dtype=torch.int32),
                                cp_size=1, cp_rank=0)
+
+
+# ---------------------------------------------------------------- bounds API
+
+def test_doc_bounds_size():
+    f = M.docmask_gqa_doc_bounds_size
+    # [2, B, Skv] int32 plus two scan aggregates per 1024-position block
+    assert f(1, 8192, 8192) == (2 * 8192 + 2 * 8) * 4
+    assert f(2, 1000, 700) == (2 * 2 * 700 + 2 * 2 * 1) * 4
+    assert f(0, 8, 8) == 0 and f(1, 8, 9) == 0 and f(1, 8, 0) == 0
+
+
+def _bounds_call(**kw):
+    b = _Buf(1 << 16)
+    a = dict(doc=b.p, cu=None, n_docs=0, B=1, S=512, Skv=512, out=b.p, nbytes=1 << 16)
+    a.update({k: (b.p if v == "same" else v) for k, v in kw.items()})
+    return M.lib().docmask_gqa_doc_bounds(a["doc"], a["cu"], a["n_docs"], a["B"], a["S"],
+                                          a["Skv"], a["out"], a["nbytes"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(out=None), INV),
+    (dict(doc=None), INV),                                # neither
+    (dict(cu="same", n_docs=2), INV),                     # both
+    (dict(doc=None, cu="same", n_docs=2, B=2), UNS),      # cu_seqlens with B > 1
+    (dict(doc=None, cu="same", n_docs=0), INV),
+    (dict(Skv=513), INV),
+    (dict(nbytes=100), WS),
+])
+def test_doc_bounds_rejects(kw, want):
+    assert _bounds_call(**kw) == want
+
+
+def test_bounds_variants_reject():
+    b = _Buf()
+    L = M.lib()
+    common = (1, 512, 512, 4, 1, 64, 1, 0, 0.125)
+    # forward: null bounds; misaligned bounds; workspace too small
+    assert L.docmask_gqa_attn_fwd_bounds(b.p, b.p, b.p, None, *common, b.p, b.p, b.p, 1 << 12,
+                                        None) == INV
+    assert L.docmask_gqa_attn_fwd_bounds(b.p, b.p, b.p, b.p + 2, *common, b.p, b.p, b.p,
+                                        1 << 12, None) == INV
+    assert L.docmask_gqa_attn_fwd_bounds(b.p, b.p, b.p, b.p, *common, b.p, b.p, b.p, 0,
+                                        None) == WS
+    assert L.docmask_gqa_attn_bwd_bounds(b.p, b.p, b.p, b.p, b.p, b.p, None, *common, b.p, b.p,
+                                        b.p, b.p, 1 << 12, None) == INV
+    assert L.docmask_gqa_attn_bwd_bounds(b.p, b.p, b.p, b.p, b.p, b.p, b.p, *common, b.p, b.p,
+                                        b.p, b.p, 0, None) == WS

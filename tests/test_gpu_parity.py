@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+import context_gqa_amd as M
 import oracle
 import workloads as W
 from tests.gpu_util import (compare, dev, doc_start_end, gpu_bwd, gpu_fwd, host,
@@ -273,3 +274,40 @@ def test_cp_split_equals_unsplit_on_gpu():
     compare("dq cp4 vs cp1", host(dq), host(q1))
     compare("dk sum vs cp1", host(dk), host(k1))
     compare("dv sum vs cp1", host(dv), host(v1))
+
+
+@pytest.mark.parametrize("name,seed,rank,use_cu", [("tiny", 0, 0, False), ("tiny", 1, 0, True),
+                                                   ("short_docs", 0, 2, False),
+                                                   ("tp405b", 1, 0, True),
+                                                   ("long_cp", 0, 7, False)])
+def test_bounds_path_matches_doc_path(name, seed, rank, use_cu):
+    """docmask_gqa_doc_bounds equals the host's document starts / ends
+    (bit-exact, ends capped at Skv), and the *_bounds calls reproduce the
+    doc_ids calls bit for bit (same kernels, same bounds)."""
+    cfg = W.CONFIGS[name]
+    case = W.make_case(cfg, seed, rank)
+    say(f"[bounds {name} seed {seed} rank {rank} cu={use_cu}]")
+    d = dev(case, use_cu=use_cu)
+    B, Sq, Hq, D = case.q.shape
+    S = Sq * cfg.cp_size
+    kw = {"cu_seqlens": d["cu_seqlens"]} if use_cu else {"doc_ids": d["doc_ids"]}
+    bounds = M.docmask_gqa_doc_bounds(**kw, B=B, S=S, Skv=case.Skv)
+    torch.cuda.synchronize()
+    got = bounds[:2 * B * case.Skv].view(2, B, case.Skv).cpu().numpy()
+    for b in range(B):
+        start, end = doc_start_end(case.lengths[b])
+        assert np.array_equal(got[0, b], start[:case.Skv])
+        assert np.array_equal(got[1, b], np.minimum(end[:case.Skv], case.Skv))
+    out_a, lse_a = gpu_fwd(case, d, use_cu=use_cu)
+    out_b, lse_b = M.docmask_gqa_attn_fwd(d["q"], d["k"], d["v"], cp_size=cfg.cp_size,
+                                          cp_rank=rank, softmax_scale=case.scale, bounds=bounds)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
+    if cfg.backward or name == "tiny":
+        ga = gpu_bwd(case, d, out_a, lse_a, use_cu=use_cu)
+        gb = M.docmask_gqa_attn_bwd(d["q"], d["k"], d["v"], out_a, d["dout"], lse_a,
+                                    cp_size=cfg.cp_size, cp_rank=rank, softmax_scale=case.scale,
+                                    bounds=bounds)
+        torch.cuda.synchronize()
+        for x, y in zip(ga, gb):
+            assert torch.equal(x, y)
