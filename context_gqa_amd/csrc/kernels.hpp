@@ -12,15 +12,20 @@ namespace dmgqa {
 // workgroup of 4 waves (32 rows per wave), 64 keys per step.
 constexpr int kFwdBM = 128;
 constexpr int kFwdBN = 64;
-// dK/dV kernel: 128 keys per work item (4 waves x 32), query rows streamed
+// dK/dV kernel: 128 keys per work item (8 waves x 16), query rows streamed
 // 64 at a time.
 constexpr int kDkdvBN = 128;
 constexpr int kDkdvBM = 64;
 // Split of the query rows reaching one key tile into work items: at least
 // this many rows per item, and about kMaxSplitTotal split items per call.
-constexpr int kMinRowsPerSplit = 512;
-constexpr int kMaxSplitTotal = 512;
+// With one split per persistent workgroup a full split is one workgroup's
+// even share of the rows, and the remainders fill the rest; on the 405B TP
+// share this beat 512 splits (fewer partial slots to add: reduce 22 -> 13
+// us) and lost badly at 320 or 384 (a second round of full splits on some
+// workgroups).
 constexpr int kDkdvGrid = 256;  // persistent workgroups of the dK/dV kernel
+constexpr int kMinRowsPerSplit = 512;
+constexpr int kMaxSplitTotal = kDkdvGrid;
 // dS stash: blocks of kStashRows query rows (aligned within each KV head's
 // row index tok*G + head) x kDkdvBN keys of one key tile, bf16.
 constexpr int kStashRows = 32;
