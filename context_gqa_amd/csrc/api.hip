@@ -334,9 +334,9 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
     if (e != hipSuccess) return DMGQA_ERR_HIP;
     timing_begin(kKDq, st);
     e = launch_bwd_dq_stash(D, kh, dstart, tile_rows, stash, L.stash_kvh_blocks,
-                            static_cast<u16*>(dq), g, L.nkt, st);
+                            static_cast<u16*>(dq), tile_info, partial, dk, dv, g, L.nkt, st);
     timing_end(kKDq, st);
-    if (e != hipSuccess) return DMGQA_ERR_HIP;
+    return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
   } else {
     timing_begin(kKSched, st);
     e = launch_sched_dkdv(dend, g, L.nkt, L.max_split_base, hdr, tile_info, items, tile_rows,

@@ -22,6 +22,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "qtile.hpp"
+#include "reduce.hpp"
 #include "tileload.hpp"
 
 namespace dmgqa {
@@ -151,36 +152,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   }
 }
 
-// Sum of the partial slots of each split key tile, in item order.  One
-// workgroup per (key tile, KV head, 1024-float chunk).
+// Sum of the partial slots of each split key tile, in item order.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const int2* __restrict__ tile_info,
                                                          const float* __restrict__ partial,
                                                          float* __restrict__ dk,
                                                          float* __restrict__ dv, Geo g, int nkt) {
-  constexpr int BN = kDkdvBN;
-  constexpr int kChunks = 2 * BN * D / 1024;
-  const int chunk = blockIdx.x % kChunks;
-  const int th = blockIdx.x / kChunks;
-  const int x = th / g.Hkv, kvh = th % g.Hkv;
-  const int2 info = tile_info[x];
-  if (info.x <= 1) return;
-  const int b = x / nkt, kt = x % nkt;
-  const int t0 = kt * BN;
-  const size_t kvstride = (size_t)g.Hkv * D;
-  const int e = chunk * 1024 + threadIdx.x * 4;
-  const int which = e / (BN * D);
-  const int kvloc = (e % (BN * D)) / D, col = e % D;
-  if (t0 + kvloc >= g.Skv) return;
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < info.x; ++sp) {
-    const size_t slot = (size_t)(info.y + sp) * g.Hkv + kvh;
-    s += *reinterpret_cast<const f32x4*>(partial + slot * 2 * BN * D + e);
-  }
-  if (which == 0) s *= g.scale;
-  float* dst = (which == 0 ? dk : dv) + ((size_t)b * g.Skv + t0 + kvloc) * kvstride +
-               (size_t)kvh * D + col;
-  *reinterpret_cast<f32x4*>(dst) = s;
+  reduce_partials<D>(tile_info, partial, dk, dv, g, nkt, (int)blockIdx.x);
 }
 
 hipError_t launch_bwd_dq(int D, const u16* q, const u16* k, const u16* v, const u16* out,
@@ -197,11 +175,12 @@ hipError_t launch_bwd_dq(int D, const u16* q, const u16* k, const u16* v, const 
 
 hipError_t launch_bwd_reduce(int D, const int2* tile_info, const float* partial, float* dk,
                              float* dv, const Geo& g, int nkt, hipStream_t st) {
-  const unsigned rgrid = (unsigned)g.B * nkt * g.Hkv * (2 * kDkdvBN * D / 1024);
   if (D == 128)
-    bwd_reduce_kernel<128><<<rgrid, 256, 0, st>>>(tile_info, partial, dk, dv, g, nkt);
+    bwd_reduce_kernel<128><<<reduce_grid<128>(g, nkt), 256, 0, st>>>(tile_info, partial, dk, dv,
+                                                                      g, nkt);
   else
-    bwd_reduce_kernel<64><<<rgrid, 256, 0, st>>>(tile_info, partial, dk, dv, g, nkt);
+    bwd_reduce_kernel<64><<<reduce_grid<64>(g, nkt), 256, 0, st>>>(tile_info, partial, dk, dv, g,
+                                                                    nkt);
   return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@
 #include "dma.hpp"
 #include "kernels.hpp"
 #include "qtile.hpp"
+#include "reduce.hpp"
 
 namespace dmgqa {
 
@@ -63,7 +64,10 @@ __device__ __forceinline__ void dma_asm16(const void* sbase, unsigned voff, char
 }  // namespace
 
 // One workgroup = 4 stash blocks (128 query rows of one KV head): wave w
-// owns block J = 4*qb + w.  Key tiles of 128 are those reaching any of the
+// owns block J = 4*qb + w.  Workgroups past the dQ grid (dq_grid onwards)
+// add the partial dK/dV slots of the split key tiles instead: dispatched
+// after every dQ workgroup, they run in the launch's tail, where the long
+// row blocks leave memory bandwidth unused.  Key tiles of 128 are those reaching any of the
 // 128 rows; their K tiles stream through two LDS stages (DMA one tile
 // ahead), and the wave's dS operands are loaded into registers two tiles
 // ahead.  Rows of a block outside the tile's reach hold
@@ -72,7 +76,12 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
     const u16* __restrict__ k, const int32_t* __restrict__ dstart,
     const int4* __restrict__ tile_rows, const u16* __restrict__ stash, int stash_kvh_blocks,
-    u16* __restrict__ dq, Geo g, int nkt) {
+    u16* __restrict__ dq, const int2* __restrict__ tile_info, const float* __restrict__ partial,
+    float* __restrict__ dk, float* __restrict__ dv, Geo g, int nkt, int dq_grid) {
+  if ((int)blockIdx.x >= dq_grid) {
+    reduce_partials<D>(tile_info, partial, dk, dv, g, nkt, (int)blockIdx.x - dq_grid);
+    return;
+  }
   using KT = KTile<D>;
   constexpr int DB = D / 32, NCH = D / 8, BN = kDkdvBN;
   __shared__ __attribute__((aligned(1024))) char sk0[KT::kBytes];
@@ -244,16 +253,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
 }
 
 hipError_t launch_bwd_dq_stash(int D, const u16* k, const int32_t* dstart, const int4* tile_rows,
-                               const u16* stash, int stash_kvh_blocks, u16* dq, const Geo& g,
-                               int nkt, hipStream_t st) {
+                               const u16* stash, int stash_kvh_blocks, u16* dq,
+                               const int2* tile_info, const float* partial, float* dk, float* dv,
+                               const Geo& g, int nkt, hipStream_t st) {
   const int nqb = (g.Sq * g.G + 127) / 128;
   const unsigned grid = (unsigned)nqb * g.B * g.Hkv;
   if (D == 128)
-    bwd_dq_stash_kernel<128><<<grid, 256, 0, st>>>(k, dstart, tile_rows, stash, stash_kvh_blocks,
-                                                   dq, g, nkt);
+    bwd_dq_stash_kernel<128><<<grid + reduce_grid<128>(g, nkt), 256, 0, st>>>(
+        k, dstart, tile_rows, stash, stash_kvh_blocks, dq, tile_info, partial, dk, dv, g, nkt,
+        (int)grid);
   else
-    bwd_dq_stash_kernel<64><<<grid, 256, 0, st>>>(k, dstart, tile_rows, stash, stash_kvh_blocks,
-                                                  dq, g, nkt);
+    bwd_dq_stash_kernel<64><<<grid + reduce_grid<64>(g, nkt), 256, 0, st>>>(
+        k, dstart, tile_rows, stash, stash_kvh_blocks, dq, tile_info, partial, dk, dv, g, nkt,
+        (int)grid);
   return hipGetLastError();
 }
 

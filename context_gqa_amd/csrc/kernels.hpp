@@ -62,9 +62,12 @@ hipError_t launch_sched_rowstat(int D, const int32_t* dend, const Geo& g, int nk
                                 int max_split_base, SchedHeader* hdr, int2* tile_info,
                                 int2* items, int4* tile_rows, const u16* out, const u16* dout,
                                 const float* lse, float* Lbuf, float* Nbuf, hipStream_t st);
+// dQ from the dS stash, and (in workgroups appended to its grid) the sum of
+// the partial dK/dV slots.
 hipError_t launch_bwd_dq_stash(int D, const u16* k, const int32_t* dstart, const int4* tile_rows,
-                               const u16* stash, int stash_kvh_blocks, u16* dq, const Geo& g,
-                               int nkt, hipStream_t st);
+                               const u16* stash, int stash_kvh_blocks, u16* dq,
+                               const int2* tile_info, const float* partial, float* dk, float* dv,
+                               const Geo& g, int nkt, hipStream_t st);
 hipError_t launch_bwd_reduce(int D, const int2* tile_info, const float* partial, float* dk,
                              float* dv, const Geo& g, int nkt, hipStream_t st);
 
