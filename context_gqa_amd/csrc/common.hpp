@@ -24,6 +24,10 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
+
+// Cache-policy operand of the buffer load / store builtins: the
+// non-temporal bit (streaming data that is not reused soon).
+constexpr int kCachePolicyNT = 2;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -350,7 +350,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
                                                       wave * 1024 + (32 * h + (grow & 31)) * 16)
                                          : 0x80000000u;
       const bf16x8 op = tr_operand_pad<kTrLd>(T, 0, 0, 0, lane);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, op), srs, off, 0, 0);
+      // non-temporal: the stash is read once, by the dQ kernel, long after
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, op), srs, off, 0,
+                                             kCachePolicyNT);
     };
 
     // S = Q K^T and dP = dO V^T of one sub-block (rows q0.. of stage st):

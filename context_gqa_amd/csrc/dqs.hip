@@ -168,14 +168,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
     const int rel = J - tr.z;
     const bool have = d.in && rel >= 0 && rel < nblk;
     // one block through a buffer resource (wave-uniform base) and a fixed
-    // per-lane offset
+    // per-lane offset; non-temporal (the stash is read once: keeping it out
+    // of the caches took the kernel from 138 to 117 us on the 405B share)
     const u16* blk = stash_h + (have ? (size_t)(tr.w + rel) * (kStashBlockBytes / 2) : 0);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<u16*>(blk), 0, kStashBlockBytes, 0x00020000);
 #pragma unroll
     for (int kq = 0; kq < 8; ++kq)
       d.op[kq] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + kq * 1024, 0, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + kq * 1024, 0, kCachePolicyNT));
   };
   f32x16 acc[DB];
 #pragma unroll
