@@ -78,6 +78,29 @@ def algorithmic_bytes(case, backward: bool) -> int:
 
 
 COPY_CALIBRATION_BYTES = 512 << 20
+# A cold repetition first writes this many bytes, more than the GPU's L2 and
+# last-level (Infinity) cache hold, so the step starts without cached inputs.
+FLUSH_BYTES = 512 << 20
+
+
+def sample_clocks(delay_s: float = 0.5):
+    """Current shader and memory clocks (MHz) from rocm-smi, read delay_s
+    seconds into a phase in which the GPU is busy with steps (returns a
+    dict, or None with the reason when rocm-smi is unavailable)."""
+    import re
+    import subprocess
+    time.sleep(delay_s)
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                             timeout=30).stdout
+    except Exception as e:  # noqa: BLE001 - reported, not fatal
+        return {"error": f"rocm-smi: {e}"}
+    res = {}
+    for key in ("sclk", "mclk", "fclk"):
+        m = re.search(key + r"[^\n]*?\((\d+)\s*Mhz\)", out, re.IGNORECASE)
+        if m:
+            res[key + "_mhz"] = int(m.group(1))
+    return res or {"error": "no clock lines in rocm-smi output"}
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -190,6 +213,8 @@ def main(argv=None) -> int:
     ap.add_argument("--seeds", default="0,1,2,3,4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip reading the GPU clocks with rocm-smi during a busy phase")
     ap.add_argument("--recompute", action="store_true",
                     help="give the backward its minimum workspace (no dS stash: dQ recomputes "
                          "the scores)")
@@ -261,10 +286,9 @@ def main(argv=None) -> int:
                          flops=useful_flops(pairs, Hq, D, cfg.backward),
                          bytes=algorithmic_bytes(case, cfg.backward)))
 
-    def step(i):
-        """One step on seed i's inputs, on the current stream: the document
-        bounds of the batch (computed from doc_ids in every step), then the
-        forward and the backward, both reading them."""
+    def fwd_part(i):
+        """The document bounds of seed i's batch (computed from doc_ids in
+        every step) and the forward."""
         r = runs[i % len(runs)]
         t, case = r["t"], r["case"]
         M.docmask_gqa_doc_bounds(t["doc"], B=case.cfg.B, S=cfg.S, Skv=case.Skv,
@@ -272,11 +296,21 @@ def main(argv=None) -> int:
         M.docmask_gqa_attn_fwd(t["q"], t["k"], t["v"], cp_size=cfg.cp_size, cp_rank=rank,
                                softmax_scale=case.scale, out=t["out"], lse=t["lse"],
                                workspace=t["wsf"], bounds=t["bounds"])
+
+    def bwd_part(i):
+        r = runs[i % len(runs)]
+        t, case = r["t"], r["case"]
         if cfg.backward:
             M.docmask_gqa_attn_bwd(t["q"], t["k"], t["v"], t["out"], t["dout"], t["lse"],
                                    cp_size=cfg.cp_size, cp_rank=rank, softmax_scale=case.scale,
                                    dq=t["dq"], dk=t["dk"], dv=t["dv"], workspace=t["wsb"],
                                    bounds=t["bounds"])
+
+    def step(i):
+        """One step on seed i's inputs, on the current stream: the document
+        bounds, then the forward and the backward, both reading them."""
+        fwd_part(i)
+        bwd_part(i)
 
     # With --graph each seed's step is captured once into a HIP graph (the
     # library makes no allocation, synchronisation or memset inside a call)
@@ -326,6 +360,63 @@ def main(argv=None) -> int:
         b.record(stream)
         torch.cuda.synchronize()
         per_seed.append(r["flops"]["total"] / (a.elapsed_time(b) / reps * 1e-3) / 1e12)
+
+    # Per seed: forward (with the bounds) and backward timed separately by
+    # HIP events around each of `reps` back-to-back repetitions (median),
+    # warm (inputs possibly cached from the previous repetition) and cold
+    # (each repetition preceded by a write of FLUSH_BYTES).
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def seed_detail(j, reps, cold):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+        for e in ev:
+            if cold:
+                flush.fill_(1.0)
+            e[0].record(stream)
+            fwd_part(j)
+            e[1].record(stream)
+            bwd_part(j)
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        fw = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+        bw = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+        st = float(np.median([e[0].elapsed_time(e[2]) for e in ev]))
+        return fw, bw, st
+
+    detail = []
+    for j, r in enumerate(runs):
+        fw, bw, st = seed_detail(j, 20, False)
+        cfw, cbw, cst = seed_detail(j, 20, True)
+        fl = r["flops"]
+        d = {"seed": r["case"].seed, "fwd_ms": round(fw, 4), "bwd_ms": round(bw, 4),
+             "step_ms": round(st, 4), "tflops": round(fl["total"] / (st * 1e-3) / 1e12, 2),
+             "fwd_tflops": round(fl["fwd"] / (fw * 1e-3) / 1e12, 2),
+             "alg_gbps": round(r["bytes"] / (st * 1e-3) / 1e9, 1),
+             "cold": {"fwd_ms": round(cfw, 4), "bwd_ms": round(cbw, 4), "step_ms": round(cst, 4),
+                      "tflops": round(fl["total"] / (cst * 1e-3) / 1e12, 2)}}
+        if cfg.backward:
+            d["bwd_tflops"] = round((fl["total"] - fl["fwd"]) / (bw * 1e-3) / 1e12, 2)
+        detail.append(d)
+    del flush
+
+    # Clocks while the GPU is busy with steps (rocm-smi from a second thread,
+    # after the timed measurements so that it cannot disturb them).
+    clocks = None
+    if not args.no_clocks:
+        import threading
+        box = {}
+        th = threading.Thread(target=lambda: box.update(c=sample_clocks()))
+        th.start()
+        t_end = time.perf_counter() + 1.5
+        i = 0
+        while time.perf_counter() < t_end or th.is_alive():
+            step(i)
+            i += 1
+            if i % 64 == 0:
+                torch.cuda.synchronize()
+        th.join()
+        torch.cuda.synchronize()
+        clocks = box.get("c")
 
     roofline = None
     kernels = {}
@@ -389,6 +480,8 @@ def main(argv=None) -> int:
         "per_seed_tflops": [round(x, 2) for x in per_seed],
         "median_seed_tflops": round(float(np.median(per_seed)), 2),
         "useful_gflop_per_seed": [round(r["flops"]["total"] / 1e9, 2) for r in runs],
+        "per_seed": detail,
+        "clocks": clocks,
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -165,8 +165,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) char stg[4 * Lds::kStage];
   __shared__ int s_item;
   // per-wave transpose scratch of the dS stash: [16 keys][32 rows] bf16,
-  // row stride 40
-  constexpr int kTrLd = 40;
+  // 64 bytes per key, its eight 8-byte pieces (4 rows each) permuted by
+  // piece ^ tr_swz(key): the transposed read of a 32-lane half covers four
+  // whole keys (all 64 banks once), and the four keys whose rows share a
+  // bank window write disjoint pieces (SQ_LDS_BANK_CONFLICT: the earlier
+  // padded rows of 40 elements cost ~4 conflict cycles per access)
+  constexpr int kTrLd = 32;
   __shared__ __attribute__((aligned(16))) u16 s_tr[STASH ? kWaves * kWaveKeys * kTrLd : 1];
 
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
@@ -331,11 +335,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
           tile_blocks * kStashBlockBytes, 0x00020000);
     // (1) dS to this wave's transpose scratch, key-major: lane (g4, j) holds
     // key j at rows 16t + 4*g4 + 0..3.
+    auto tr_swz = [](int key) __attribute__((always_inline)) { return 2 * ((key >> 2) & 3); };
     auto stash_put = [&](const bf16x8& dsop) __attribute__((always_inline)) {
       u16* T = s_tr + wave * kWaveKeys * kTrLd;
       const u32x4 w4 = __builtin_bit_cast(u32x4, dsop);
-      *reinterpret_cast<uint2*>(T + j * kTrLd + 4 * g4) = uint2{w4[0], w4[1]};
-      *reinterpret_cast<uint2*>(T + j * kTrLd + 16 + 4 * g4) = uint2{w4[2], w4[3]};
+      *reinterpret_cast<uint2*>(T + j * kTrLd + 4 * (g4 ^ tr_swz(j))) = uint2{w4[0], w4[1]};
+      *reinterpret_cast<uint2*>(T + j * kTrLd + 4 * ((4 + g4) ^ tr_swz(j))) =
+          uint2{w4[2], w4[3]};
     };
     // (2) transposed read: lane (h, i) gets row i, keys 8(e/4) + 4h + e%4
     // of the wave's 16, stored as chunk (w, lane) of the row's stash block.
@@ -349,7 +355,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       const unsigned off = R + i < r_end ? (unsigned)(((grow >> 5) - tr_z) * kStashBlockBytes +
                                                       wave * 1024 + (32 * h + (grow & 31)) * 16)
                                          : 0x80000000u;
-      const bf16x8 op = tr_operand_pad<kTrLd>(T, 0, 0, 0, lane);
+      // transposed read (as a padded-tile operand read, with the pieces
+      // permuted): 16-lane group grp reads keys 4(grp/2) + s/4 (+8),
+      // rows 16(grp%2) + 4(s%4) .. +3
+      const int s4 = lane & 15, grp = lane >> 4;
+      const int k0 = 4 * (grp >> 1) + (s4 >> 2), k1 = k0 + 8;
+      const int pc = 4 * (grp & 1) + (s4 & 3);
+      const i16x4 lo = ds_read_tr(T + k0 * kTrLd + 4 * (pc ^ tr_swz(k0)));
+      const i16x4 hi = ds_read_tr(T + k1 * kTrLd + 4 * (pc ^ tr_swz(k1)));
+      const bf16x4 la = __builtin_bit_cast(bf16x4, lo), ha = __builtin_bit_cast(bf16x4, hi);
+      const bf16x8 op = {la[0], la[1], la[2], la[3], ha[0], ha[1], ha[2], ha[3]};
       // non-temporal: the stash is read once, by the dQ kernel, long after
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, op), srs, off, 0,
                                              kCachePolicyNT);
