@@ -203,6 +203,104 @@ def cpu_baseline(runs, min_s: float = 10.0, max_s: float = 30.0) -> dict:
                       f"backward on seeds {done} (same inputs as the GPU steps)"}
 
 
+def all_ranks(args) -> int:
+    """Per-rank study of one workload on one GPU: every CP rank's share
+    (forward with its document bounds, then backward), timed by HIP events
+    (median of `--steps` repetitions per rank), with the document mask of
+    each seed and with a single document over the whole sequence (pure
+    causal mask, same shapes).  Prints one JSON line: per rank the key
+    prefix, allowed pairs per head, forward / backward / step times and
+    useful TFLOP/s; per mask the slowest / fastest rank ratio of the step
+    time and of throughput."""
+    import torch
+    import context_gqa_amd as M
+    import workloads as W
+    cfg = W.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    seeds = [int(x) for x in args.seeds.split(",") if x != ""]
+    ranks = list(range(cfg.cp_size))
+    B, S, Hq, Hkv, D = cfg.B, cfg.S, cfg.Hq, cfg.Hkv, cfg.D
+    c = W.chunk_len(S, cfg.cp_size)
+    Sq = 2 * c
+    f_ws = max(M.docmask_gqa_fwd_workspace_size(B, S, W.kv_prefix_len(S, cfg.cp_size, r), Hq,
+                                                 Hkv, D, cfg.cp_size) for r in ranks)
+    b_ws = max(M.docmask_gqa_bwd_workspace_size(B, S, W.kv_prefix_len(S, cfg.cp_size, r), Hq,
+                                                Hkv, D, cfg.cp_size) for r in ranks)
+    wsf = torch.empty(max(1, f_ws), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(max(1, b_ws), dtype=torch.uint8, device=dev)
+    out = torch.empty(B, Sq, Hq, D, dtype=torch.bfloat16, device=dev)
+    dq = torch.empty_like(out)
+    lse = torch.empty(B, Sq, Hq, dtype=torch.float32, device=dev)
+    dk = torch.empty(B, S, Hkv, D, dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    bounds = torch.empty(M.docmask_gqa_doc_bounds_size(B, S, S) // 4, dtype=torch.int32,
+                         device=dev)
+    stream = torch.cuda.current_stream()
+    res = {"study": "per-rank imbalance", "workload": f"{cfg.name}: {cfg.description}",
+           "cp_size": cfg.cp_size, "ranks": ranks, "seeds": seeds, "reps": args.steps,
+           "masks": {}}
+    for mask in ("document", "causal"):
+        per = []
+        for seed in seeds:
+            full = W.full_tensors(cfg, seed)
+            lengths = None if mask == "document" else [[S] for _ in range(B)]
+            qg, kg, vg, dg = (x.to(dev) for x in full)
+            for r in ranks:
+                case = W.make_case(cfg, seed, r, full=full, lengths=lengths)
+                Skv = case.Skv
+                q = W.take_local_rows(qg, S, cfg.cp_size, r)
+                do = W.take_local_rows(dg, S, cfg.cp_size, r)
+                k, v = kg[:, :Skv], vg[:, :Skv]
+                doc = torch.from_numpy(case.doc_ids).to(dev)
+                dkr, dvr = dk[:, :Skv], dv[:, :Skv]
+                pairs = sum(allowed_pairs(l, S, cfg.cp_size, r) for l in case.lengths)
+                fl = useful_flops(pairs, Hq, D, cfg.backward)
+
+                def fwd():
+                    M.docmask_gqa_doc_bounds(doc, B=B, S=S, Skv=Skv, out=bounds)
+                    M.docmask_gqa_attn_fwd(q, k, v, cp_size=cfg.cp_size, cp_rank=r,
+                                           softmax_scale=case.scale, out=out, lse=lse,
+                                           workspace=wsf, bounds=bounds)
+
+                def bwd():
+                    M.docmask_gqa_attn_bwd(q, k, v, out, do, lse, cp_size=cfg.cp_size, cp_rank=r,
+                                           softmax_scale=case.scale, dq=dq, dk=dkr, dv=dvr,
+                                           workspace=wsb, bounds=bounds)
+                for _ in range(args.warmup):
+                    fwd(); bwd()
+                ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                      for _ in range(args.steps)]
+                for e in ev:
+                    e[0].record(stream); fwd(); e[1].record(stream); bwd(); e[2].record(stream)
+                torch.cuda.synchronize()
+                fw = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+                bw = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+                st = float(np.median([e[0].elapsed_time(e[2]) for e in ev]))
+                per.append({"seed": seed, "rank": r, "Skv": Skv, "pairs_per_head": pairs,
+                            "fwd_ms": round(fw, 4), "bwd_ms": round(bw, 4), "step_ms": round(st, 4),
+                            "tflops": round(fl["total"] / (st * 1e-3) / 1e12, 2)})
+                print(f"{mask} seed {seed} rank {r}: {st:.3f} ms, {per[-1]['tflops']} TFLOP/s",
+                      file=sys.stderr, flush=True)
+            del qg, kg, vg, dg, full
+        summ = {}
+        for seed in seeds:
+            rows = [x for x in per if x["seed"] == seed]
+            t = [x["step_ms"] for x in rows]
+            f = [x["tflops"] for x in rows]
+            summ[str(seed)] = {"slowest_over_fastest_step": round(max(t) / min(t), 3),
+                               # a CP group waits for its slowest rank
+                               "mean_over_slowest_step": round(float(np.mean(t)) / max(t), 3),
+                               "slowest_rank": rows[int(np.argmax(t))]["rank"],
+                               "fastest_rank": rows[int(np.argmin(t))]["rank"],
+                               "tflops_min": min(f), "tflops_max": max(f),
+                               "tflops_all_ranks": round(
+                                   sum(x["pairs_per_head"] for x in rows) * Hq * 12 * D
+                                   / (sum(t) * 1e-3) / 1e12, 2)}
+        res["masks"][mask] = {"per_rank": per, "summary": summ}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,6 +311,9 @@ def main(argv=None) -> int:
     ap.add_argument("--seeds", default="0,1,2,3,4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--all-ranks", action="store_true",
+                    help="per-rank study instead of the benchmark line: every CP rank of the "
+                         "workload, document and single-document masks (see all_ranks)")
     ap.add_argument("--no-clocks", action="store_true",
                     help="skip reading the GPU clocks with rocm-smi during a busy phase")
     ap.add_argument("--recompute", action="store_true",
@@ -254,6 +355,8 @@ def main(argv=None) -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     M.lib()
+    if args.all_ranks:
+        return all_ranks(args)
     cfg = W.CONFIGS[args.workload]
     rank = cfg.ranks[0] if args.rank is None else args.rank
     seeds = [int(s) for s in args.seeds.split(",") if s != ""]
