@@ -88,15 +88,14 @@ typedef __attribute__((address_space(3))) char lds_char;
 // wait for the block just issued); the kernel orders every read of a stage
 // after an explicit vmcnt wait and a barrier instead.
 template <int IMM>
-__device__ __forceinline__ void dma_lds16(const void* sbase, unsigned voff, char* lds) {
-  const unsigned m0 =
-      __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_char*)lds) - (unsigned)IMM;
+__device__ __forceinline__ void dma_lds16(const void* sbase, unsigned voff, unsigned lds) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds) - (unsigned)IMM;
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(voff),
                "s"(sbase), "s"(m0), "i"(IMM)
                : "memory");
 }
-__device__ __forceinline__ void dma_lds4(const void* sbase, unsigned voff, char* lds) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_char*)lds);
+__device__ __forceinline__ void dma_lds4(const void* sbase, unsigned voff, unsigned lds) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase),
                "s"(m0)
                : "memory");
@@ -163,6 +162,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   // ring of 4 stages (kStage is a multiple of 256 bytes)
   static_assert(Lds::kStage % 256 == 0, "stage alignment");
   __shared__ __attribute__((aligned(1024))) char stg[4 * Lds::kStage];
+  // LDS byte address of stg, taken once (the cast checks for null); DMA
+  // addresses are offsets from it
+  const unsigned stg_lds = (unsigned)(uintptr_t)(lds_char*)stg;
+  auto lds_of = [&](const char* p) __attribute__((always_inline)) {
+    return stg_lds + (unsigned)(p - stg);
+  };
   __shared__ int s_item;
   // per-wave transpose scratch of the dS stash: [16 keys][32 rows] bf16,
   // 64 bytes per key, its eight 8-byte pieces (4 rows each) permuted by
@@ -299,15 +304,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       char* tq = st + 64 * 16 * rq + c0 * kGroupBytes;
       static_for<D / 64>([&](auto m) __attribute__((always_inline)) {
         constexpr int M = decltype(m)::value;
-        dma_lds16<128 * M>(q, nx_qoff, tq + 2 * M * kGroupBytes);
+        dma_lds16<128 * M>(q, nx_qoff, lds_of(tq) + 2 * M * kGroupBytes);
       });
       // row statistics, lanes 0..15: rows 16(w%4) + lane; waves 0-3 load
       // -lse/scale, waves 4-7 -D
       if (lane < 16) {
         if (wave < 4)
-          dma_lds4(Lbuf, nx_ridm * 4u, st + Lds::kL + 64 * rq);
+          dma_lds4(Lbuf, nx_ridm * 4u, lds_of(st) + Lds::kL + 64 * rq);
         else
-          dma_lds4(Nbuf, nx_ridm * 4u, st + Lds::kN + 64 * rq);
+          dma_lds4(Nbuf, nx_ridm * 4u, lds_of(st) + Lds::kN + 64 * rq);
       }
     };
     auto issue_o = [&](char* st) __attribute__((always_inline)) {
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       char* tq = st + Lds::kTile + 64 * 16 * rq + c0 * kGroupBytes;
       static_for<D / 64>([&](auto m) __attribute__((always_inline)) {
         constexpr int M = decltype(m)::value;
-        dma_lds16<128 * M>(dout, nx_qoff, tq + 2 * M * kGroupBytes);
+        dma_lds16<128 * M>(dout, nx_qoff, lds_of(tq) + 2 * M * kGroupBytes);
       });
     };
 

@@ -53,9 +53,8 @@ typedef __attribute__((address_space(3))) char lds_char;
 // wave-uniform).  The immediate offset moves the LDS address too, so M0 is
 // lds - IMM.
 template <int IMM>
-__device__ __forceinline__ void dma_asm16(const void* sbase, unsigned voff, char* lds) {
-  const unsigned m0 =
-      __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_char*)lds) - (unsigned)IMM;
+__device__ __forceinline__ void dma_asm16(const void* sbase, unsigned voff, unsigned lds) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds) - (unsigned)IMM;
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(voff),
                "s"(sbase), "s"(m0), "i"(IMM)
                : "memory");
@@ -84,8 +83,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
   }
   using KT = KTile<D>;
   constexpr int DB = D / 32, NCH = D / 8, BN = kDkdvBN;
-  __shared__ __attribute__((aligned(1024))) char sk0[KT::kBytes];
-  __shared__ __attribute__((aligned(1024))) char sk1[KT::kBytes];
+  __shared__ __attribute__((aligned(1024))) char sk[2 * KT::kBytes];
+  char* const sk0 = sk;
+  char* const sk1 = sk + KT::kBytes;
+  // LDS byte address of sk, taken once (the cast checks for null)
+  const unsigned sk_lds = (unsigned)(uintptr_t)(lds_char*)sk;
 
   const int nrows = g.Sq * g.G;
   const int nqb = (nrows + 127) / 128;
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
       char* dst = st + hf * KT::kHalf + 64 * 16 * wave;
       static_for<NCH / 4>([&](auto cc) __attribute__((always_inline)) {
         constexpr int C = decltype(cc)::value;
-        dma_asm16<64 * C>(tb, off, dst + C * kGroupBytes);
+        dma_asm16<64 * C>(tb, off, sk_lds + (unsigned)(dst - sk) + C * kGroupBytes);
       });
     };
     if (!partial) {

@@ -52,9 +52,8 @@ constexpr float kRescaleLog2 = 8.f;
 // compiler adds no waits of its own for these LDS writes; every read of a
 // stage follows an explicit vmcnt wait and a barrier.
 template <int IMM>
-__device__ __forceinline__ void dma_lds16(const void* sbase, unsigned voff, char* lds) {
-  const unsigned m0 =
-      __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_char*)lds) - (unsigned)IMM;
+__device__ __forceinline__ void dma_lds16(const void* sbase, unsigned voff, unsigned lds) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds) - (unsigned)IMM;
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(voff),
                "s"(sbase), "s"(m0), "i"(IMM)
                : "memory");
@@ -94,6 +93,9 @@ __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict
   constexpr int kTile = D / 32 * kGroupBytes;   // bytes of a K (or V) tile
   constexpr int kStage = 2 * kTile;
   __shared__ __attribute__((aligned(1024))) char stg[2 * kStage];
+  // LDS byte address of stg (the cast to the LDS address space checks for
+  // null, so it is taken once; DMA addresses are offsets from it)
+  const unsigned stg_lds = (unsigned)(uintptr_t)(lds_char*)stg;
 
   const int nrows = g.Sq * g.G;
   const int nt = (nrows + BM - 1) / BM;
@@ -164,13 +166,15 @@ __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict
   auto issue_k = [&](unsigned off, char* st) __attribute__((always_inline)) {
     static_for<D / 32>([&](auto cc) __attribute__((always_inline)) {
       constexpr int C = decltype(cc)::value;
-      dma_lds16<64 * C>(kbase, off, st + 64 * 16 * wave + C * kGroupBytes);
+      dma_lds16<64 * C>(kbase, off,
+                        stg_lds + (unsigned)(st - stg) + 64 * 16 * wave + C * kGroupBytes);
     });
   };
   auto issue_v = [&](unsigned off, char* st) __attribute__((always_inline)) {
     static_for<D / 32>([&](auto cc) __attribute__((always_inline)) {
       constexpr int C = decltype(cc)::value;
-      dma_lds16<64 * C>(vbase, off, st + kTile + 64 * 16 * wave + C * kGroupBytes);
+      dma_lds16<64 * C>(vbase, off,
+                        stg_lds + (unsigned)(st - stg) + kTile + 64 * 16 * wave + C * kGroupBytes);
     });
   };
 
@@ -198,12 +202,15 @@ __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict
     if (!full) {
       // allowed keys lo..pos relative to this lane's first key t0 + 4h;
       // register r holds key offset 8*(r/4) + r%4 (+32 for s1)
-      const int lo_rel = lo - (t0 + 4 * h), hi_rel = pos - (t0 + 4 * h);
+      // key offset c is allowed iff lo_rel <= c <= hi_rel, one unsigned
+      // compare (hi_rel >= lo_rel: a row always sees its own position)
+      const int lo_rel = lo - (t0 + 4 * h);
+      const unsigned span = (unsigned)(pos - lo);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int c = 8 * (r >> 2) + (r & 3);
-        if (c < lo_rel || c > hi_rel) s0[r] = -INFINITY;
-        if (c + 32 < lo_rel || c + 32 > hi_rel) s1[r] = -INFINITY;
+        if ((unsigned)(c - lo_rel) > span) s0[r] = -INFINITY;
+        if ((unsigned)(c + 32 - lo_rel) > span) s1[r] = -INFINITY;
       }
     }
     float mx = max3f(s0[0], s1[0], s0[1]);
