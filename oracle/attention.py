@@ -20,6 +20,14 @@ What it computes, and where the pages state it:
   the model is a causal decoder ("full causal mask" in Herd section 3.3.2).
   Reading used here: key t is allowed for query position p iff t <= p and
   doc(t) == doc(p).
+* Interval masks -- "Scaling Llama 3 Training with Efficient Parallelism
+  Strategies" (review), section "Context Parallelism (CP)", implementation
+  details and Figure 7: with the whole K/V gathered, a rank can apply any
+  attention mask (causal, document, CP-document are drawn).  The form
+  supported here is a causal mask with a per-position window start: key t is
+  allowed for query position p iff lo[p] <= t <= p (lo given per position;
+  the document mask is lo = first position of p's document).  Every
+  function below takes either doc_ids or lo.
 * GQA -- Herd section 3.3.2 and "Paper notes", "Two architectural choices":
   groups of query heads share one key/value head.  Reading used here:
   contiguous groups, query head h uses KV head h // (Hq // Hkv).
@@ -51,7 +59,7 @@ from typing import List, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
-    "chunk_positions", "allowed_mask", "allowed_counts", "attn_probs",
+    "chunk_positions", "allowed_mask", "interval_mask", "allowed_counts", "attn_probs",
     "attn_fwd", "attn_bwd", "attn_fwd_rows", "attn_bwd_rows",
     "attn_bwd_kv_rows", "to_f64",
 ]
@@ -88,17 +96,35 @@ def allowed_mask(doc: np.ndarray, pos: np.ndarray, Skv: int) -> np.ndarray:
     return causal & same_doc
 
 
-def allowed_counts(doc_ids: np.ndarray, cp_size: int, cp_rank: int, Skv: int,
-                   block: int = 256) -> np.ndarray:
+def interval_mask(lo: np.ndarray, pos: np.ndarray, Skv: int) -> np.ndarray:
+    """Explicit boolean mask M[i, t] for query positions `pos` over keys
+    t in [0, Skv): lo[p] <= t <= p."""
+    t = np.arange(Skv, dtype=np.int64)
+    return (t[None, :] >= np.asarray(lo)[pos][:, None]) & (t[None, :] <= pos[:, None])
+
+
+def _masks(doc_ids, lo):
+    """The mask source: (array [B, S], fn(b, positions, Skv) -> explicit mask)."""
+    if (doc_ids is None) == (lo is None):
+        raise ValueError("pass exactly one of doc_ids / lo")
+    if lo is not None:
+        arr = np.asarray(lo)
+        return arr, lambda b, p, Skv: interval_mask(arr[b], p, Skv)
+    arr = np.asarray(doc_ids)
+    return arr, lambda b, p, Skv: allowed_mask(arr[b], p, Skv)
+
+
+def allowed_counts(doc_ids: Optional[np.ndarray], cp_size: int, cp_rank: int, Skv: int,
+                   block: int = 256, lo: Optional[np.ndarray] = None) -> np.ndarray:
     """Number of allowed keys of every local row, counted from the explicit
-    mask.  doc_ids: [B, S].  Returns int64 [B, Sq]."""
-    doc_ids = np.asarray(doc_ids)
-    B, S = doc_ids.shape
+    mask.  doc_ids (or lo): [B, S].  Returns int64 [B, Sq]."""
+    arr, mask = _masks(doc_ids, lo)
+    B, S = arr.shape
     pos = chunk_positions(S, cp_size, cp_rank)
     out = np.zeros((B, pos.size), dtype=np.int64)
     for b in range(B):
         for s in range(0, pos.size, block):
-            out[b, s:s + block] = allowed_mask(doc_ids[b], pos[s:s + block], Skv).sum(1)
+            out[b, s:s + block] = mask(b, pos[s:s + block], Skv).sum(1)
     return out
 
 
@@ -193,13 +219,15 @@ def _check(q, k, doc_ids, cp_size, cp_rank):
     return B, Sq, Hq, D, Skv, Hkv, Hq // Hkv, pos
 
 
-def attn_probs(q, k, doc_ids, cp_size: int, cp_rank: int, softmax_scale: float):
+def attn_probs(q, k, doc_ids, cp_size: int, cp_rank: int, softmax_scale: float,
+               lo=None):
     """Explicit probability matrix P [B, Sq, Hq, Skv] (small cases only)."""
-    q = to_f64(q); k = to_f64(k); doc_ids = np.asarray(doc_ids)
-    B, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, doc_ids, cp_size, cp_rank)
+    q = to_f64(q); k = to_f64(k)
+    arr, mask = _masks(doc_ids, lo)
+    B, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, arr, cp_size, cp_rank)
     P = np.zeros((B, Sq, Hq, Skv))
     for b in range(B):
-        M = allowed_mask(doc_ids[b], pos, Skv)
+        M = mask(b, pos, Skv)
         for g in range(Hkv):
             hs = _group_heads(g, G)
             p, _, _ = _softmax_block(q[b, :, hs], k[b, :, g], k[b, :, g], M, softmax_scale)
@@ -208,11 +236,13 @@ def attn_probs(q, k, doc_ids, cp_size: int, cp_rank: int, softmax_scale: float):
 
 
 def attn_fwd(q, k, v, doc_ids, cp_size: int, cp_rank: int, softmax_scale: float,
-             window: bool = True, threads: Optional[int] = None):
+             window: bool = True, threads: Optional[int] = None, lo=None):
     """Forward.  q [B,Sq,Hq,D] (local rows), k/v [B,Skv,Hkv,D] (gathered,
-    global order), doc_ids [B,S].  Returns out [B,Sq,Hq,D], lse [B,Sq,Hq]."""
-    q = to_f64(q); k = to_f64(k); v = to_f64(v); doc_ids = np.asarray(doc_ids)
-    B, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, doc_ids, cp_size, cp_rank)
+    global order), doc_ids [B,S] (or lo [B,S]).  Returns out [B,Sq,Hq,D],
+    lse [B,Sq,Hq]."""
+    q = to_f64(q); k = to_f64(k); v = to_f64(v)
+    arr, mask = _masks(doc_ids, lo)
+    B, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, arr, cp_size, cp_rank)
     out = np.zeros((B, Sq, Hq, D))
     lse = np.zeros((B, Sq, Hq))
     nb = _blocks(Sq, G, Skv if not window else min(Skv, 16384))
@@ -221,7 +251,7 @@ def attn_fwd(q, k, v, doc_ids, cp_size: int, cp_rank: int, softmax_scale: float,
     def work(t):
         b, g, s = t
         e = min(s + nb, Sq)
-        M = allowed_mask(doc_ids[b], pos[s:e], Skv)
+        M = mask(b, pos[s:e], Skv)
         lo, hi = _window(M, window)
         hs = _group_heads(g, G)
         _, o, l = _softmax_block(q[b, s:e, hs], k[b, lo:hi, g], v[b, lo:hi, g],
@@ -238,13 +268,13 @@ def attn_fwd(q, k, v, doc_ids, cp_size: int, cp_rank: int, softmax_scale: float,
 
 def attn_bwd(q, k, v, dout, doc_ids, cp_size: int, cp_rank: int,
              softmax_scale: float, window: bool = True,
-             threads: Optional[int] = None, return_fwd: bool = False):
+             threads: Optional[int] = None, return_fwd: bool = False, lo=None):
     """Backward.  Recomputes P and the oracle's own fp64 output, then applies
     the chain rule.  Returns dq [B,Sq,Hq,D], dk/dv [B,Skv,Hkv,D] (rows that no
     local query reaches are exactly 0); with return_fwd also out and lse."""
     q = to_f64(q); k = to_f64(k); v = to_f64(v); dout = to_f64(dout)
-    doc_ids = np.asarray(doc_ids)
-    B, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, doc_ids, cp_size, cp_rank)
+    arr, mask = _masks(doc_ids, lo)
+    B, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, arr, cp_size, cp_rank)
     dq = np.zeros((B, Sq, Hq, D))
     dk = np.zeros((B, Skv, Hkv, D))
     dv = np.zeros((B, Skv, Hkv, D))
@@ -258,7 +288,7 @@ def attn_bwd(q, k, v, dout, doc_ids, cp_size: int, cp_rank: int,
         b, g, s = t
         e = min(s + nb, Sq)
         n = e - s
-        M = allowed_mask(doc_ids[b], pos[s:e], Skv)
+        M = mask(b, pos[s:e], Skv)
         lo, hi = _window(M, window)
         hs = _group_heads(g, G)
         qb = q[b, s:e, hs]
@@ -287,12 +317,13 @@ def attn_bwd(q, k, v, dout, doc_ids, cp_size: int, cp_rank: int,
 
 # --- sampled forms for workloads too large for the full oracle ---------------
 
-def _row_stats(q, k, v, doc_b, pos_rows, scale, G, g):
-    """out, lse, window per single row (all G heads of KV group g)."""
+def _row_stats(q, k, v, mask_b, pos_rows, scale, G, g):
+    """out, lse, window per single row (all G heads of KV group g); mask_b
+    gives the explicit mask of query positions over the keys."""
     res = []
     Skv = k.shape[0]
     for p, qr in zip(pos_rows, q):
-        M = allowed_mask(doc_b, np.array([p]), Skv)
+        M = mask_b(np.array([p]), Skv)
         lo, hi = _window(M, True)
         P, o, l = _softmax_block(qr[None], k[lo:hi, g], v[lo:hi, g], M[:, lo:hi], scale)
         res.append((lo, hi, P[0], o[0], l[0]))
@@ -300,35 +331,40 @@ def _row_stats(q, k, v, doc_b, pos_rows, scale, G, g):
 
 
 def attn_fwd_rows(q, k, v, doc_ids, cp_size: int, cp_rank: int,
-                  softmax_scale: float, b: int, rows: Sequence[int]):
+                  softmax_scale: float, b: int, rows: Sequence[int], lo=None):
     """out [n, Hq, D] and lse [n, Hq] of selected local rows of batch b.
     Each row is computed on its own, exactly as in attn_fwd."""
     q = to_f64(q[b:b + 1]); k = to_f64(k[b:b + 1]); v = to_f64(v[b:b + 1])
-    doc_ids = np.asarray(doc_ids)[b:b + 1]
-    _, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, doc_ids, cp_size, cp_rank)
+    arr, mask = _masks(None if doc_ids is None else np.asarray(doc_ids)[b:b + 1],
+                       None if lo is None else np.asarray(lo)[b:b + 1])
+    _, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, arr, cp_size, cp_rank)
     rows = np.asarray(rows, dtype=np.int64)
     out = np.zeros((rows.size, Hq, D)); lse = np.zeros((rows.size, Hq))
     for g in range(Hkv):
         hs = _group_heads(g, G)
         for i, (lo, hi, P, o, l) in enumerate(
-                _row_stats(q[0, rows][:, hs], k[0], v[0], doc_ids[0], pos[rows], softmax_scale, G, g)):
+                _row_stats(q[0, rows][:, hs], k[0], v[0], lambda p, n: mask(0, p, n), pos[rows],
+                           softmax_scale, G, g)):
             out[i, hs] = o
             lse[i, hs] = l
     return out, lse
 
 
 def attn_bwd_rows(q, k, v, dout, doc_ids, cp_size: int, cp_rank: int,
-                  softmax_scale: float, b: int, rows: Sequence[int]):
+                  softmax_scale: float, b: int, rows: Sequence[int], lo=None):
     """dq [n, Hq, D] of selected local rows of batch b (each row's dq needs
     only that row's own probabilities and output)."""
     q = to_f64(q[b:b + 1]); k = to_f64(k[b:b + 1]); v = to_f64(v[b:b + 1])
-    dout = to_f64(dout[b:b + 1]); doc_ids = np.asarray(doc_ids)[b:b + 1]
-    _, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, doc_ids, cp_size, cp_rank)
+    dout = to_f64(dout[b:b + 1])
+    arr, mask = _masks(None if doc_ids is None else np.asarray(doc_ids)[b:b + 1],
+                       None if lo is None else np.asarray(lo)[b:b + 1])
+    _, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, arr, cp_size, cp_rank)
     rows = np.asarray(rows, dtype=np.int64)
     dq = np.zeros((rows.size, Hq, D))
     for g in range(Hkv):
         hs = _group_heads(g, G)
-        stats = _row_stats(q[0, rows][:, hs], k[0], v[0], doc_ids[0], pos[rows], softmax_scale, G, g)
+        stats = _row_stats(q[0, rows][:, hs], k[0], v[0], lambda p, n: mask(0, p, n), pos[rows],
+                           softmax_scale, G, g)
         for i, (lo, hi, P, o, l) in enumerate(stats):
             do = dout[0, rows[i], hs]                      # [G, D]
             Dr = (do * o).sum(-1)
@@ -340,30 +376,32 @@ def attn_bwd_rows(q, k, v, dout, doc_ids, cp_size: int, cp_rank: int,
 
 def attn_bwd_kv_rows(q, k, v, dout, doc_ids, cp_size: int, cp_rank: int,
                      softmax_scale: float, b: int, kv_rows: Sequence[int],
-                     max_query_rows: Optional[int] = None):
+                     max_query_rows: Optional[int] = None, lo=None):
     """dk, dv [n, Hkv, D] at selected key positions of batch b.  Every local
     row that reaches one of those keys gets its full forward (lse and output)
     computed first, as attn_bwd does; then the keys' columns of dS and P are
     summed over those rows and all heads of the group."""
     q = to_f64(q[b:b + 1]); k = to_f64(k[b:b + 1]); v = to_f64(v[b:b + 1])
-    dout = to_f64(dout[b:b + 1]); doc_ids = np.asarray(doc_ids)[b:b + 1]
-    _, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, doc_ids, cp_size, cp_rank)
+    dout = to_f64(dout[b:b + 1])
+    doc_b = None if doc_ids is None else np.asarray(doc_ids)[b:b + 1]
+    lo_b = None if lo is None else np.asarray(lo)[b:b + 1]
+    arr, mask = _masks(doc_b, lo_b)
+    _, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, arr, cp_size, cp_rank)
     kv_rows = np.asarray(kv_rows, dtype=np.int64)
-    doc = doc_ids[0]
     # Which local rows reach any selected key: explicit mask, row blocks.
     reach = np.zeros(Sq, dtype=bool)
     for s in range(0, Sq, 512):
-        M = allowed_mask(doc, pos[s:s + 512], Skv)
+        M = mask(0, pos[s:s + 512], Skv)
         reach[s:s + 512] = M[:, kv_rows].any(1)
     rows = np.flatnonzero(reach)
     if max_query_rows is not None and rows.size > max_query_rows:
         raise ValueError(f"{rows.size} query rows reach the selected keys "
                          f"(limit {max_query_rows})")
-    out, lse = attn_fwd_rows(q, k, v, doc_ids, cp_size, cp_rank, softmax_scale, 0, rows)
+    out, lse = attn_fwd_rows(q, k, v, doc_b, cp_size, cp_rank, softmax_scale, 0, rows, lo=lo_b)
     dk = np.zeros((kv_rows.size, Hkv, D)); dv = np.zeros((kv_rows.size, Hkv, D))
     if rows.size == 0:
         return dk, dv
-    M = allowed_mask(doc, pos[rows], Skv)[:, kv_rows]          # [n, T]
+    M = mask(0, pos[rows], Skv)[:, kv_rows]                    # [n, T]
     for g in range(Hkv):
         hs = _group_heads(g, G)
         qr = q[0, rows][:, hs]                                   # [n, G, D]

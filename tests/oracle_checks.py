@@ -380,10 +380,91 @@ def check_sampled_forms(orc):
             assert np.max(np.abs(dv2 - dv[b, kvr])) < 1e-12
 
 
+def _window_lo(lengths, Wn):
+    """lo[p] of a sliding window of Wn keys inside documents, from the lengths."""
+    p = np.arange(sum(lengths))
+    return np.maximum(_doc_start_from_lengths(lengths), p - Wn + 1)
+
+
+def _band_docmask(lengths, Wn):
+    """Explicit [S, S] mask: same document, causal, at most Wn keys back."""
+    m = _docmask_from_lengths(lengths)
+    i = np.arange(m.shape[0])
+    return m & (i[None, :] > i[:, None] - Wn)
+
+
+def check_interval_brute(orc):
+    """interval_mask is lo[p] <= t <= p, and the row counts are p - lo[p] + 1."""
+    g = np.random.default_rng(5)
+    S, Skv = 40, 40
+    lo = np.minimum(np.maximum.accumulate(g.integers(0, S, S)), np.arange(S))
+    pos = np.arange(S)
+    M = orc.interval_mask(lo, pos, Skv)
+    for p in range(S):
+        for t in range(Skv):
+            assert M[p, t] == (lo[p] <= t <= p)
+    cnt = orc.allowed_counts(None, 1, 0, Skv, lo=lo[None])
+    assert np.array_equal(cnt[0], pos - lo + 1)
+
+
+def check_interval_sliding_window(orc):
+    """A sliding window of W keys inside documents (lo = max(document start,
+    p - W + 1)) equals full-sequence attention with an explicit band mask,
+    forward through torch SDPA and backward through torch.autograd, both in
+    float64, on every CP rank."""
+    S, cp, Hq, Hkv, D = 96, 2, 4, 2, 8
+    lengths = [11, 40, 1, 44]
+    Wn = 7
+    doc, q, k, v, do = _case(S, cp, Hq, Hkv, D, lengths, seed=41)
+    lo = _window_lo(lengths, Wn)[None]
+    scale = 0.3
+    mask = _band_docmask(lengths, Wn)
+    ref = _sdpa_full(q, k, v, mask, scale)
+    G = Hq // Hkv
+    qt = torch.from_numpy(q).requires_grad_(True)
+    kt = torch.from_numpy(k).requires_grad_(True)
+    vt = torch.from_numpy(v).requires_grad_(True)
+    sc = torch.einsum("bshd,bthd->bhst", qt, kt.repeat_interleave(G, dim=2)) * scale
+    pr = torch.softmax(sc.masked_fill(~torch.from_numpy(mask), float("-inf")), -1)
+    o = torch.einsum("bhst,bthd->bshd", pr, vt.repeat_interleave(G, dim=2))
+    c = S // (2 * cp)
+    for r in range(cp):
+        Skv = (2 * cp - r) * c
+        ql, dol = _local(q, S, cp, r), _local(do, S, cp, r)
+        out, _ = orc.attn_fwd(ql, k[:, :Skv], v[:, :Skv], None, cp, r, scale, threads=1, lo=lo)
+        assert np.max(np.abs(out - _local(ref, S, cp, r))) < 1e-12, r
+        pos = torch.from_numpy(orc.chunk_positions(S, cp, r))
+        for t in (qt, kt, vt):
+            t.grad = None
+        (o[:, pos] * torch.from_numpy(dol)).sum().backward(retain_graph=True)
+        dq, dk, dv = orc.attn_bwd(ql, k[:, :Skv], v[:, :Skv], dol, None, cp, r, scale,
+                                  threads=1, lo=lo)
+        assert np.max(np.abs(dq - qt.grad[:, pos].numpy())) < 1e-11
+        assert np.max(np.abs(dk - kt.grad[:, :Skv].numpy())) < 1e-11
+        assert np.max(np.abs(dv - vt.grad[:, :Skv].numpy())) < 1e-11
+
+
+def check_interval_is_document_mask(orc):
+    """lo = first position of each document gives the document-masked result."""
+    S, cp, Hq, Hkv, D = 64, 2, 4, 1, 8
+    lengths = [5, 30, 29]
+    doc, q, k, v, do = _case(S, cp, Hq, Hkv, D, lengths, seed=51)
+    lo = _doc_start_from_lengths(lengths)[None]
+    c = S // (2 * cp)
+    for r in range(cp):
+        Skv = (2 * cp - r) * c
+        args = (_local(q, S, cp, r), k[:, :Skv], v[:, :Skv], _local(do, S, cp, r))
+        a = orc.attn_bwd(*args, doc, cp, r, 0.4, threads=1, return_fwd=True)
+        b = orc.attn_bwd(*args, None, cp, r, 0.4, threads=1, return_fwd=True, lo=lo)
+        for x, y in zip(a, b):
+            assert np.max(np.abs(x - y)) == 0.0
+
+
 ALL_CHECKS = [
     check_chunk_permutation, check_causal_equal_work, check_interval_rule,
     check_q_zero, check_softmax_rows, check_per_document,
     check_sdpa_explicit_mask, check_gqa_vs_mha, check_cp_split,
     check_finite_differences, check_autograd, check_window,
-    check_sampled_forms,
+    check_sampled_forms, check_interval_brute, check_interval_sliding_window,
+    check_interval_is_document_mask,
 ]

@@ -93,6 +93,11 @@ def _mut_heads_strided(g, G):
     return slice(g, None, max(1, G))
 
 
+def _mut_interval_open_lo(lo, pos, Skv):
+    t = np.arange(Skv)
+    return (t[None, :] > np.asarray(lo)[pos][:, None]) & (t[None, :] <= pos[:, None])
+
+
 def _mut_softmax_no_scale(qb, kw, vw, M, scale):
     return _ORIG['_softmax_block'](qb, kw, vw, M, 1.0)
 
@@ -107,6 +112,7 @@ MUTATIONS = {
     "dv_uses_out": ("_backward_block", _mut_dv_transposed),
     "heads_strided": ("_group_heads", _mut_heads_strided),
     "softmax_no_scale": ("_softmax_block", _mut_softmax_no_scale),
+    "interval_open_lo": ("interval_mask", _mut_interval_open_lo),
 }
 
 
