@@ -51,6 +51,8 @@ SIGNATURES = {
     "docmask_gqa_doc_bounds": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "docmask_gqa_check_docs": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
     "docmask_gqa_check_cu_seqlens": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
+    "docmask_gqa_interval_bounds": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "docmask_gqa_check_intervals": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
     "docmask_gqa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "docmask_gqa_version": (ctypes.c_int, []),
     "docmask_gqa_timing_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -282,6 +284,36 @@ def docmask_gqa_check_docs(doc_ids, stream=None) -> int:
     rc = lib().docmask_gqa_check_docs(_ptr(doc_ids), B, S, _stream(stream))
     if rc < 0:
         raise DocmaskGQAError(rc, "docmask_gqa_check_docs")
+    return rc
+
+
+def docmask_gqa_interval_bounds(lo, *, Skv: int, out=None, stream=None):
+    """Bounds of the causal interval mask "query p attends to keys lo[b, p] .. p"
+    (lo int32 [B, S], non-decreasing along p, 0 <= lo[p] <= p) for the
+    attention calls' `bounds=` argument; same buffer as docmask_gqa_doc_bounds."""
+    import torch
+    _need(lo, "lo", torch.int32, 2)
+    B, S = lo.shape
+    need = docmask_gqa_doc_bounds_size(B, S, Skv)
+    if out is None:
+        out = torch.empty(max(need // 4, 1), dtype=torch.int32, device=lo.device)
+    _need(out, "bounds", torch.int32, 1)
+    rc = lib().docmask_gqa_interval_bounds(_ptr(lo), B, S, Skv, _ptr(out), out.numel() * 4,
+                                           _stream(stream))
+    if rc != DMGQA_OK:
+        raise DocmaskGQAError(rc, "docmask_gqa_interval_bounds")
+    return out
+
+
+def docmask_gqa_check_intervals(lo, stream=None) -> int:
+    """0 if every row of lo [B, S] is non-decreasing with 0 <= lo[p] <= p
+    (synchronises)."""
+    import torch
+    _need(lo, "lo", torch.int32, 2)
+    B, S = lo.shape
+    rc = lib().docmask_gqa_check_intervals(_ptr(lo), B, S, _stream(stream))
+    if rc < 0:
+        raise DocmaskGQAError(rc, "docmask_gqa_check_intervals")
     return rc
 
 

@@ -415,6 +415,38 @@ int docmask_gqa_doc_bounds(const int32_t* doc_ids, const int32_t* cu_seqlens, in
                      bounds + 2 * (size_t)B * Skv, st);
 }
 
+int docmask_gqa_interval_bounds(const int32_t* lo, int32_t B, int32_t S, int32_t Skv,
+                                int32_t* bounds, size_t bounds_bytes, void* stream) {
+  if (B < 0 || S < 0 || Skv < 0 || Skv > S) return DMGQA_ERR_INVALID_ARG;
+  if (B == 0 || Skv == 0) return DMGQA_OK;
+  if ((long long)B * S >= (1LL << 31)) return DMGQA_ERR_UNSUPPORTED;
+  if (!lo || !aligned(lo, 4)) return DMGQA_ERR_INVALID_ARG;
+  if (!bounds || !aligned(bounds, 4)) return DMGQA_ERR_INVALID_ARG;
+  if (bounds_bytes < docmask_gqa_doc_bounds_size(B, S, Skv)) return DMGQA_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return launch_prep_interval(lo, B, S, Skv, bounds, bounds + (size_t)B * Skv, st) == hipSuccess
+             ? DMGQA_OK
+             : DMGQA_ERR_HIP;
+}
+
+int docmask_gqa_check_intervals(const int32_t* lo, int32_t B, int32_t S, void* stream) {
+  if (B < 0 || S < 0) return DMGQA_ERR_INVALID_ARG;
+  if (B == 0 || S == 0) return 0;
+  if (!lo) return DMGQA_ERR_INVALID_ARG;
+  std::vector<int32_t> h((size_t)B * S);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(h.data(), lo, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return DMGQA_ERR_HIP;
+  for (int b = 0; b < B; ++b) {
+    const int32_t* l = h.data() + (size_t)b * S;
+    for (int p = 0; p < S; ++p)
+      if (l[p] < 0 || l[p] > p || (p > 0 && l[p] < l[p - 1])) return 1;
+  }
+  return 0;
+}
+
 int docmask_gqa_check_docs(const int32_t* doc_ids, int32_t B, int32_t S, void* stream) {
   if (B < 0 || S < 0) return DMGQA_ERR_INVALID_ARG;
   if (B == 0 || S == 0) return 0;

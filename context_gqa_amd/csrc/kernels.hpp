@@ -43,6 +43,9 @@ hipError_t launch_prep_docs(const int32_t* doc, int B, int S, int Skv, int32_t* 
                             int32_t* dend, int32_t* agg, hipStream_t st);
 hipError_t launch_prep_cu(const int32_t* cu, int n_docs, int Skv, int32_t* dstart, int32_t* dend,
                           hipStream_t st);
+// Bounds of an interval mask (keys lo[p] .. p) from lo [B, S].
+hipError_t launch_prep_interval(const int32_t* lo, int B, int S, int Skv, int32_t* dstart,
+                                int32_t* dend, hipStream_t st);
 hipError_t launch_sched_dkdv(const int32_t* dend, const Geo& g, int nkt, int max_split_base,
                              SchedHeader* hdr, int2* tile_info, int2* items, int4* tile_rows,
                              hipStream_t st);

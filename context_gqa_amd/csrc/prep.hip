@@ -137,6 +137,34 @@ __global__ __launch_bounds__(256) void prep_cu(const int32_t* __restrict__ cu, i
   dend[t] = min(cu[lo + 1], Skv);
 }
 
+// Interval masks: query position p attends to keys lo[p] .. p, lo
+// non-decreasing with 0 <= lo[p] <= p (the all-gathered K/V let a CP rank
+// apply any mask of this kind: "Scaling Llama 3 Training with Efficient
+// Parallelism Strategies", section "Context Parallelism (CP)", Figure 7).
+// The document mask is lo = first position of p's document; a sliding
+// window of W keys inside documents is lo = max(document start, p - W + 1).
+// The attention kernels need the same two arrays as for documents:
+//   dstart[t] = lo[t]
+//   dend[t]   = one past the last query position p with lo[p] <= t, capped
+//               at Skv (lo non-decreasing: the first p > t with lo[p] > t,
+//               by binary search over (t, S)).
+// grid = (ceil(Skv / 256), B).
+__global__ __launch_bounds__(256) void prep_interval(const int32_t* __restrict__ lo, int S,
+                                                     int Skv, int32_t* __restrict__ dstart,
+                                                     int32_t* __restrict__ dend) {
+  const int b = blockIdx.y;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= Skv) return;
+  const int32_t* l = lo + (size_t)b * S;
+  dstart[(size_t)b * Skv + t] = l[t];
+  int a = t + 1, z = S;   // first p in [t+1, S) with l[p] > t, or S
+  while (a < z) {
+    const int mid = (a + z) >> 1;
+    if (l[mid] > t) z = mid; else a = mid + 1;
+  }
+  dend[(size_t)b * Skv + t] = min(a, Skv);
+}
+
 // Local token range(s) whose positions fall in [p0, p1): at most one range
 // in each of the rank's two chunks.
 __device__ __forceinline__ void token_ranges(int p0, int p1, const Geo& g, int& a0, int& na,
@@ -352,6 +380,13 @@ hipError_t launch_prep_docs(const int32_t* doc, int B, int S, int Skv, int32_t* 
                                                  agg + (size_t)B * nblk);
   prep_scan_fix<<<grid, kScanThreads, 0, st>>>(Skv, nblk, dstart, dend, agg,
                                                agg + (size_t)B * nblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_interval(const int32_t* lo, int B, int S, int Skv, int32_t* dstart,
+                                int32_t* dend, hipStream_t st) {
+  dim3 grid((Skv + 255) / 256, B);
+  prep_interval<<<grid, 256, 0, st>>>(lo, S, Skv, dstart, dend);
   return hipGetLastError();
 }
 

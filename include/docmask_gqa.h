@@ -146,11 +146,29 @@ int docmask_gqa_doc_bounds(const int32_t* doc_ids, const int32_t* cu_seqlens,
                            int32_t n_docs, int32_t B, int32_t S, int32_t Skv,
                            int32_t* bounds, size_t bounds_bytes, void* stream);
 
+/* Bounds of a causal interval mask: query position p (global, 0 <= p < S)
+ * attends to keys lo[b][p] .. p, where lo (int32 [B, S], device, 4-byte
+ * aligned) is non-decreasing along p with 0 <= lo[p] <= p.  The all-gathered
+ * K/V let each CP rank apply such masks ("Scaling Llama 3 Training with
+ * Efficient Parallelism Strategies", section "Context Parallelism (CP)",
+ * Figure 7: causal, document and CP-document masks); besides the document
+ * mask (lo = first position of p's document) this covers a sliding window
+ * of W keys, also inside documents (lo = max(document start, p - W + 1)).
+ * Writes the same bounds array as docmask_gqa_doc_bounds (same size:
+ * docmask_gqa_doc_bounds_size(B, S, Skv)), for the *_bounds calls:
+ *   bounds[0][b][t] = lo[b][t],
+ *   bounds[1][b][t] = one past the last p with lo[b][p] <= t, capped at Skv.
+ * Asynchronous on `stream`; lo is not validated (precondition; see
+ * docmask_gqa_check_intervals): other lo arrays give undefined results. */
+int docmask_gqa_interval_bounds(const int32_t* lo, int32_t B, int32_t S,
+                                int32_t Skv, int32_t* bounds,
+                                size_t bounds_bytes, void* stream);
+
 /* The forward and backward with the masking given as a bounds array from
- * docmask_gqa_doc_bounds (same B, S and Skv; its writes ordered before
- * these calls) instead of doc_ids / cu_seqlens; everything else as in
- * docmask_gqa_attn_fwd / docmask_gqa_attn_bwd, with the same workspace
- * sizes.  The bounds are not validated against the sizes beyond alignment:
+ * docmask_gqa_doc_bounds or docmask_gqa_interval_bounds (same B, S and
+ * Skv; its writes ordered before these calls) instead of doc_ids /
+ * cu_seqlens; everything else as in docmask_gqa_attn_fwd /
+ * docmask_gqa_attn_bwd, with the same workspace sizes.  The bounds are not validated against the sizes beyond alignment:
  * a bounds array of other sizes is undefined behaviour. */
 int docmask_gqa_attn_fwd_bounds(const void* q, const void* k, const void* v,
                                 const int32_t* bounds, int32_t B, int32_t S,
@@ -174,6 +192,12 @@ int docmask_gqa_attn_bwd_bounds(const void* q, const void* k, const void* v,
  * or a negative status. */
 int docmask_gqa_check_docs(const int32_t* doc_ids, int32_t B, int32_t S,
                            void* stream);
+
+/* Debug check of the interval precondition: copies lo [B, S] to the host,
+ * synchronising `stream`.  Returns 0 if every row is non-decreasing with
+ * 0 <= lo[p] <= p, 1 otherwise, or a negative status. */
+int docmask_gqa_check_intervals(const int32_t* lo, int32_t B, int32_t S,
+                                void* stream);
 
 /* Debug check of cu_seqlens [n_docs+1] (synchronises `stream`).  Returns 0
  * if cu[0] == 0, cu[n_docs] == S and the offsets strictly increase, 1
