@@ -40,12 +40,14 @@ def local_positions(S: int, cp: int, r: int) -> np.ndarray:
                            np.arange((2 * cp - 1 - r) * c, (2 * cp - r) * c)])
 
 
-def allowed_pairs(lengths, S: int, cp: int, r: int) -> int:
+def allowed_pairs(lengths, S: int, cp: int, r: int, window=None) -> int:
     """Allowed (query, key) pairs of the rank's local rows (per query head):
-    each local position p may attend to its document's keys start(p)..p."""
+    each local position p may attend to its document's keys start(p)..p
+    (with a sliding window: the last `window` of them)."""
     starts = np.repeat(np.concatenate([[0], np.cumsum(lengths)[:-1]]), lengths)
     pos = local_positions(S, cp, r)
-    return int((pos - starts[pos] + 1).sum())
+    lo = starts[pos] if window is None else np.maximum(starts[pos], pos - window + 1)
+    return int((pos - lo + 1).sum())
 
 
 def useful_flops(pairs: int, Hq: int, D: int, backward: bool) -> dict:
@@ -186,8 +188,9 @@ def cpu_baseline(runs, min_s: float = 10.0, max_s: float = 30.0) -> dict:
         r = runs[i % len(runs)]
         c = r["case"]
         t1 = time.perf_counter()
-        oracle.attn_bwd(c.q, c.k, c.v, c.dout, c.doc_ids, c.cfg.cp_size, c.rank, c.scale,
-                        threads=cores, return_fwd=True)
+        oracle.attn_bwd(c.q, c.k, c.v, c.dout, None if c.lo is not None else c.doc_ids,
+                        c.cfg.cp_size, c.rank, c.scale, threads=cores, return_fwd=True,
+                        lo=c.lo)
         last = time.perf_counter() - t1
         flops += r["flops"]["total"]
         done.append(c.seed)
@@ -376,6 +379,8 @@ def main(argv=None) -> int:
         S = cfg.S
         t = dict(q=case.q.to(dev), k=case.k.to(dev), v=case.v.to(dev), dout=case.dout.to(dev),
                  doc=torch.from_numpy(case.doc_ids).to(dev))
+        if case.lo is not None:
+            t["lo"] = torch.from_numpy(case.lo).to(dev)
         t["out"] = torch.empty_like(t["q"])
         t["lse"] = torch.empty(B, Sq, Hq, dtype=torch.float32, device=dev)
         t["dq"] = torch.empty_like(t["q"])
@@ -390,7 +395,7 @@ def main(argv=None) -> int:
                     else M.docmask_gqa_bwd_workspace_size)
         t["wsb"] = torch.empty(max(1, wsb_size(B, S, Skv, Hq, Hkv, D, cfg.cp_size)),
                                dtype=torch.uint8, device=dev)
-        pairs = sum(allowed_pairs(l, S, cfg.cp_size, rank) for l in case.lengths)
+        pairs = sum(allowed_pairs(l, S, cfg.cp_size, rank, cfg.window) for l in case.lengths)
         runs.append(dict(case=case, t=t, pairs=pairs,
                          flops=useful_flops(pairs, Hq, D, cfg.backward),
                          bytes=algorithmic_bytes(case, cfg.backward)))
@@ -400,8 +405,11 @@ def main(argv=None) -> int:
         every step) and the forward."""
         r = runs[i % len(runs)]
         t, case = r["t"], r["case"]
-        M.docmask_gqa_doc_bounds(t["doc"], B=case.cfg.B, S=cfg.S, Skv=case.Skv,
-                                 out=t["bounds"])
+        if "lo" in t:
+            M.docmask_gqa_interval_bounds(t["lo"], Skv=case.Skv, out=t["bounds"])
+        else:
+            M.docmask_gqa_doc_bounds(t["doc"], B=case.cfg.B, S=cfg.S, Skv=case.Skv,
+                                     out=t["bounds"])
         M.docmask_gqa_attn_fwd(t["q"], t["k"], t["v"], cp_size=cfg.cp_size, cp_rank=rank,
                                softmax_scale=case.scale, out=t["out"], lse=t["lse"],
                                workspace=t["wsf"], bounds=t["bounds"])
@@ -583,7 +591,10 @@ def main(argv=None) -> int:
                    "launch": "hip graph per seed" if args.graph else "eager",
                    "backward": "recompute (minimum workspace)" if args.recompute
                                else "dS stash",
-                   "masking": "document bounds from doc_ids once per step, read by the "
+                   "masking": ("sliding window of %d keys inside the documents: interval "
+                               "bounds from the window starts once per step" % cfg.window)
+                              if cfg.window is not None else
+                              "document bounds from doc_ids once per step, read by the "
                               "forward and the backward"},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "per_seed_tflops": [round(x, 2) for x in per_seed],

@@ -424,9 +424,10 @@ int docmask_gqa_interval_bounds(const int32_t* lo, int32_t B, int32_t S, int32_t
   if (!bounds || !aligned(bounds, 4)) return DMGQA_ERR_INVALID_ARG;
   if (bounds_bytes < docmask_gqa_doc_bounds_size(B, S, Skv)) return DMGQA_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  return launch_prep_interval(lo, B, S, Skv, bounds, bounds + (size_t)B * Skv, st) == hipSuccess
-             ? DMGQA_OK
-             : DMGQA_ERR_HIP;
+  timing_begin(kKPrep, st);
+  const hipError_t e = launch_prep_interval(lo, B, S, Skv, bounds, bounds + (size_t)B * Skv, st);
+  timing_end(kKPrep, st);
+  return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
 }
 
 int docmask_gqa_check_intervals(const int32_t* lo, int32_t B, int32_t S, void* stream) {

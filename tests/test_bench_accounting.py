@@ -18,6 +18,21 @@ def test_allowed_pairs_matches_explicit_mask(name, seed):
         assert bench.allowed_pairs(L, cfg.S, cfg.cp_size, r) == want
 
 
+@pytest.mark.parametrize("name,seed,window,cp,r", [("tp405b_swa", 0, 1024, 1, 0),
+                                                  ("tp405b", 2, 37, 1, 0),
+                                                  ("short_docs", 1, 200, 4, 3)])
+def test_windowed_pairs_match_explicit_interval_mask(name, seed, window, cp, r):
+    """The sliding-window count equals the oracle's explicit interval mask
+    (keys max(document start, p - window + 1) .. p) built from the same
+    window starts as the workload's cases."""
+    cfg = W.CONFIGS[name]
+    L = W.doc_lengths(cfg.doc_kind, cfg.S, seed)
+    lo = W.window_starts(L, window)[None]
+    Skv = W.kv_prefix_len(cfg.S, cp, r)
+    want = int(oracle.allowed_counts(None, cp, r, Skv, lo=lo).sum())
+    assert bench.allowed_pairs(L, cfg.S, cp, r, window) == want
+
+
 def test_single_doc_pairs_closed_form():
     S, cp = 32768, 4
     for r in range(cp):

@@ -26,7 +26,7 @@ import numpy as np
 __all__ = [
     "Config", "CONFIGS", "doc_lengths", "doc_ids_from_lengths",
     "cu_seqlens_from_lengths", "full_tensors", "take_local_rows", "Case",
-    "make_case", "chunk_len", "kv_prefix_len",
+    "make_case", "chunk_len", "kv_prefix_len", "window_starts",
 ]
 
 
@@ -44,6 +44,9 @@ class Config:
     backward: bool
     B: int = 1
     description: str = ""
+    # sliding window: query position p attends to keys
+    # max(document start, p - window + 1) .. p (None: the document mask)
+    window: Optional[int] = None
 
 
 # The five workloads (plus the single-document variant of the last one).
@@ -66,6 +69,10 @@ CONFIGS: Dict[str, Config] = {
     "single_doc": Config("single_doc", 32768, 4, (0, 1, 2, 3), 16, 1, 128, "single", 0.5, True,
                          description="same shape as short_docs with one document "
                                      "(pure causal mask)"),
+    "tp405b_swa": Config("tp405b_swa", 8192, 1, (0,), 16, 1, 128, "lognormal1024", 0.5, True,
+                         description="405B TP=8 per-GPU share with a sliding window of 1024 "
+                                     "keys inside the documents (interval mask)",
+                         window=1024),
 }
 
 
@@ -105,6 +112,15 @@ def doc_ids_from_lengths(lengths: List[int]) -> np.ndarray:
     """Per-token document index (int32), documents numbered 0,1,2,... in order."""
     return np.repeat(np.arange(len(lengths), dtype=np.int32),
                      np.asarray(lengths, dtype=np.int64)).astype(np.int32)
+
+
+def window_starts(lengths: List[int], window: int) -> np.ndarray:
+    """Per-position first allowed key of a sliding window of `window` keys
+    inside documents: max(document start, p - window + 1) (int32)."""
+    starts = np.repeat(np.concatenate([[0], np.cumsum(lengths)[:-1]]),
+                       np.asarray(lengths, dtype=np.int64))
+    p = np.arange(int(sum(lengths)))
+    return np.maximum(starts, p - window + 1).astype(np.int32)
 
 
 def cu_seqlens_from_lengths(lengths: List[int]) -> np.ndarray:
@@ -170,6 +186,7 @@ class Case:
     dout: "object"                # bf16 [B, Sq, Hq, D]
     Skv: int
     scale: float = field(default=0.0)
+    lo: Optional[np.ndarray] = None  # int32 [B, S] window starts (windowed configs)
 
     @property
     def Sq(self) -> int:
@@ -190,6 +207,8 @@ def make_case(cfg: Config, seed: int, rank: int, Skv: Optional[int] = None,
         Skv = kv_prefix_len(cfg.S, cfg.cp_size, rank)
     ql = take_local_rows(q, cfg.S, cfg.cp_size, rank)
     dl = take_local_rows(dout, cfg.S, cfg.cp_size, rank)
+    lo = (np.stack([window_starts(l, cfg.window) for l in lengths])
+          if cfg.window is not None else None)
     return Case(cfg, seed, rank, lengths, doc_ids, cu, ql,
                 k[:, :Skv].contiguous(), v[:, :Skv].contiguous(), dl, Skv,
-                scale=1.0 / math.sqrt(cfg.D))
+                scale=1.0 / math.sqrt(cfg.D), lo=lo)
