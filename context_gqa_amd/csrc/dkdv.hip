@@ -216,7 +216,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const int r_begin = split * rps;
     const int r_end = min(r_begin + rps, rows_total);
     const int nsb = r_end > r_begin ? (r_end - r_begin + 31) / 32 : 0;
-    const int nblk = (nsb + 1) / 2;
 
     // this lane's key and its K / V operands (B of S = Q K^T, dP = dO V^T:
     // lane l holds key j, elements 32ks + 8*g4 .. +7)

@@ -44,8 +44,7 @@ void timing_begin(int kernel, hipStream_t st) {
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_on) return;
   hipEvent_t e = take_event();
-  if (!e) return;
-  hipEventRecord(e, st);
+  if (!e || hipEventRecord(e, st) != hipSuccess) return;  // untimed, not an error
   g_recs.push_back({kernel, e, nullptr});
   g_open[kernel] = (int)g_recs.size() - 1;
 }
@@ -54,8 +53,7 @@ void timing_end(int kernel, hipStream_t st) {
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_on || g_open[kernel] < 0) return;
   hipEvent_t e = take_event();
-  if (!e) return;
-  hipEventRecord(e, st);
+  if (!e || hipEventRecord(e, st) != hipSuccess) return;
   g_recs[g_open[kernel]].stop = e;
   g_open[kernel] = -1;
 }
