@@ -91,6 +91,10 @@ def sample_clocks(delay_s: float = 0.5):
     dict, or None with the reason when rocm-smi is unavailable)."""
     import re
     import subprocess
+    if "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        # under a profiler every new process loads its library, and the
+        # rocm-smi launcher would replace itself with python after that
+        return {"error": "skipped under a profiler"}
     time.sleep(delay_s)
     try:
         out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
@@ -103,6 +107,8 @@ def sample_clocks(delay_s: float = 0.5):
         if m:
             res[key + "_mhz"] = int(m.group(1))
     return res or {"error": "no clock lines in rocm-smi output"}
+
+
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
