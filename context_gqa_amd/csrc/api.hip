@@ -66,8 +66,8 @@ int check_docs_args(const int32_t* doc_ids, const int32_t* cu, int n_docs, const
 
 // Workspace layout.
 struct Layout {
-  size_t dstart, dend, agg, rowstat, hdr, tile_info, items, tile_rows, partial, stash, total_min,
-      total;
+  size_t dstart, dend, agg, order, rowstat, hdr, tile_info, items, tile_rows, partial, stash,
+      total_min, total;
   int nkt, max_split_base;
   int stash_kvh_blocks;   // stash blocks reserved per KV head
 };
@@ -100,6 +100,9 @@ Layout layout(const Shape& s, bool backward) {
   L.dstart = off; off = align_up(off + pos);
   L.dend = off; off = align_up(off + pos);
   L.agg = off; off = align_up(off + 2 * (size_t)s.B * nblk * sizeof(int32_t));
+  // dispatch order of the query tiles (forward, or dQ from the stash)
+  const size_t nt = ((size_t)s.Sq * s.G + kFwdBM - 1) / kFwdBM;
+  L.order = off; off = align_up(off + (size_t)s.B * nt * sizeof(int32_t));
   if (backward) {
     L.nkt = (s.Skv + kDkdvBN - 1) / kDkdvBN;
     L.max_split_base = kMaxSplitTotal / s.Hkv > 1 ? kMaxSplitTotal / s.Hkv : 1;
@@ -206,10 +209,14 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* doc_ids
   rc = call_bounds(doc_ids, cu_seqlens, n_docs, bounds, s, ws, L, st, &dstart, &dend);
   if (rc != DMGQA_OK) return rc;
   const Geo g = make_geo(s, softmax_scale);
+  int32_t* order = reinterpret_cast<int32_t*>(ws + L.order);
+  timing_begin(kKOrder, st);
+  hipError_t e = launch_tile_order_fwd(dstart, g, order, st);
+  timing_end(kKOrder, st);
+  if (e != hipSuccess) return DMGQA_ERR_HIP;
   timing_begin(kKFwd, st);
-  hipError_t e = launch_fwd(D, static_cast<const u16*>(q), static_cast<const u16*>(k),
-                            static_cast<const u16*>(v), dstart, static_cast<u16*>(out), lse, g,
-                            st);
+  e = launch_fwd(D, static_cast<const u16*>(q), static_cast<const u16*>(k),
+                 static_cast<const u16*>(v), dstart, order, static_cast<u16*>(out), lse, g, st);
   timing_end(kKFwd, st);
   return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
 }
@@ -314,6 +321,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   int4* tile_rows = reinterpret_cast<int4*>(ws + L.tile_rows);
   float* partial = reinterpret_cast<float*>(ws + L.partial);
   u16* stash = use_stash ? reinterpret_cast<u16*>(ws + L.stash) : nullptr;
+  int32_t* dq_order = reinterpret_cast<int32_t*>(ws + L.order);
   const u16* qh = static_cast<const u16*>(q);
   const u16* kh = static_cast<const u16*>(k);
   const u16* vh = static_cast<const u16*>(v);
@@ -323,8 +331,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   hipError_t e;
   if (use_stash) {
     timing_begin(kKSchedRowstat, st);
-    e = launch_sched_rowstat(D, dend, g, L.nkt, L.max_split_base, hdr, tile_info, items,
-                             tile_rows, oh, doh, lse, Lbuf, Nbuf, st);
+    e = launch_sched_rowstat(D, dstart, dend, g, L.nkt, L.max_split_base, hdr, tile_info, items,
+                             tile_rows, dq_order, oh, doh, lse, Lbuf, Nbuf, st);
     timing_end(kKSchedRowstat, st);
     if (e != hipSuccess) return DMGQA_ERR_HIP;
     timing_begin(kKDkdv, st);
@@ -333,7 +341,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
     timing_end(kKDkdv, st);
     if (e != hipSuccess) return DMGQA_ERR_HIP;
     timing_begin(kKDq, st);
-    e = launch_bwd_dq_stash(D, kh, dstart, tile_rows, stash, L.stash_kvh_blocks,
+    e = launch_bwd_dq_stash(D, kh, dstart, tile_rows, stash, L.stash_kvh_blocks, dq_order,
                             static_cast<u16*>(dq), tile_info, partial, dk, dv, g, L.nkt, st);
     timing_end(kKDq, st);
     return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;

@@ -75,7 +75,7 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
     const u16* __restrict__ k, const int32_t* __restrict__ dstart,
     const int4* __restrict__ tile_rows, const u16* __restrict__ stash, int stash_kvh_blocks,
-    u16* __restrict__ dq, const int2* __restrict__ tile_info, const float* __restrict__ partial,
+    const int32_t* __restrict__ order, u16* __restrict__ dq, const int2* __restrict__ tile_info, const float* __restrict__ partial,
     float* __restrict__ dk, float* __restrict__ dv, Geo g, int nkt, int dq_grid) {
   if ((int)blockIdx.x >= dq_grid) {
     reduce_partials<D>(tile_info, partial, dk, dv, g, nkt, (int)blockIdx.x - dq_grid);
@@ -91,10 +91,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
 
   const int nrows = g.Sq * g.G;
   const int nqb = (nrows + 127) / 128;
-  const int nbg = g.B * g.Hkv;
-  const int qb = nqb - 1 - (int)(blockIdx.x / nbg);     // heavy (late) row blocks first
-  const int bg = blockIdx.x % nbg;
-  const int b = bg / g.Hkv, kvh = bg % g.Hkv;
+  // (batch row, row block) items in the heaviest-first order, the KV heads
+  // of an item consecutively (clamped: the order is a permutation)
+  const int item = min(max(order[blockIdx.x / g.Hkv], 0), g.B * nqb - 1);
+  const int b = item / nqb, qb = item - b * nqb;
+  const int kvh = blockIdx.x % g.Hkv;
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int h = lane >> 5, i = lane & 31;
   const int J = 4 * qb + wave;                 // this wave's 32-row block
@@ -256,18 +257,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
 }
 
 hipError_t launch_bwd_dq_stash(int D, const u16* k, const int32_t* dstart, const int4* tile_rows,
-                               const u16* stash, int stash_kvh_blocks, u16* dq,
-                               const int2* tile_info, const float* partial, float* dk, float* dv,
-                               const Geo& g, int nkt, hipStream_t st) {
+                               const u16* stash, int stash_kvh_blocks, const int32_t* order,
+                               u16* dq, const int2* tile_info, const float* partial, float* dk,
+                               float* dv, const Geo& g, int nkt, hipStream_t st) {
   const int nqb = (g.Sq * g.G + 127) / 128;
   const unsigned grid = (unsigned)nqb * g.B * g.Hkv;
   if (D == 128)
     bwd_dq_stash_kernel<128><<<grid + reduce_grid<128>(g, nkt), 256, 0, st>>>(
-        k, dstart, tile_rows, stash, stash_kvh_blocks, dq, tile_info, partial, dk, dv, g, nkt,
+        k, dstart, tile_rows, stash, stash_kvh_blocks, order, dq, tile_info, partial, dk, dv, g,
+        nkt,
         (int)grid);
   else
     bwd_dq_stash_kernel<64><<<grid + reduce_grid<64>(g, nkt), 256, 0, st>>>(
-        k, dstart, tile_rows, stash, stash_kvh_blocks, dq, tile_info, partial, dk, dv, g, nkt,
+        k, dstart, tile_rows, stash, stash_kvh_blocks, order, dq, tile_info, partial, dk, dv, g,
+        nkt,
         (int)grid);
   return hipGetLastError();
 }

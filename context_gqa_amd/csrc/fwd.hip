@@ -87,6 +87,7 @@ __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict
                                                           const u16* __restrict__ k,
                                                           const u16* __restrict__ v,
                                                           const int32_t* __restrict__ dstart,
+                                                          const int32_t* __restrict__ order,
                                                           u16* __restrict__ out,
                                                           float* __restrict__ lse, Geo g) {
   constexpr int BM = kRows, BN = kFwdBN, KK = D / 16, DB = D / 32;
@@ -99,11 +100,11 @@ __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict
 
   const int nrows = g.Sq * g.G;
   const int nt = (nrows + BM - 1) / BM;
-  const int nbg = g.B * g.Hkv;
-  // heaviest tiles (latest positions) are dispatched first
-  const int tile = nt - 1 - (int)(blockIdx.x / nbg);
-  const int bg = blockIdx.x % nbg;
-  const int b = bg / g.Hkv, kvh = bg % g.Hkv;
+  // (batch row, tile) items in the heaviest-first order, the KV heads of an
+  // item consecutively (clamped: the order is a permutation of 0 .. B*nt-1)
+  const int item = min(max(order[blockIdx.x / g.Hkv], 0), g.B * nt - 1);
+  const int b = item / nt, tile = item - b * nt;
+  const int kvh = blockIdx.x % g.Hkv;
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int h = lane >> 5, i = lane & 31;
 
@@ -295,13 +296,13 @@ __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict
 }
 
 hipError_t launch_fwd(int D, const u16* q, const u16* k, const u16* v, const int32_t* dstart,
-                      u16* out, float* lse, const Geo& g, hipStream_t st) {
+                      const int32_t* order, u16* out, float* lse, const Geo& g, hipStream_t st) {
   const int nt = (g.Sq * g.G + kRows - 1) / kRows;
   const unsigned grid = (unsigned)nt * g.B * g.Hkv;
   if (D == 128)
-    fwd_kernel<128><<<grid, kWaves * 64, 0, st>>>(q, k, v, dstart, out, lse, g);
+    fwd_kernel<128><<<grid, kWaves * 64, 0, st>>>(q, k, v, dstart, order, out, lse, g);
   else
-    fwd_kernel<64><<<grid, kWaves * 64, 0, st>>>(q, k, v, dstart, out, lse, g);
+    fwd_kernel<64><<<grid, kWaves * 64, 0, st>>>(q, k, v, dstart, order, out, lse, g);
   return hipGetLastError();
 }
 

@@ -50,7 +50,7 @@ hipError_t launch_sched_dkdv(const int32_t* dend, const Geo& g, int nkt, int max
                              SchedHeader* hdr, int2* tile_info, int2* items, int4* tile_rows,
                              hipStream_t st);
 hipError_t launch_fwd(int D, const u16* q, const u16* k, const u16* v, const int32_t* dstart,
-                      u16* out, float* lse, const Geo& g, hipStream_t st);
+                      const int32_t* order, u16* out, float* lse, const Geo& g, hipStream_t st);
 hipError_t launch_bwd_dq(int D, const u16* q, const u16* k, const u16* v, const u16* out,
                          const u16* dout, const float* lse, const int32_t* dstart, u16* dq,
                          float* Lbuf, float* Nbuf, const Geo& g, hipStream_t st);
@@ -61,14 +61,19 @@ hipError_t launch_bwd_dkdv(int D, const u16* q, const u16* k, const u16* v, cons
                            float* partial, float* dk, float* dv, const Geo& g, int nkt,
                            hipStream_t st);
 // Schedule (one block) and per-row statistics (stash path) in one launch.
-hipError_t launch_sched_rowstat(int D, const int32_t* dend, const Geo& g, int nkt,
-                                int max_split_base, SchedHeader* hdr, int2* tile_info,
-                                int2* items, int4* tile_rows, const u16* out, const u16* dout,
-                                const float* lse, float* Lbuf, float* Nbuf, hipStream_t st);
+hipError_t launch_sched_rowstat(int D, const int32_t* dstart, const int32_t* dend, const Geo& g,
+                                int nkt, int max_split_base, SchedHeader* hdr, int2* tile_info,
+                                int2* items, int4* tile_rows, int32_t* dq_order, const u16* out,
+                                const u16* dout, const float* lse, float* Lbuf, float* Nbuf,
+                                hipStream_t st);
+// Heaviest-first dispatch order of the forward's query tiles (one block):
+// order[i] = b * nt + tile for B * nt items, nt = ceil(Sq * G / kFwdBM).
+hipError_t launch_tile_order_fwd(const int32_t* dstart, const Geo& g, int32_t* order,
+                                 hipStream_t st);
 // dQ from the dS stash, and (in workgroups appended to its grid) the sum of
 // the partial dK/dV slots.
 hipError_t launch_bwd_dq_stash(int D, const u16* k, const int32_t* dstart, const int4* tile_rows,
-                               const u16* stash, int stash_kvh_blocks, u16* dq,
+                               const u16* stash, int stash_kvh_blocks, const int32_t* order, u16* dq,
                                const int2* tile_info, const float* partial, float* dk, float* dv,
                                const Geo& g, int nkt, hipStream_t st);
 hipError_t launch_bwd_reduce(int D, const int2* tile_info, const float* partial, float* dk,
@@ -76,7 +81,9 @@ hipError_t launch_bwd_reduce(int D, const int2* tile_info, const float* partial,
 
 // Kernel timing (benchmark use): when enabled, each launch below is
 // bracketed by HIP events recorded on the launch stream.
-enum KernelId { kKPrep = 0, kKFwd, kKSched, kKDq, kKDkdv, kKReduce, kKSchedRowstat, kNumKernels };
+enum KernelId {
+  kKPrep = 0, kKFwd, kKSched, kKDq, kKDkdv, kKReduce, kKSchedRowstat, kKOrder, kNumKernels
+};
 void timing_begin(int kernel, hipStream_t st);
 void timing_end(int kernel, hipStream_t st);
 

@@ -10,6 +10,7 @@
 // attention kernels read these arrays instead of comparing document ids.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "qtile.hpp"
 
 namespace dmgqa {
 
@@ -355,19 +356,116 @@ __device__ void rowstat_rows(const u16* __restrict__ out, const u16* __restrict_
   }
 }
 
-// The schedule (block 0) and the row statistics (the other blocks) in one
-// launch: the single-block schedule then runs beside the row statistics.
+// Inclusive block-wide scan with + of `v`.
+__device__ int block_scan_add(int v, int* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) sh[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < (kScanThreads / 64) ? sh[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      int u = __shfl_up(w, o);
+      if (lane >= o) w += u;
+    }
+    if (lane < kScanThreads / 64) sh[16 + lane] = w;
+  }
+  __syncthreads();
+  if (wave > 0) v += sh[16 + wave - 1];
+  __syncthreads();
+  return v;
+}
+
+// Dispatch order of the query tiles of the forward (BN = kFwdBN) or dQ
+// (BN = kDkdvBN) kernel: the B * nt items (batch row, tile) sorted by
+// decreasing cost, the number of BN-key tiles the tile's rows reach
+// (heaviest first, the longest-processing-time rule, so that the long tiles
+// of long documents do not start last).  A counting sort over kOrderBins
+// cost classes (costs beyond the last class share it); items of one class
+// keep no particular order.  Only which workgroup computes a tile changes,
+// never its result.  One block of kScanThreads threads.
+constexpr int kOrderBins = 4096;
+static_assert(kOrderBins % kScanThreads == 0, "bins per thread");
+
+template <int BN>
+__device__ void tile_order_body(const int32_t* __restrict__ dstart, const Geo& g,
+                                int32_t* __restrict__ order) {
+  __shared__ int cnt[kOrderBins];
+  __shared__ int sh[32];
+  constexpr int BM = kFwdBM;
+  const int nt = (g.Sq * g.G + BM - 1) / BM;
+  const int n = g.B * nt;
+  for (int i = threadIdx.x; i < kOrderBins; i += kScanThreads) cnt[i] = 0;
+  __syncthreads();
+  // class 0 holds the heaviest items
+  auto cls = [&](int x) {
+    const int b = x / nt, t = x - b * nt;
+    const QTileKeys kr = qtile_keys<BM, BN>(t * BM, dstart + (size_t)b * g.Skv, g);
+    return kOrderBins - 1 - min(kr.na + kr.nb, kOrderBins - 1);
+  };
+  // the classes of the first kKeep items of each thread stay in registers
+  constexpr int kKeep = 4;
+  int keep[kKeep];
+#pragma unroll
+  for (int e = 0; e < kKeep; ++e) {
+    const int x = threadIdx.x + e * kScanThreads;
+    keep[e] = x < n ? cls(x) : 0;
+  }
+#pragma unroll
+  for (int e = 0; e < kKeep; ++e)
+    if (threadIdx.x + e * kScanThreads < n) atomicAdd(&cnt[keep[e]], 1);
+  for (int x = threadIdx.x + kKeep * kScanThreads; x < n; x += kScanThreads)
+    atomicAdd(&cnt[cls(x)], 1);
+  __syncthreads();
+  // exclusive prefix sum over the classes (thread i owns classes per*i ..)
+  constexpr int per = kOrderBins / kScanThreads;
+  int loc[per];
+  int tot = 0;
+#pragma unroll
+  for (int e = 0; e < per; ++e) {
+    loc[e] = tot;
+    tot += cnt[per * threadIdx.x + e];
+  }
+  const int base = block_scan_add(tot, sh) - tot;
+#pragma unroll
+  for (int e = 0; e < per; ++e) cnt[per * threadIdx.x + e] = base + loc[e];
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kKeep; ++e) {
+    const int x = threadIdx.x + e * kScanThreads;
+    if (x < n) order[atomicAdd(&cnt[keep[e]], 1)] = x;
+  }
+  for (int x = threadIdx.x + kKeep * kScanThreads; x < n; x += kScanThreads)
+    order[atomicAdd(&cnt[cls(x)], 1)] = x;
+}
+
+__global__ __launch_bounds__(kScanThreads) void tile_order_fwd(const int32_t* __restrict__ dstart,
+                                                               Geo g, int32_t* __restrict__ order) {
+  tile_order_body<kFwdBN>(dstart, g, order);
+}
+
+// The dK/dV schedule (block 0), the dQ tile order (block 1) and the row
+// statistics (the other blocks) in one launch: the single-block parts then
+// run beside the row statistics.
 template <int D>
 __global__ __launch_bounds__(kScanThreads) void sched_rowstat(
-    const int32_t* __restrict__ dend, Geo g, int nkt, int max_split_base,
-    SchedHeader* __restrict__ hdr, int2* __restrict__ tile_info, int2* __restrict__ items,
-    int4* __restrict__ tile_rows, const u16* __restrict__ out, const u16* __restrict__ dout,
-    const float* __restrict__ lse, float* __restrict__ Lbuf, float* __restrict__ Nbuf) {
+    const int32_t* __restrict__ dstart, const int32_t* __restrict__ dend, Geo g, int nkt,
+    int max_split_base, SchedHeader* __restrict__ hdr, int2* __restrict__ tile_info,
+    int2* __restrict__ items, int4* __restrict__ tile_rows, int32_t* __restrict__ dq_order,
+    const u16* __restrict__ out, const u16* __restrict__ dout, const float* __restrict__ lse,
+    float* __restrict__ Lbuf, float* __restrict__ Nbuf) {
   if (blockIdx.x == 0)
     sched_body(dend, g, nkt, max_split_base, hdr, tile_info, items, tile_rows);
+  else if (blockIdx.x == 1)
+    tile_order_body<kDkdvBN>(dstart, g, dq_order);
   else
     rowstat_rows<D>(out, dout, lse, Lbuf, Nbuf, g.B * g.Sq * g.Hq, 1.f / g.scale,
-                    (int)blockIdx.x - 1);
+                    (int)blockIdx.x - 2);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -404,21 +502,28 @@ hipError_t launch_sched_dkdv(const int32_t* dend, const Geo& g, int nkt, int max
   return hipGetLastError();
 }
 
-hipError_t launch_sched_rowstat(int D, const int32_t* dend, const Geo& g, int nkt,
-                                int max_split_base, SchedHeader* hdr, int2* tile_info,
-                                int2* items, int4* tile_rows, const u16* out, const u16* dout,
-                                const float* lse, float* Lbuf, float* Nbuf, hipStream_t st) {
+hipError_t launch_sched_rowstat(int D, const int32_t* dstart, const int32_t* dend, const Geo& g,
+                                int nkt, int max_split_base, SchedHeader* hdr, int2* tile_info,
+                                int2* items, int4* tile_rows, int32_t* dq_order, const u16* out,
+                                const u16* dout, const float* lse, float* Lbuf, float* Nbuf,
+                                hipStream_t st) {
   const int nrows = g.B * g.Sq * g.Hq;
   const int rows_per_block = kScanThreads / (D / 8);
-  const unsigned grid = 1u + (unsigned)((nrows + rows_per_block - 1) / rows_per_block);
+  const unsigned grid = 2u + (unsigned)((nrows + rows_per_block - 1) / rows_per_block);
   if (D == 128)
-    sched_rowstat<128><<<grid, kScanThreads, 0, st>>>(dend, g, nkt, max_split_base, hdr,
-                                                      tile_info, items, tile_rows, out, dout,
-                                                      lse, Lbuf, Nbuf);
+    sched_rowstat<128><<<grid, kScanThreads, 0, st>>>(dstart, dend, g, nkt, max_split_base, hdr,
+                                                      tile_info, items, tile_rows, dq_order, out,
+                                                      dout, lse, Lbuf, Nbuf);
   else
-    sched_rowstat<64><<<grid, kScanThreads, 0, st>>>(dend, g, nkt, max_split_base, hdr,
-                                                     tile_info, items, tile_rows, out, dout,
-                                                     lse, Lbuf, Nbuf);
+    sched_rowstat<64><<<grid, kScanThreads, 0, st>>>(dstart, dend, g, nkt, max_split_base, hdr,
+                                                     tile_info, items, tile_rows, dq_order, out,
+                                                     dout, lse, Lbuf, Nbuf);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_order_fwd(const int32_t* dstart, const Geo& g, int32_t* order,
+                                 hipStream_t st) {
+  tile_order_fwd<<<1, kScanThreads, 0, st>>>(dstart, g, order);
   return hipGetLastError();
 }
 
