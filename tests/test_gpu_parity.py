@@ -278,12 +278,14 @@ def test_cp_split_equals_unsplit_on_gpu():
 
 @pytest.mark.parametrize("name,seed,rank,use_cu", [("tiny", 0, 0, False), ("tiny", 1, 0, True),
                                                    ("short_docs", 0, 2, False),
+                                                   ("short_docs", 1, 0, False),
                                                    ("tp405b", 1, 0, True),
                                                    ("long_cp", 0, 7, False)])
 def test_bounds_path_matches_doc_path(name, seed, rank, use_cu):
     """docmask_gqa_doc_bounds equals the host's document starts / ends
     (bit-exact, ends capped at Skv), and the *_bounds calls reproduce the
-    doc_ids calls bit for bit (same kernels, same bounds)."""
+    doc_ids calls bit for bit (same kernels, same bounds).  Skv from 512 to
+    131072 keys (short_docs rank 0: 32768, a multiple of the scan block)."""
     cfg = W.CONFIGS[name]
     case = W.make_case(cfg, seed, rank)
     say(f"[bounds {name} seed {seed} rank {rank} cu={use_cu}]")
