@@ -28,6 +28,14 @@ What it computes, and where the pages state it:
   allowed for query position p iff lo[p] <= t <= p (lo given per position;
   the document mask is lo = first position of p's document).  Every
   function below takes either doc_ids or lo.
+* Non-causal intervals -- the same page, section on pipeline parallelism
+  for multimodal training (Figure 5 and its second challenge): the
+  cross-attention layers take image sequences of 1.2K-3K tokens next to text
+  of under 200 tokens.  Reading used here (the page gives no mask): text
+  query p attends to every image token of its own sample, i.e. an interval
+  with an exclusive end not tied to the position, lo[p] <= t < hi[p], over
+  keys indexed independently of the queries.  Every function below that
+  takes lo also takes hi; without hi the end is p (inclusive).
 * GQA -- Herd section 3.3.2 and "Paper notes", "Two architectural choices":
   groups of query heads share one key/value head.  Reading used here:
   contiguous groups, query head h uses KV head h // (Hq // Hkv).
@@ -96,29 +104,42 @@ def allowed_mask(doc: np.ndarray, pos: np.ndarray, Skv: int) -> np.ndarray:
     return causal & same_doc
 
 
-def interval_mask(lo: np.ndarray, pos: np.ndarray, Skv: int) -> np.ndarray:
+def interval_mask(lo: np.ndarray, pos: np.ndarray, Skv: int,
+                  hi: Optional[np.ndarray] = None) -> np.ndarray:
     """Explicit boolean mask M[i, t] for query positions `pos` over keys
-    t in [0, Skv): lo[p] <= t <= p."""
+    t in [0, Skv): lo[p] <= t <= p, or with `hi` (exclusive ends, not tied
+    to the position) lo[p] <= t < hi[p]."""
     t = np.arange(Skv, dtype=np.int64)
-    return (t[None, :] >= np.asarray(lo)[pos][:, None]) & (t[None, :] <= pos[:, None])
+    end = pos + 1 if hi is None else np.asarray(hi)[pos]
+    return (t[None, :] >= np.asarray(lo)[pos][:, None]) & (t[None, :] < end[:, None])
 
 
-def _masks(doc_ids, lo):
+def _masks(doc_ids, lo, hi=None):
     """The mask source: (array [B, S], fn(b, positions, Skv) -> explicit mask)."""
     if (doc_ids is None) == (lo is None):
         raise ValueError("pass exactly one of doc_ids / lo")
+    if hi is not None and lo is None:
+        raise ValueError("hi needs lo")
     if lo is not None:
         arr = np.asarray(lo)
-        return arr, lambda b, p, Skv: interval_mask(arr[b], p, Skv)
+        if hi is None:
+            return arr, lambda b, p, Skv: interval_mask(arr[b], p, Skv)
+        harr = np.asarray(hi)
+        if harr.shape != arr.shape:
+            raise ValueError("lo and hi must have the same shape")
+        if np.any(harr <= arr):
+            raise ValueError("every query needs at least one key (lo < hi)")
+        return arr, lambda b, p, Skv: interval_mask(arr[b], p, Skv, harr[b])
     arr = np.asarray(doc_ids)
     return arr, lambda b, p, Skv: allowed_mask(arr[b], p, Skv)
 
 
 def allowed_counts(doc_ids: Optional[np.ndarray], cp_size: int, cp_rank: int, Skv: int,
-                   block: int = 256, lo: Optional[np.ndarray] = None) -> np.ndarray:
+                   block: int = 256, lo: Optional[np.ndarray] = None,
+                   hi: Optional[np.ndarray] = None) -> np.ndarray:
     """Number of allowed keys of every local row, counted from the explicit
-    mask.  doc_ids (or lo): [B, S].  Returns int64 [B, Sq]."""
-    arr, mask = _masks(doc_ids, lo)
+    mask.  doc_ids (or lo, and optionally hi): [B, S].  Returns int64 [B, Sq]."""
+    arr, mask = _masks(doc_ids, lo, hi)
     B, S = arr.shape
     pos = chunk_positions(S, cp_size, cp_rank)
     out = np.zeros((B, pos.size), dtype=np.int64)
@@ -203,7 +224,7 @@ def _run(tasks, fn, threads: int):
         return list(ex.map(fn, tasks))
 
 
-def _check(q, k, doc_ids, cp_size, cp_rank):
+def _check(q, k, doc_ids, cp_size, cp_rank, hi=None):
     B, Sq, Hq, D = q.shape
     Bk, Skv, Hkv, Dk = k.shape
     S = doc_ids.shape[1]
@@ -214,17 +235,20 @@ def _check(q, k, doc_ids, cp_size, cp_rank):
     pos = chunk_positions(S, cp_size, cp_rank)
     if pos.size != Sq:
         raise ValueError("q must hold 2*S/(2*cp_size) local rows")
-    if Skv > S or Skv <= int(pos.max()):
-        raise ValueError("K/V must cover every position a local row can reach")
+    if hi is None:
+        if Skv > S or Skv <= int(pos.max()):
+            raise ValueError("K/V must cover every position a local row can reach")
+    elif int(np.max(np.asarray(hi)[:, pos])) > Skv:
+        raise ValueError("K/V must cover every key a local row can reach")
     return B, Sq, Hq, D, Skv, Hkv, Hq // Hkv, pos
 
 
 def attn_probs(q, k, doc_ids, cp_size: int, cp_rank: int, softmax_scale: float,
-               lo=None):
+               lo=None, hi=None):
     """Explicit probability matrix P [B, Sq, Hq, Skv] (small cases only)."""
     q = to_f64(q); k = to_f64(k)
-    arr, mask = _masks(doc_ids, lo)
-    B, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, arr, cp_size, cp_rank)
+    arr, mask = _masks(doc_ids, lo, hi)
+    B, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, arr, cp_size, cp_rank, hi)
     P = np.zeros((B, Sq, Hq, Skv))
     for b in range(B):
         M = mask(b, pos, Skv)
@@ -236,13 +260,13 @@ def attn_probs(q, k, doc_ids, cp_size: int, cp_rank: int, softmax_scale: float,
 
 
 def attn_fwd(q, k, v, doc_ids, cp_size: int, cp_rank: int, softmax_scale: float,
-             window: bool = True, threads: Optional[int] = None, lo=None):
+             window: bool = True, threads: Optional[int] = None, lo=None, hi=None):
     """Forward.  q [B,Sq,Hq,D] (local rows), k/v [B,Skv,Hkv,D] (gathered,
     global order), doc_ids [B,S] (or lo [B,S]).  Returns out [B,Sq,Hq,D],
     lse [B,Sq,Hq]."""
     q = to_f64(q); k = to_f64(k); v = to_f64(v)
-    arr, mask = _masks(doc_ids, lo)
-    B, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, arr, cp_size, cp_rank)
+    arr, mask = _masks(doc_ids, lo, hi)
+    B, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, arr, cp_size, cp_rank, hi)
     out = np.zeros((B, Sq, Hq, D))
     lse = np.zeros((B, Sq, Hq))
     nb = _blocks(Sq, G, Skv if not window else min(Skv, 16384))
@@ -268,13 +292,13 @@ def attn_fwd(q, k, v, doc_ids, cp_size: int, cp_rank: int, softmax_scale: float,
 
 def attn_bwd(q, k, v, dout, doc_ids, cp_size: int, cp_rank: int,
              softmax_scale: float, window: bool = True,
-             threads: Optional[int] = None, return_fwd: bool = False, lo=None):
+             threads: Optional[int] = None, return_fwd: bool = False, lo=None, hi=None):
     """Backward.  Recomputes P and the oracle's own fp64 output, then applies
     the chain rule.  Returns dq [B,Sq,Hq,D], dk/dv [B,Skv,Hkv,D] (rows that no
     local query reaches are exactly 0); with return_fwd also out and lse."""
     q = to_f64(q); k = to_f64(k); v = to_f64(v); dout = to_f64(dout)
-    arr, mask = _masks(doc_ids, lo)
-    B, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, arr, cp_size, cp_rank)
+    arr, mask = _masks(doc_ids, lo, hi)
+    B, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, arr, cp_size, cp_rank, hi)
     dq = np.zeros((B, Sq, Hq, D))
     dk = np.zeros((B, Skv, Hkv, D))
     dv = np.zeros((B, Skv, Hkv, D))
@@ -331,13 +355,14 @@ def _row_stats(q, k, v, mask_b, pos_rows, scale, G, g):
 
 
 def attn_fwd_rows(q, k, v, doc_ids, cp_size: int, cp_rank: int,
-                  softmax_scale: float, b: int, rows: Sequence[int], lo=None):
+                  softmax_scale: float, b: int, rows: Sequence[int], lo=None, hi=None):
     """out [n, Hq, D] and lse [n, Hq] of selected local rows of batch b.
     Each row is computed on its own, exactly as in attn_fwd."""
     q = to_f64(q[b:b + 1]); k = to_f64(k[b:b + 1]); v = to_f64(v[b:b + 1])
+    hi = None if hi is None else np.asarray(hi)[b:b + 1]
     arr, mask = _masks(None if doc_ids is None else np.asarray(doc_ids)[b:b + 1],
-                       None if lo is None else np.asarray(lo)[b:b + 1])
-    _, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, arr, cp_size, cp_rank)
+                       None if lo is None else np.asarray(lo)[b:b + 1], hi)
+    _, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, arr, cp_size, cp_rank, hi)
     rows = np.asarray(rows, dtype=np.int64)
     out = np.zeros((rows.size, Hq, D)); lse = np.zeros((rows.size, Hq))
     for g in range(Hkv):
@@ -351,14 +376,15 @@ def attn_fwd_rows(q, k, v, doc_ids, cp_size: int, cp_rank: int,
 
 
 def attn_bwd_rows(q, k, v, dout, doc_ids, cp_size: int, cp_rank: int,
-                  softmax_scale: float, b: int, rows: Sequence[int], lo=None):
+                  softmax_scale: float, b: int, rows: Sequence[int], lo=None, hi=None):
     """dq [n, Hq, D] of selected local rows of batch b (each row's dq needs
     only that row's own probabilities and output)."""
     q = to_f64(q[b:b + 1]); k = to_f64(k[b:b + 1]); v = to_f64(v[b:b + 1])
     dout = to_f64(dout[b:b + 1])
+    hi = None if hi is None else np.asarray(hi)[b:b + 1]
     arr, mask = _masks(None if doc_ids is None else np.asarray(doc_ids)[b:b + 1],
-                       None if lo is None else np.asarray(lo)[b:b + 1])
-    _, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, arr, cp_size, cp_rank)
+                       None if lo is None else np.asarray(lo)[b:b + 1], hi)
+    _, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, arr, cp_size, cp_rank, hi)
     rows = np.asarray(rows, dtype=np.int64)
     dq = np.zeros((rows.size, Hq, D))
     for g in range(Hkv):
@@ -376,7 +402,7 @@ def attn_bwd_rows(q, k, v, dout, doc_ids, cp_size: int, cp_rank: int,
 
 def attn_bwd_kv_rows(q, k, v, dout, doc_ids, cp_size: int, cp_rank: int,
                      softmax_scale: float, b: int, kv_rows: Sequence[int],
-                     max_query_rows: Optional[int] = None, lo=None):
+                     max_query_rows: Optional[int] = None, lo=None, hi=None):
     """dk, dv [n, Hkv, D] at selected key positions of batch b.  Every local
     row that reaches one of those keys gets its full forward (lse and output)
     computed first, as attn_bwd does; then the keys' columns of dS and P are
@@ -385,8 +411,9 @@ def attn_bwd_kv_rows(q, k, v, dout, doc_ids, cp_size: int, cp_rank: int,
     dout = to_f64(dout[b:b + 1])
     doc_b = None if doc_ids is None else np.asarray(doc_ids)[b:b + 1]
     lo_b = None if lo is None else np.asarray(lo)[b:b + 1]
-    arr, mask = _masks(doc_b, lo_b)
-    _, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, arr, cp_size, cp_rank)
+    hi_b = None if hi is None else np.asarray(hi)[b:b + 1]
+    arr, mask = _masks(doc_b, lo_b, hi_b)
+    _, Sq, Hq, D, Skv, Hkv, G, pos = _check(q, k, arr, cp_size, cp_rank, hi_b)
     kv_rows = np.asarray(kv_rows, dtype=np.int64)
     # Which local rows reach any selected key: explicit mask, row blocks.
     reach = np.zeros(Sq, dtype=bool)
@@ -397,7 +424,8 @@ def attn_bwd_kv_rows(q, k, v, dout, doc_ids, cp_size: int, cp_rank: int,
     if max_query_rows is not None and rows.size > max_query_rows:
         raise ValueError(f"{rows.size} query rows reach the selected keys "
                          f"(limit {max_query_rows})")
-    out, lse = attn_fwd_rows(q, k, v, doc_b, cp_size, cp_rank, softmax_scale, 0, rows, lo=lo_b)
+    out, lse = attn_fwd_rows(q, k, v, doc_b, cp_size, cp_rank, softmax_scale, 0, rows, lo=lo_b,
+                             hi=hi_b)
     dk = np.zeros((kv_rows.size, Hkv, D)); dv = np.zeros((kv_rows.size, Hkv, D))
     if rows.size == 0:
         return dk, dv

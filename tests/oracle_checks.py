@@ -460,11 +460,105 @@ def check_interval_is_document_mask(orc):
             assert np.max(np.abs(x - y)) == 0.0
 
 
+def _cross_case(text, image, Hq, Hkv, D, seed):
+    """Text queries against the image tokens of their own sample: lo / hi of
+    every text token (its sample's image span) and random tensors; the keys
+    are indexed on their own (Skv = all image tokens)."""
+    istart = np.concatenate([[0], np.cumsum(image)[:-1]])
+    lo = np.repeat(istart, text)
+    hi = np.repeat(istart + np.asarray(image), text)
+    S, Skv = sum(text), sum(image)
+    q = _rand((1, S, Hq, D), seed, 0.7)
+    k = _rand((1, Skv, Hkv, D), seed + 1, 0.7)
+    v = _rand((1, Skv, Hkv, D), seed + 2, 1.0)
+    do = _rand((1, S, Hq, D), seed + 3, 1.0)
+    return lo[None], hi[None], q, k, v, do
+
+
+def check_cross_brute(orc):
+    """With hi, interval_mask is lo[p] <= t < hi[p] over keys indexed on
+    their own, and the row counts are hi - lo."""
+    g = np.random.default_rng(7)
+    S, Skv = 30, 50
+    lo = np.sort(g.integers(0, Skv - 1, S))
+    hi = np.maximum(np.sort(g.integers(1, Skv + 1, S)), lo + 1)
+    pos = np.arange(S)
+    M = orc.interval_mask(lo, pos, Skv, hi)
+    for p in range(S):
+        for t in range(Skv):
+            assert M[p, t] == (lo[p] <= t < hi[p])
+    cnt = orc.allowed_counts(None, 1, 0, Skv, lo=lo[None], hi=hi[None])
+    assert np.array_equal(cnt[0], hi - lo)
+
+
+def check_cross_attention(orc):
+    """Text queries attending to every image token of their own sample (lo,
+    hi = the sample's image span, more keys than queries) equal float64
+    attention with the explicit block mask: output and log-sum-exp directly,
+    gradients through torch.autograd; the per-row and per-key sampled forms
+    agree with the full ones."""
+    text, image = [4, 7, 3, 2], [13, 5, 21, 9]
+    Hq, Hkv, D = 4, 2, 8
+    lo, hi, q, k, v, do = _cross_case(text, image, Hq, Hkv, D, seed=61)
+    S, Skv, G, scale = sum(text), sum(image), Hq // Hkv, 0.35
+    mask = np.zeros((S, Skv), dtype=bool)
+    for p in range(S):
+        mask[p, lo[0, p]:hi[0, p]] = True
+    qt = torch.from_numpy(q).requires_grad_(True)
+    kt = torch.from_numpy(k).requires_grad_(True)
+    vt = torch.from_numpy(v).requires_grad_(True)
+    sc = torch.einsum("bshd,bthd->bhst", qt, kt.repeat_interleave(G, dim=2)) * scale
+    sc = sc.masked_fill(~torch.from_numpy(mask), float("-inf"))
+    o = torch.einsum("bhst,bthd->bshd", torch.softmax(sc, -1), vt.repeat_interleave(G, dim=2))
+    lse_ref = torch.logsumexp(sc, -1).permute(0, 2, 1).detach().numpy()
+    (o * torch.from_numpy(do)).sum().backward()
+    dq, dk, dv, out, lse = orc.attn_bwd(q, k, v, do, None, 1, 0, scale, threads=1,
+                                        return_fwd=True, lo=lo, hi=hi)
+    fo, fl = orc.attn_fwd(q, k, v, None, 1, 0, scale, threads=1, lo=lo, hi=hi)
+    o_ref = o.detach().numpy()
+    for x in (out, fo):
+        assert np.max(np.abs(x - o_ref)) < 1e-12
+    for x in (lse, fl):
+        assert np.max(np.abs(x - lse_ref)) < 1e-12
+    assert np.max(np.abs(dq - qt.grad.numpy())) < 1e-11
+    assert np.max(np.abs(dk - kt.grad.numpy())) < 1e-11
+    assert np.max(np.abs(dv - vt.grad.numpy())) < 1e-11
+    rows = [0, 5, S - 1]
+    ro, rl = orc.attn_fwd_rows(q, k, v, None, 1, 0, scale, 0, rows, lo=lo, hi=hi)
+    assert np.max(np.abs(ro - out[0, rows])) < 1e-12
+    assert np.max(np.abs(rl - lse[0, rows])) < 1e-12
+    rdq = orc.attn_bwd_rows(q, k, v, do, None, 1, 0, scale, 0, rows, lo=lo, hi=hi)
+    assert np.max(np.abs(rdq - dq[0, rows])) < 1e-12
+    kv = [0, 14, Skv - 1]
+    rdk, rdv = orc.attn_bwd_kv_rows(q, k, v, do, None, 1, 0, scale, 0, kv, lo=lo, hi=hi)
+    assert np.max(np.abs(rdk - dk[0, kv])) < 1e-12
+    assert np.max(np.abs(rdv - dv[0, kv])) < 1e-12
+
+
+def check_cross_causal_special_case(orc):
+    """hi[p] = p + 1 is the causal interval: the same results as lo alone,
+    on every CP rank."""
+    S, cp, Hq, Hkv, D = 64, 2, 4, 2, 8
+    lengths = [9, 23, 32]
+    doc, q, k, v, do = _case(S, cp, Hq, Hkv, D, lengths, seed=71)
+    lo = _window_lo(lengths, 6)[None]
+    hi = (np.arange(S) + 1)[None]
+    c = S // (2 * cp)
+    for r in range(cp):
+        Skv = (2 * cp - r) * c
+        args = (_local(q, S, cp, r), k[:, :Skv], v[:, :Skv], _local(do, S, cp, r))
+        a = orc.attn_bwd(*args, None, cp, r, 0.4, threads=1, return_fwd=True, lo=lo)
+        b = orc.attn_bwd(*args, None, cp, r, 0.4, threads=1, return_fwd=True, lo=lo, hi=hi)
+        for x, y in zip(a, b):
+            assert np.max(np.abs(x - y)) == 0.0
+
+
 ALL_CHECKS = [
     check_chunk_permutation, check_causal_equal_work, check_interval_rule,
     check_q_zero, check_softmax_rows, check_per_document,
     check_sdpa_explicit_mask, check_gqa_vs_mha, check_cp_split,
     check_finite_differences, check_autograd, check_window,
     check_sampled_forms, check_interval_brute, check_interval_sliding_window,
-    check_interval_is_document_mask,
+    check_interval_is_document_mask, check_cross_brute, check_cross_attention,
+    check_cross_causal_special_case,
 ]

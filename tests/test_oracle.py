@@ -93,9 +93,16 @@ def _mut_heads_strided(g, G):
     return slice(g, None, max(1, G))
 
 
-def _mut_interval_open_lo(lo, pos, Skv):
+def _mut_interval_open_lo(lo, pos, Skv, hi=None):
     t = np.arange(Skv)
-    return (t[None, :] > np.asarray(lo)[pos][:, None]) & (t[None, :] <= pos[:, None])
+    end = pos + 1 if hi is None else np.asarray(hi)[pos]
+    return (t[None, :] > np.asarray(lo)[pos][:, None]) & (t[None, :] < end[:, None])
+
+
+def _mut_interval_hi_inclusive(lo, pos, Skv, hi=None):
+    t = np.arange(Skv)
+    end = pos if hi is None else np.asarray(hi)[pos]
+    return (t[None, :] >= np.asarray(lo)[pos][:, None]) & (t[None, :] <= end[:, None])
 
 
 def _mut_softmax_no_scale(qb, kw, vw, M, scale):
@@ -113,6 +120,7 @@ MUTATIONS = {
     "heads_strided": ("_group_heads", _mut_heads_strided),
     "softmax_no_scale": ("_softmax_block", _mut_softmax_no_scale),
     "interval_open_lo": ("interval_mask", _mut_interval_open_lo),
+    "interval_hi_inclusive": ("interval_mask", _mut_interval_hi_inclusive),
 }
 
 
