@@ -9,4 +9,5 @@ from .binding import (  # noqa: F401
     docmask_gqa_check_docs, docmask_gqa_fwd_workspace_size, docmask_gqa_status_string,
     docmask_gqa_version, lib, status_string, docmask_gqa_timing_enable,
     docmask_gqa_kernel_times, docmask_gqa_interval_bounds, docmask_gqa_check_intervals,
+    docmask_gqa_attn_fwd_cross, docmask_gqa_check_cross_intervals,
 )

@@ -53,6 +53,10 @@ SIGNATURES = {
     "docmask_gqa_check_cu_seqlens": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
     "docmask_gqa_interval_bounds": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "docmask_gqa_check_intervals": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
+    "docmask_gqa_fwd_cross_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "docmask_gqa_attn_fwd_cross": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                                  _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "docmask_gqa_check_cross_intervals": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp]),
     "docmask_gqa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "docmask_gqa_version": (ctypes.c_int, []),
     "docmask_gqa_timing_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -314,6 +318,57 @@ def docmask_gqa_check_intervals(lo, stream=None) -> int:
     rc = lib().docmask_gqa_check_intervals(_ptr(lo), B, S, _stream(stream))
     if rc < 0:
         raise DocmaskGQAError(rc, "docmask_gqa_check_intervals")
+    return rc
+
+
+def docmask_gqa_attn_fwd_cross(q, k, v, lo, hi, *, softmax_scale: Optional[float] = None,
+                               out=None, lse=None, workspace=None, stream=None):
+    """Cross-attention forward: query token p of q [B,S,Hq,D] attends to keys
+    lo[b,p] .. hi[b,p]-1 of k/v [B,Skv,Hkv,D] (lo, hi int32 [B,S],
+    non-decreasing, 0 <= lo < hi <= Skv).  Returns out [B,S,Hq,D] bf16 and
+    lse [B,S,Hq] fp32."""
+    import torch
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(lo, "lo", torch.int32, 2)
+    _need(hi, "hi", torch.int32, 2)
+    B, S, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k and v must be [B, Skv, Hkv, D] matching q")
+    if tuple(lo.shape) != (B, S) or tuple(hi.shape) != (B, S):
+        raise ValueError("lo and hi must be [B, S]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(B, S, Hq, dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    need = lib().docmask_gqa_fwd_cross_workspace_size(B, S, Skv, Hq, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    rc = lib().docmask_gqa_attn_fwd_cross(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(lo), _ptr(hi), B, S, Skv, Hq, Hkv, D,
+        float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != DMGQA_OK:
+        raise DocmaskGQAError(rc, "docmask_gqa_attn_fwd_cross")
+    return out, lse
+
+
+def docmask_gqa_check_cross_intervals(lo, hi, Skv: int, stream=None) -> int:
+    """0 if lo, hi [B, S] are non-decreasing with 0 <= lo < hi <= Skv
+    (synchronises)."""
+    import torch
+    _need(lo, "lo", torch.int32, 2)
+    _need(hi, "hi", torch.int32, 2)
+    B, S = lo.shape
+    rc = lib().docmask_gqa_check_cross_intervals(_ptr(lo), _ptr(hi), B, S, Skv, _stream(stream))
+    if rc < 0:
+        raise DocmaskGQAError(rc, "docmask_gqa_check_cross_intervals")
     return rc
 
 

@@ -211,14 +211,32 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* doc_ids
   const Geo g = make_geo(s, softmax_scale);
   int32_t* order = reinterpret_cast<int32_t*>(ws + L.order);
   timing_begin(kKOrder, st);
-  hipError_t e = launch_tile_order_fwd(dstart, g, order, st);
+  hipError_t e = launch_tile_order_fwd(dstart, nullptr, g, order, st);
   timing_end(kKOrder, st);
   if (e != hipSuccess) return DMGQA_ERR_HIP;
   timing_begin(kKFwd, st);
   e = launch_fwd(D, static_cast<const u16*>(q), static_cast<const u16*>(k),
-                 static_cast<const u16*>(v), dstart, order, static_cast<u16*>(out), lse, g, st);
+                 static_cast<const u16*>(v), dstart, nullptr, order, static_cast<u16*>(out), lse, g,
+                 st);
   timing_end(kKFwd, st);
   return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
+}
+
+// Shape of a cross-attention call: S query tokens (cp_size 1, so the local
+// rows are the S tokens in order) against Skv keys indexed on their own.
+int check_cross_shape(int B, int S, int Skv, int Hq, int Hkv, int D, Shape* s) {
+  int rc = check_shape(B, S, S, Hq, Hkv, D, 1, 0, s);
+  if (rc != DMGQA_OK) return rc;
+  if (Skv < 0 || (Skv == 0 && !s->empty)) return DMGQA_ERR_INVALID_ARG;
+  if ((long long)Skv * 2 >= (1LL << 31) || (long long)B * Skv * Hkv * D >= (1LL << 31))
+    return DMGQA_ERR_UNSUPPORTED;
+  s->Skv = Skv;
+  return DMGQA_OK;
+}
+
+size_t cross_workspace_bytes(const Shape& s) {
+  const size_t nt = ((size_t)s.Sq * s.G + kFwdBM - 1) / kFwdBM;
+  return align_up((size_t)s.B * nt * sizeof(int32_t));
 }
 
 }  // namespace
@@ -436,6 +454,65 @@ int docmask_gqa_interval_bounds(const int32_t* lo, int32_t B, int32_t S, int32_t
   const hipError_t e = launch_prep_interval(lo, B, S, Skv, bounds, bounds + (size_t)B * Skv, st);
   timing_end(kKPrep, st);
   return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
+}
+
+size_t docmask_gqa_fwd_cross_workspace_size(int32_t B, int32_t S, int32_t Skv, int32_t Hq,
+                                            int32_t Hkv, int32_t D) {
+  Shape s;
+  if (check_cross_shape(B, S, Skv, Hq, Hkv, D, &s) != DMGQA_OK || s.empty) return 0;
+  return cross_workspace_bytes(s);
+}
+
+int docmask_gqa_attn_fwd_cross(const void* q, const void* k, const void* v, const int32_t* lo,
+                               const int32_t* hi, int32_t B, int32_t S, int32_t Skv, int32_t Hq,
+                               int32_t Hkv, int32_t D, float softmax_scale, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  int rc = check_cross_shape(B, S, Skv, Hq, Hkv, D, &s);
+  if (rc != DMGQA_OK) return rc;
+  if (!std::isfinite(softmax_scale) || softmax_scale == 0.f) return DMGQA_ERR_INVALID_ARG;
+  if (s.empty) return DMGQA_OK;
+  if (!q || !k || !v || !lo || !hi || !out || !lse || !workspace) return DMGQA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(lse, 4) || !aligned(lo, 4) || !aligned(hi, 4) || !aligned(workspace, 16))
+    return DMGQA_ERR_INVALID_ARG;
+  if (workspace_bytes < cross_workspace_bytes(s)) return DMGQA_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const Geo g = make_geo(s, softmax_scale);
+  int32_t* order = static_cast<int32_t*>(workspace);
+  timing_begin(kKOrder, st);
+  hipError_t e = launch_tile_order_fwd(lo, hi, g, order, st);
+  timing_end(kKOrder, st);
+  if (e != hipSuccess) return DMGQA_ERR_HIP;
+  timing_begin(kKFwd, st);
+  e = launch_fwd(D, static_cast<const u16*>(q), static_cast<const u16*>(k),
+                 static_cast<const u16*>(v), lo, hi, order, static_cast<u16*>(out), lse, g, st);
+  timing_end(kKFwd, st);
+  return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
+}
+
+int docmask_gqa_check_cross_intervals(const int32_t* lo, const int32_t* hi, int32_t B, int32_t S,
+                                      int32_t Skv, void* stream) {
+  if (B < 0 || S < 0 || Skv < 0) return DMGQA_ERR_INVALID_ARG;
+  if (B == 0 || S == 0) return 0;
+  if (!lo || !hi) return DMGQA_ERR_INVALID_ARG;
+  std::vector<int32_t> hl((size_t)B * S), hh((size_t)B * S);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(hl.data(), lo, hl.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipMemcpyAsync(hh.data(), hi, hh.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return DMGQA_ERR_HIP;
+  for (int b = 0; b < B; ++b) {
+    const int32_t* l = hl.data() + (size_t)b * S;
+    const int32_t* h = hh.data() + (size_t)b * S;
+    for (int p = 0; p < S; ++p) {
+      if (l[p] < 0 || l[p] >= h[p] || h[p] > Skv) return 1;
+      if (p > 0 && (l[p] < l[p - 1] || h[p] < h[p - 1])) return 1;
+    }
+  }
+  return 0;
 }
 
 int docmask_gqa_check_intervals(const int32_t* lo, int32_t B, int32_t S, void* stream) {

@@ -82,11 +82,15 @@ __device__ __forceinline__ bf16x8 tr_group(const char* tile, const int (&lane_of
 
 }  // namespace
 
-template <int D>
+// CROSS: interval masks with explicit ends -- row p reaches keys dstart[p]
+// .. dhi[p]-1 (both [B, S], indexed by query position, keys indexed on
+// their own); otherwise keys dstart[p] .. p with dstart [B, Skv].
+template <int D, bool CROSS>
 __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict__ q,
                                                           const u16* __restrict__ k,
                                                           const u16* __restrict__ v,
                                                           const int32_t* __restrict__ dstart,
+                                                          const int32_t* __restrict__ dhi,
                                                           const int32_t* __restrict__ order,
                                                           u16* __restrict__ out,
                                                           float* __restrict__ lse, Geo g) {
@@ -115,15 +119,19 @@ __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict
   const int tok = rr / g.G;
   const int head = kvh * g.G + rr % g.G;
   const int pos = local_pos(tok, g.c, g.cp, g.rank);
-  const int32_t* ds = dstart + (size_t)b * g.Skv;
+  const int32_t* ds = dstart + (size_t)b * (CROSS ? g.S : g.Skv);
+  const int32_t* dh = CROSS ? dhi + (size_t)b * g.S : nullptr;
   const int lo = ds[pos];
+  // last key this row reaches
+  const int last = CROSS ? dh[pos] - 1 : pos;
 
   const size_t qoff = (((size_t)b * g.Sq + tok) * g.Hq + head) * D;
   bf16x8 qop[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) qop[kk] = ld_bf16x8(q + qoff + 8 * h + 16 * kk);
 
-  const QTileKeys kr = qtile_keys<BM, BN>(row0, ds, g);
+  const QTileKeys kr =
+      CROSS ? qtile_keys_iv<BM, BN>(row0, ds, dh, g) : qtile_keys<BM, BN>(row0, ds, g);
   const int ntiles = kr.na + kr.nb;
 
   float m = -INFINITY, l = 0.f;
@@ -161,7 +169,7 @@ __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict
   // byte offset of this lane's row chunk from the batch / head base (K and
   // V share the layout; the host keeps each tensor below 2^31 elements)
   auto dma_off = [&](int it) __attribute__((always_inline)) {
-    const int key = min(tile_start(it) + drow, g.Skv - 1);
+    const int key = max(min(tile_start(it) + drow, g.Skv - 1), 0);
     return ((unsigned)key * (unsigned)kvstride + coff) * 2u;
   };
   auto issue_k = [&](unsigned off, char* st) __attribute__((always_inline)) {
@@ -201,12 +209,12 @@ __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict
     mid();
     const bool full = kr.max_lo <= t0 && t0 + BN - 1 <= kr.min_pos;
     if (!full) {
-      // allowed keys lo..pos relative to this lane's first key t0 + 4h;
+      // allowed keys lo..last relative to this lane's first key t0 + 4h;
       // register r holds key offset 8*(r/4) + r%4 (+32 for s1)
       // key offset c is allowed iff lo_rel <= c <= hi_rel, one unsigned
-      // compare (hi_rel >= lo_rel: a row always sees its own position)
+      // compare (hi_rel >= lo_rel: a row always reaches at least one key)
       const int lo_rel = lo - (t0 + 4 * h);
-      const unsigned span = (unsigned)(pos - lo);
+      const unsigned span = (unsigned)(last - lo);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int c = 8 * (r >> 2) + (r & 3);
@@ -296,13 +304,18 @@ __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict
 }
 
 hipError_t launch_fwd(int D, const u16* q, const u16* k, const u16* v, const int32_t* dstart,
-                      const int32_t* order, u16* out, float* lse, const Geo& g, hipStream_t st) {
+                      const int32_t* dhi, const int32_t* order, u16* out, float* lse,
+                      const Geo& g, hipStream_t st) {
   const int nt = (g.Sq * g.G + kRows - 1) / kRows;
   const unsigned grid = (unsigned)nt * g.B * g.Hkv;
-  if (D == 128)
-    fwd_kernel<128><<<grid, kWaves * 64, 0, st>>>(q, k, v, dstart, order, out, lse, g);
-  else
-    fwd_kernel<64><<<grid, kWaves * 64, 0, st>>>(q, k, v, dstart, order, out, lse, g);
+#define DMGQA_FWD(DD, CC) \
+  fwd_kernel<DD, CC><<<grid, kWaves * 64, 0, st>>>(q, k, v, dstart, dhi, order, out, lse, g)
+  if (D == 128) {
+    if (dhi) DMGQA_FWD(128, true); else DMGQA_FWD(128, false);
+  } else {
+    if (dhi) DMGQA_FWD(64, true); else DMGQA_FWD(64, false);
+  }
+#undef DMGQA_FWD
   return hipGetLastError();
 }
 

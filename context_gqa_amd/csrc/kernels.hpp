@@ -49,8 +49,11 @@ hipError_t launch_prep_interval(const int32_t* lo, int B, int S, int Skv, int32_
 hipError_t launch_sched_dkdv(const int32_t* dend, const Geo& g, int nkt, int max_split_base,
                              SchedHeader* hdr, int2* tile_info, int2* items, int4* tile_rows,
                              hipStream_t st);
+// dhi == nullptr: causal interval masks (keys dstart[p] .. p, dstart [B, Skv]);
+// else keys dstart[p] .. dhi[p]-1 with dstart, dhi [B, S].
 hipError_t launch_fwd(int D, const u16* q, const u16* k, const u16* v, const int32_t* dstart,
-                      const int32_t* order, u16* out, float* lse, const Geo& g, hipStream_t st);
+                      const int32_t* dhi, const int32_t* order, u16* out, float* lse,
+                      const Geo& g, hipStream_t st);
 hipError_t launch_bwd_dq(int D, const u16* q, const u16* k, const u16* v, const u16* out,
                          const u16* dout, const float* lse, const int32_t* dstart, u16* dq,
                          float* Lbuf, float* Nbuf, const Geo& g, hipStream_t st);
@@ -68,8 +71,8 @@ hipError_t launch_sched_rowstat(int D, const int32_t* dstart, const int32_t* den
                                 hipStream_t st);
 // Heaviest-first dispatch order of the forward's query tiles (one block):
 // order[i] = b * nt + tile for B * nt items, nt = ceil(Sq * G / kFwdBM).
-hipError_t launch_tile_order_fwd(const int32_t* dstart, const Geo& g, int32_t* order,
-                                 hipStream_t st);
+hipError_t launch_tile_order_fwd(const int32_t* dstart, const int32_t* dhi, const Geo& g,
+                                 int32_t* order, hipStream_t st);
 // dQ from the dS stash, and (in workgroups appended to its grid) the sum of
 // the partial dK/dV slots.
 hipError_t launch_bwd_dq_stash(int D, const u16* k, const int32_t* dstart, const int4* tile_rows,

@@ -392,9 +392,10 @@ __device__ int block_scan_add(int v, int* sh) {
 constexpr int kOrderBins = 4096;
 static_assert(kOrderBins % kScanThreads == 0, "bins per thread");
 
-template <int BN>
+template <int BN, bool CROSS = false>
 __device__ void tile_order_body(const int32_t* __restrict__ dstart, const Geo& g,
-                                int32_t* __restrict__ order) {
+                                int32_t* __restrict__ order,
+                                const int32_t* __restrict__ dhi = nullptr) {
   __shared__ int cnt[kOrderBins];
   __shared__ int sh[32];
   constexpr int BM = kFwdBM;
@@ -405,7 +406,9 @@ __device__ void tile_order_body(const int32_t* __restrict__ dstart, const Geo& g
   // class 0 holds the heaviest items
   auto cls = [&](int x) {
     const int b = x / nt, t = x - b * nt;
-    const QTileKeys kr = qtile_keys<BM, BN>(t * BM, dstart + (size_t)b * g.Skv, g);
+    const QTileKeys kr =
+        CROSS ? qtile_keys_iv<BM, BN>(t * BM, dstart + (size_t)b * g.S, dhi + (size_t)b * g.S, g)
+              : qtile_keys<BM, BN>(t * BM, dstart + (size_t)b * g.Skv, g);
     return kOrderBins - 1 - min(kr.na + kr.nb, kOrderBins - 1);
   };
   // the classes of the first kKeep items of each thread stay in registers
@@ -447,6 +450,13 @@ __device__ void tile_order_body(const int32_t* __restrict__ dstart, const Geo& g
 __global__ __launch_bounds__(kScanThreads) void tile_order_fwd(const int32_t* __restrict__ dstart,
                                                                Geo g, int32_t* __restrict__ order) {
   tile_order_body<kFwdBN>(dstart, g, order);
+}
+
+// The same for interval masks with explicit ends (dstart, dhi [B, S]).
+__global__ __launch_bounds__(kScanThreads) void tile_order_fwd_iv(
+    const int32_t* __restrict__ dstart, const int32_t* __restrict__ dhi, Geo g,
+    int32_t* __restrict__ order) {
+  tile_order_body<kFwdBN, true>(dstart, g, order, dhi);
 }
 
 // The dK/dV schedule (block 0), the dQ tile order (block 1) and the row
@@ -521,9 +531,12 @@ hipError_t launch_sched_rowstat(int D, const int32_t* dstart, const int32_t* den
   return hipGetLastError();
 }
 
-hipError_t launch_tile_order_fwd(const int32_t* dstart, const Geo& g, int32_t* order,
-                                 hipStream_t st) {
-  tile_order_fwd<<<1, kScanThreads, 0, st>>>(dstart, g, order);
+hipError_t launch_tile_order_fwd(const int32_t* dstart, const int32_t* dhi, const Geo& g,
+                                 int32_t* order, hipStream_t st) {
+  if (dhi)
+    tile_order_fwd_iv<<<1, kScanThreads, 0, st>>>(dstart, dhi, g, order);
+  else
+    tile_order_fwd<<<1, kScanThreads, 0, st>>>(dstart, g, order);
   return hipGetLastError();
 }
 

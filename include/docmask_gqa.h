@@ -164,6 +164,34 @@ int docmask_gqa_interval_bounds(const int32_t* lo, int32_t B, int32_t S,
                                 int32_t Skv, int32_t* bounds,
                                 size_t bounds_bytes, void* stream);
 
+/* Cross-attention forward: non-causal intervals with explicit ends.  From
+ * "Scaling Llama 3 Training with Efficient Parallelism Strategies", the
+ * section on pipeline parallelism for multimodal training (Figure 5 and its
+ * second challenge): cross-attention layers take image sequences of 1.2K-3K
+ * tokens next to text of under 200 tokens.  Query token p (no context
+ * parallelism: the rows of q are the S tokens in order) attends to keys
+ * lo[b][p] .. hi[b][p]-1 of k and v, whose rows are indexed on their own
+ * (for example the image tokens of p's sample).
+ *   q, out : bf16 [B, S, Hq, D], S even;  k, v : bf16 [B, Skv, Hkv, D];
+ *   lse    : fp32 [B, S, Hq];
+ *   lo, hi : int32 [B, S] device arrays, non-decreasing in p, with
+ *            0 <= lo[b][p] < hi[b][p] <= Skv.  These are preconditions the
+ *            call does not check; docmask_gqa_check_cross_intervals checks
+ *            them synchronously and returns 0 (valid) or 1.
+ * Workspace: docmask_gqa_fwd_cross_workspace_size bytes (the tile order).
+ * There is no backward for this form yet.  Errors and ownership as above. */
+size_t docmask_gqa_fwd_cross_workspace_size(int32_t B, int32_t S, int32_t Skv,
+                                            int32_t Hq, int32_t Hkv, int32_t D);
+int docmask_gqa_attn_fwd_cross(const void* q, const void* k, const void* v,
+                               const int32_t* lo, const int32_t* hi, int32_t B,
+                               int32_t S, int32_t Skv, int32_t Hq, int32_t Hkv,
+                               int32_t D, float softmax_scale, void* out,
+                               float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream);
+int docmask_gqa_check_cross_intervals(const int32_t* lo, const int32_t* hi,
+                                      int32_t B, int32_t S, int32_t Skv,
+                                      void* stream);
+
 /* The forward and backward with the masking given as a bounds array from
  * docmask_gqa_doc_bounds or docmask_gqa_interval_bounds (same B, S and
  * Skv; its writes ordered before these calls) instead of doc_ids /

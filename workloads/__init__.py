@@ -158,6 +158,43 @@ def full_tensors(cfg: Config, seed: int, dtype=None):
     return q.to(out_dtype), k.to(out_dtype), v.to(out_dtype), dout.to(out_dtype)
 
 
+def cross_lengths(n: int, seed: int, text=(100, 200), image=(1200, 3000)):
+    """Per-sample text and image token counts of a cross-attention batch:
+    uniform in [text[0], text[1]) and [image[0], image[1]] (the multimodal
+    sizes of "Scaling Llama 3 Training with Efficient Parallelism
+    Strategies": image 1.2K-3K tokens, text under 200); the last text count
+    is bumped by one if needed so that the text total is even."""
+    rng = np.random.default_rng(seed)
+    t = rng.integers(text[0], text[1], n)
+    im = rng.integers(image[0], image[1] + 1, n)
+    if t.sum() % 2:
+        t[-1] += 1
+    return t.tolist(), im.tolist()
+
+
+def cross_bounds(text: List[int], image: List[int]):
+    """lo, hi (int32 [S]) of every text token: the image span of its sample
+    when the samples' text and image tokens are packed in order."""
+    istart = np.concatenate([[0], np.cumsum(image)[:-1]])
+    lo = np.repeat(istart, text).astype(np.int32)
+    hi = np.repeat(istart + np.asarray(image), text).astype(np.int32)
+    return lo, hi
+
+
+def cross_tensors(B: int, S: int, Skv: int, Hq: int, Hkv: int, D: int, seed: int,
+                  value_scale: float = 0.5):
+    """q [B,S,Hq,D] and k, v [B,Skv,Hkv,D], drawn in that order from one CPU
+    torch.Generator seeded with `seed` as fp32 N(0,1), scaled, rounded to
+    bf16."""
+    import torch
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    q = torch.randn(B, S, Hq, D, generator=g, dtype=torch.float32) * value_scale
+    k = torch.randn(B, Skv, Hkv, D, generator=g, dtype=torch.float32) * value_scale
+    v = torch.randn(B, Skv, Hkv, D, generator=g, dtype=torch.float32) * value_scale
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
 def take_local_rows(x, S: int, cp_size: int, cp_rank: int):
     """The rank-local row layout used by the attention calls: along dim 1,
     the rank's first chunk (chunk cp_rank) followed by its second chunk
