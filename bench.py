@@ -212,6 +212,54 @@ def cpu_baseline(runs, min_s: float = 10.0, max_s: float = 30.0) -> dict:
                       f"backward on seeds {done} (same inputs as the GPU steps)"}
 
 
+def cross_study(args) -> int:
+    """Forward-only measurement of the cross-attention form: 32 packed
+    samples of 100-199 text tokens against 1200-3000 image tokens each
+    (query token p attends to its own sample's image tokens), 16 query heads
+    on 1 KV head, d = 128, one JSON line per seed."""
+    import torch
+    import context_gqa_amd as M
+    import workloads as W
+    seeds = [int(x) for x in args.seeds.split(",") if x != ""]
+    res = []
+    for seed in seeds:
+        text, image = W.cross_lengths(32, seed=seed)
+        lo, hi = W.cross_bounds(text, image)
+        S, Skv, Hq, Hkv, D = sum(text), sum(image), 16, 1, 128
+        q, k, v = (x.cuda() for x in W.cross_tensors(1, S, Skv, Hq, Hkv, D, seed=seed + 100))
+        lo_d = torch.from_numpy(lo[None]).cuda()
+        hi_d = torch.from_numpy(hi[None]).cuda()
+        out = torch.empty_like(q)
+        lse = torch.empty(1, S, Hq, dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(M.lib().docmask_gqa_fwd_cross_workspace_size(1, S, Skv, Hq, Hkv, D), 1),
+                         dtype=torch.uint8, device="cuda")
+
+        def call():
+            M.docmask_gqa_attn_fwd_cross(q, k, v, lo_d, hi_d, out=out, lse=lse, workspace=ws)
+
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.steps
+        pairs = int(np.dot(np.asarray(text, dtype=np.int64), np.asarray(image, dtype=np.int64)))
+        flops = 4.0 * D * pairs * Hq
+        res.append({"seed": seed, "S": S, "Skv": Skv, "fwd_ms": round(ms, 4),
+                    "tflops": round(flops / (ms * 1e-3) / 1e12, 2)})
+        print(f"cross seed {seed}: S={S} Skv={Skv} {ms:.4f} ms {res[-1]['tflops']} TFLOP/s",
+              file=sys.stderr, flush=True)
+    print(json.dumps({"study": "cross-attention forward", "heads": "16/1", "head_dim": 128,
+                      "samples": 32, "text": "100-199", "image": "1200-3000",
+                      "steps": args.steps, "warmup": args.warmup, "per_seed": res}))
+    return 0
+
+
 def all_ranks(args) -> int:
     """Per-rank study of one workload on one GPU: every CP rank's share
     (forward with its document bounds, then backward), timed by HIP events
@@ -329,6 +377,9 @@ def main(argv=None) -> int:
     ap.add_argument("--all-ranks", action="store_true",
                     help="per-rank study instead of the benchmark line: every CP rank of the "
                          "workload, document and single-document masks (see all_ranks)")
+    ap.add_argument("--cross", action="store_true",
+                    help="forward-only measurement of the cross-attention form (text queries "
+                         "over their own sample's image tokens) instead of the benchmark line")
     ap.add_argument("--no-clocks", action="store_true",
                     help="skip reading the GPU clocks with rocm-smi during a busy phase")
     ap.add_argument("--recompute", action="store_true",
@@ -372,6 +423,8 @@ def main(argv=None) -> int:
     M.lib()
     if args.all_ranks:
         return all_ranks(args)
+    if args.cross:
+        return cross_study(args)
     cfg = W.CONFIGS[args.workload]
     rank = cfg.ranks[0] if args.rank is None else args.rank
     seeds = [int(s) for s in args.seeds.split(",") if s != ""]
