@@ -207,3 +207,51 @@ def test_bounds_variants_reject():
                                         b.p, b.p, 1 << 12, None) == INV
     assert L.docmask_gqa_attn_bwd_bounds(b.p, b.p, b.p, b.p, b.p, b.p, b.p, *common, b.p, b.p,
                                         b.p, b.p, 0, None) == WS
+
+
+# ---------------------------------------------------------------- cross-attention forward
+
+def test_cross_workspace_size():
+    f = M.lib().docmask_gqa_fwd_cross_workspace_size
+    # the tile order: B * ceil(S * G / 128) int32, 256-byte aligned
+    assert f(1, 4870, 66775, 16, 1, 128) == -(-(-(-4870 * 16 // 128) * 4) // 256) * 256
+    assert f(2, 64, 3000, 4, 4, 64) == 256
+    assert f(1, 63, 100, 4, 1, 64) == 0          # S odd
+    assert f(1, 64, 0, 4, 1, 64) == 0            # no keys
+    assert f(1, 64, 100, 4, 1, 96) == 0          # D unsupported
+    assert f(0, 64, 100, 4, 1, 64) == 0          # empty
+
+
+def _cross_call(**kw):
+    b = _Buf(1 << 16)
+    a = dict(q=b.p, k=b.p, v=b.p, lo=b.p, hi=b.p, B=1, S=64, Skv=300, Hq=4, Hkv=1, D=64,
+             scale=0.125, out=b.p, lse=b.p, ws=b.p, nbytes=1 << 16)
+    a.update(kw)
+    return M.lib().docmask_gqa_attn_fwd_cross(a["q"], a["k"], a["v"], a["lo"], a["hi"], a["B"],
+                                              a["S"], a["Skv"], a["Hq"], a["Hkv"], a["D"],
+                                              a["scale"], a["out"], a["lse"], a["ws"],
+                                              a["nbytes"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(lo=None), INV),
+    (dict(hi=None), INV),
+    (dict(S=63), INV),                 # S must be even
+    (dict(Skv=0), INV),
+    (dict(Hq=6, Hkv=4), INV),          # Hq % Hkv
+    (dict(D=96), UNS),
+    (dict(scale=0.0), INV),
+    (dict(scale=float("inf")), INV),
+    (dict(nbytes=4), WS),
+    (dict(ws=None), INV),
+])
+def test_cross_fwd_rejects(kw, want):
+    """Every check happens before any HIP call, so these run without a GPU."""
+    assert _cross_call(**kw) == want
+
+
+def test_cross_checker_rejects_sizes():
+    L = M.lib()
+    assert L.docmask_gqa_check_cross_intervals(None, None, -1, 4, 4, None) == INV
+    assert L.docmask_gqa_check_cross_intervals(None, None, 0, 4, 4, None) == 0
+    assert L.docmask_gqa_check_cross_intervals(None, None, 1, 4, 4, None) == INV
