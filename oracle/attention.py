@@ -67,7 +67,7 @@ from typing import List, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
-    "chunk_positions", "allowed_mask", "interval_mask", "allowed_counts", "attn_probs",
+    "chunk_positions", "query_positions", "allowed_mask", "interval_mask", "allowed_counts", "attn_probs",
     "attn_fwd", "attn_bwd", "attn_fwd_rows", "attn_bwd_rows",
     "attn_bwd_kv_rows", "to_f64",
 ]
@@ -93,6 +93,18 @@ def chunk_positions(S: int, cp_size: int, cp_rank: int) -> np.ndarray:
     j = 2 * cp_size - 1 - cp_rank
     second = np.arange(j * c, (j + 1) * c, dtype=np.int64)
     return np.concatenate([first, second])
+
+
+def query_positions(S: int, cp_size: int, cp_rank: int, hi=None) -> np.ndarray:
+    """Positions of the local query rows.  With hi (the cross-attention form)
+    and cp_size 1 the rows are the S query tokens in order, for any S: the
+    multimodal cross-attention of "Scaling Llama 3 Training with Efficient
+    Parallelism Strategies" (pipeline parallelism for multimodal training)
+    is not split over context-parallel ranks.  For even S that is the same
+    as the chunk map with one rank.  Otherwise the chunk map."""
+    if hi is not None and cp_size == 1 and cp_rank == 0:
+        return np.arange(S, dtype=np.int64)
+    return chunk_positions(S, cp_size, cp_rank)
 
 
 def allowed_mask(doc: np.ndarray, pos: np.ndarray, Skv: int) -> np.ndarray:
@@ -141,7 +153,7 @@ def allowed_counts(doc_ids: Optional[np.ndarray], cp_size: int, cp_rank: int, Sk
     mask.  doc_ids (or lo, and optionally hi): [B, S].  Returns int64 [B, Sq]."""
     arr, mask = _masks(doc_ids, lo, hi)
     B, S = arr.shape
-    pos = chunk_positions(S, cp_size, cp_rank)
+    pos = query_positions(S, cp_size, cp_rank, hi)
     out = np.zeros((B, pos.size), dtype=np.int64)
     for b in range(B):
         for s in range(0, pos.size, block):
@@ -232,7 +244,7 @@ def _check(q, k, doc_ids, cp_size, cp_rank, hi=None):
         raise ValueError("shape mismatch")
     if Hq % Hkv != 0:
         raise ValueError("Hq must be a multiple of Hkv")
-    pos = chunk_positions(S, cp_size, cp_rank)
+    pos = query_positions(S, cp_size, cp_rank, hi)
     if pos.size != Sq:
         raise ValueError("q must hold 2*S/(2*cp_size) local rows")
     if hi is None:

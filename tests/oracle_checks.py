@@ -496,8 +496,13 @@ def check_cross_attention(orc):
     hi = the sample's image span, more keys than queries) equal float64
     attention with the explicit block mask: output and log-sum-exp directly,
     gradients through torch.autograd; the per-row and per-key sampled forms
-    agree with the full ones."""
-    text, image = [4, 7, 3, 2], [13, 5, 21, 9]
+    agree with the full ones.  An even and an odd number of text tokens
+    (cross-attention is not split over CP ranks, so any count is valid)."""
+    _cross_attention_case(orc, [4, 7, 3, 2], [13, 5, 21, 9])
+    _cross_attention_case(orc, [4, 7, 3, 3], [13, 5, 21, 9])
+
+
+def _cross_attention_case(orc, text, image):
     Hq, Hkv, D = 4, 2, 8
     lo, hi, q, k, v, do = _cross_case(text, image, Hq, Hkv, D, seed=61)
     S, Skv, G, scale = sum(text), sum(image), Hq // Hkv, 0.35

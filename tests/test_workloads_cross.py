@@ -4,14 +4,17 @@ import numpy as np
 import workloads as W
 
 
-def test_cross_lengths_ranges_and_even_total():
+def test_cross_lengths_ranges():
+    totals = []
     for seed in range(5):
         t, im = W.cross_lengths(32, seed)
         assert len(t) == len(im) == 32
-        assert sum(t) % 2 == 0
-        assert all(100 <= x <= 200 for x in t)        # 200 only after the parity bump
+        assert all(100 <= x < 200 for x in t)
         assert all(1200 <= x <= 3000 for x in im)
+        totals.append(sum(t))
         assert W.cross_lengths(32, seed) == (t, im)   # seeded
+    # no parity adjustment: odd text totals occur (any S is accepted)
+    assert any(x % 2 for x in totals)
 
 
 def test_cross_bounds_are_each_samples_image_span():

@@ -162,13 +162,10 @@ def cross_lengths(n: int, seed: int, text=(100, 200), image=(1200, 3000)):
     """Per-sample text and image token counts of a cross-attention batch:
     uniform in [text[0], text[1]) and [image[0], image[1]] (the multimodal
     sizes of "Scaling Llama 3 Training with Efficient Parallelism
-    Strategies": image 1.2K-3K tokens, text under 200); the last text count
-    is bumped by one if needed so that the text total is even."""
+    Strategies": image 1.2K-3K tokens, text under 200)."""
     rng = np.random.default_rng(seed)
     t = rng.integers(text[0], text[1], n)
     im = rng.integers(image[0], image[1] + 1, n)
-    if t.sum() % 2:
-        t[-1] += 1
     return t.tolist(), im.tolist()
 
 
