@@ -23,6 +23,10 @@ DMGQA_ERR_UNSUPPORTED = -2
 DMGQA_ERR_WORKSPACE = -3
 DMGQA_ERR_HIP = -4
 
+DMGQA_BWD_PATH_RECOMPUTE = 0
+DMGQA_BWD_PATH_STASH = 1
+DMGQA_BWD_PATH_MIXED = 2
+
 _lib = None
 
 _i32 = ctypes.c_int32
@@ -35,6 +39,8 @@ SIGNATURES = {
     "docmask_gqa_fwd_workspace_size": (_sz, [_i32] * 7),
     "docmask_gqa_bwd_workspace_size": (_sz, [_i32] * 7),
     "docmask_gqa_bwd_workspace_size_min": (_sz, [_i32] * 7),
+    "docmask_gqa_bwd_workspace_size_full": (_sz, [_i32] * 7),
+    "docmask_gqa_bwd_path": (ctypes.c_int, [_i32] * 8 + [_sz]),
     "docmask_gqa_attn_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp,
                                             _sz, _vp]),
@@ -56,6 +62,10 @@ SIGNATURES = {
     "docmask_gqa_fwd_cross_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "docmask_gqa_attn_fwd_cross": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                                   _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "docmask_gqa_bwd_cross_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "docmask_gqa_attn_bwd_cross": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                                  _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp,
+                                                  _vp, _vp, _sz, _vp]),
     "docmask_gqa_check_cross_intervals": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp]),
     "docmask_gqa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "docmask_gqa_version": (ctypes.c_int, []),
@@ -107,6 +117,17 @@ def docmask_gqa_bwd_workspace_size(B, S, Skv, Hq, Hkv, D, cp_size) -> int:
 
 def docmask_gqa_bwd_workspace_size_min(B, S, Skv, Hq, Hkv, D, cp_size) -> int:
     return int(lib().docmask_gqa_bwd_workspace_size_min(B, S, Skv, Hq, Hkv, D, cp_size))
+
+
+def docmask_gqa_bwd_workspace_size_full(B, S, Skv, Hq, Hkv, D, cp_size) -> int:
+    return int(lib().docmask_gqa_bwd_workspace_size_full(B, S, Skv, Hq, Hkv, D, cp_size))
+
+
+def docmask_gqa_bwd_path(B, S, Skv, Hq, Hkv, D, cp_size, cp_rank, workspace_bytes) -> int:
+    """DMGQA_BWD_PATH_* the backward takes with this workspace (or a negative
+    status)."""
+    return int(lib().docmask_gqa_bwd_path(B, S, Skv, Hq, Hkv, D, cp_size, cp_rank,
+                                          int(workspace_bytes)))
 
 
 def _ptr(t) -> Optional[int]:
@@ -357,6 +378,51 @@ def docmask_gqa_attn_fwd_cross(q, k, v, lo, hi, *, softmax_scale: Optional[float
     if rc != DMGQA_OK:
         raise DocmaskGQAError(rc, "docmask_gqa_attn_fwd_cross")
     return out, lse
+
+
+def docmask_gqa_attn_bwd_cross(q, k, v, out, dout, lse, lo, hi, *,
+                               softmax_scale: Optional[float] = None, dq=None, dk=None,
+                               dv=None, workspace=None, stream=None):
+    """Cross-attention backward (same masking as docmask_gqa_attn_fwd_cross):
+    dq [B,S,Hq,D] bf16, dk/dv [B,Skv,Hkv,D] fp32 from the forward's out and
+    lse and the output gradient dout."""
+    import torch
+    for t, n in ((q, "q"), (out, "out"), (dout, "dout")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    _need(lo, "lo", torch.int32, 2)
+    _need(hi, "hi", torch.int32, 2)
+    B, S, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if tuple(out.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("out and dout must match q")
+    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k and v must be [B, Skv, Hkv, D] matching q")
+    if tuple(lo.shape) != (B, S) or tuple(hi.shape) != (B, S):
+        raise ValueError("lo and hi must be [B, S]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=torch.float32, device=k.device)
+    if dv is None:
+        dv = torch.empty(k.shape, dtype=torch.float32, device=k.device)
+    _need(dq, "dq", torch.bfloat16, 4)
+    _need(dk, "dk", torch.float32, 4)
+    _need(dv, "dv", torch.float32, 4)
+    need = lib().docmask_gqa_bwd_cross_workspace_size(B, S, Skv, Hq, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    rc = lib().docmask_gqa_attn_bwd_cross(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(lo), _ptr(hi), B, S,
+        Skv, Hq, Hkv, D, float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != DMGQA_OK:
+        raise DocmaskGQAError(rc, "docmask_gqa_attn_bwd_cross")
+    return dq, dk, dv
 
 
 def docmask_gqa_check_cross_intervals(lo, hi, Skv: int, stream=None) -> int:

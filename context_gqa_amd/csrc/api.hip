@@ -54,6 +54,11 @@ int check_shape(int B, int S, int Skv, int Hq, int Hkv, int D, int cp, int rank,
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// The kernels track the running maximum of the raw scores and rescale only
+// when it grows, which assumes the scale is positive; a finite positive
+// scale is required.
+bool scale_ok(float x) { return std::isfinite(x) && x > 0.f; }
+
 int check_docs_args(const int32_t* doc_ids, const int32_t* cu, int n_docs, const Shape& s) {
   if ((doc_ids == nullptr) == (cu == nullptr)) return DMGQA_ERR_INVALID_ARG;
   if (doc_ids && !aligned(doc_ids, 4)) return DMGQA_ERR_INVALID_ARG;
@@ -64,18 +69,24 @@ int check_docs_args(const int32_t* doc_ids, const int32_t* cu, int n_docs, const
   return DMGQA_OK;
 }
 
-// Workspace layout.
+// Workspace layout.  Up to total_min: what every backward path needs (the
+// bounds, the schedule, the row statistics and the partial-sum slots); the
+// dS stash and the partial dQ buffer follow (see plan_stash).
 struct Layout {
-  size_t dstart, dend, agg, order, rowstat, hdr, tile_info, items, tile_rows, partial, stash,
-      total_min, total;
+  size_t dstart, dend, agg, order, rowstat, hdr, tile_info, items, tile_rows, partial,
+      total_min;
   int nkt, max_split_base;
-  int stash_kvh_blocks;   // stash blocks reserved per KV head
 };
 
+// Default budget of the dS stash (all KV heads together) in the workspace
+// that docmask_gqa_bwd_workspace_size asks for.
+constexpr long long kDefaultStashBudget = 2LL << 30;
+
 // Upper bound, over all document layouts, of the dS stash blocks of one KV
-// head: a key tile starting at t0 reaches at most the local tokens with
-// positions in [t0, S), a contiguous range [tlo, thi) of local tokens, i.e.
-// query rows [tlo*G, thi*G) covered by blocks of kStashRows rows.
+// head for the shape's rank and Skv: a key tile starting at t0 reaches at
+// most the local tokens with positions in [t0, S), a contiguous range
+// [tlo, thi) of local tokens, i.e. query rows [tlo*G, thi*G) covered by
+// blocks of kStashRows rows.
 long long stash_blocks_bound(const Shape& s, int nkt) {
   const long long baseA = (long long)s.rank * s.c;
   const long long baseB = (long long)(2 * s.cp - 1 - s.rank) * s.c;
@@ -90,6 +101,21 @@ long long stash_blocks_bound(const Shape& s, int nkt) {
     if (thi > tlo) total += (thi * s.G + kStashRows - 1) / kStashRows - tlo * s.G / kStashRows;
   }
   return total * s.B;
+}
+
+// The same bound for any rank that may pass this Skv (the size queries take
+// no rank): the maximum over those ranks, or, for more than 64 ranks, every
+// key tile reaching every local row.
+long long stash_blocks_any_rank(Shape s, int nkt) {
+  if (s.cp > 64)
+    return (long long)s.B * nkt * (((long long)s.Sq * s.G + kStashRows - 1) / kStashRows + 1);
+  long long m = 0;
+  for (int r = 0; r < s.cp; ++r) {
+    if ((long long)(2 * s.cp - r) * s.c > s.Skv) continue;   // needs a longer K/V prefix
+    s.rank = r;
+    m = std::max(m, stash_blocks_bound(s, nkt));
+  }
+  return m;
 }
 
 Layout layout(const Shape& s, bool backward) {
@@ -114,20 +140,70 @@ Layout layout(const Shape& s, bool backward) {
     L.tile_rows = off; off = align_up(off + ntiles * sizeof(int4));
     const size_t slots = 2 * (size_t)L.max_split_base * s.Hkv;
     L.partial = off; off = align_up(off + slots * 2 * kDkdvBN * s.D * sizeof(float));
-    L.total_min = off;
-    const long long blocks = stash_blocks_bound(s, L.nkt);
-    // the dK/dV kernel addresses one tile's stash with 32-bit byte offsets
-    // below 2^31 (a tile holds at most ceil(Sq*G/32) + 1 blocks)
-    const long long tile_bytes =
-        ((long long)s.Sq * s.G / kStashRows + 2) * (long long)kStashBlockBytes;
-    L.stash_kvh_blocks = blocks < (1LL << 31) && tile_bytes < (1LL << 31) ? (int)blocks : -1;
-    L.stash = off;
-    if (L.stash_kvh_blocks >= 0)
-      off = align_up(off + (size_t)blocks * s.Hkv * kStashBlockBytes);
   }
-  L.total = off;
-  if (!backward) L.total_min = off;
+  L.total_min = off;
   return L;
+}
+
+// How the backward forms dQ, from the workspace it was given:
+//  - kStash: the dS stash holds every key tile the rank's layout can reach
+//    (the worst-case bound fits); dQ is one product per key tile.
+//  - kMixed: a stash of `budget` blocks per KV head (at least one) plus an
+//    fp32 partial-dQ buffer; key tiles are stashed in order while they fit,
+//    and the query tiles that reach the rest recompute those tiles' share.
+//  - kRecompute: no stash; dQ recomputes S, P and dP for every key tile.
+enum StashMode { kRecompute = 0, kStash = 1, kMixed = 2 };
+struct StashPlan {
+  StashMode mode;
+  size_t stash, dq_part;   // byte offsets in the workspace
+  int budget;              // stash blocks per KV head
+};
+
+size_t dq_part_bytes(const Shape& s) {
+  return align_up((size_t)s.B * s.Sq * s.Hq * s.D * sizeof(float));
+}
+
+// The dK/dV kernel addresses one tile's stash with 32-bit byte offsets (a
+// tile holds at most ceil(Sq*G/32) + 1 blocks).
+bool stash_addressable(const Shape& s) {
+  return ((long long)s.Sq * s.G / kStashRows + 2) * (long long)kStashBlockBytes < (1LL << 31);
+}
+
+StashPlan plan_stash(const Shape& s, const Layout& L, size_t workspace_bytes) {
+  StashPlan p{kRecompute, L.total_min, 0, 0};
+  if (!stash_addressable(s) || workspace_bytes <= L.total_min) return p;
+  const long long per_block = (long long)s.Hkv * kStashBlockBytes;
+  const long long bound = stash_blocks_bound(s, L.nkt);
+  const size_t avail = workspace_bytes - L.total_min;
+  if (bound < (1LL << 31) && (long long)avail >= bound * per_block) {
+    p.mode = kStash;
+    p.budget = (int)bound;
+    return p;
+  }
+  const size_t dqb = dq_part_bytes(s);
+  if (avail <= dqb) return p;
+  const long long blocks = std::min<long long>(
+      std::min<long long>((long long)(avail - dqb) / per_block, bound), (1LL << 31) - 1);
+  if (blocks < 1) return p;
+  p.mode = kMixed;
+  p.dq_part = L.total_min;
+  p.stash = L.total_min + dqb;
+  p.budget = (int)blocks;
+  return p;
+}
+
+// Workspace of the default backward: the whole worst-case stash if it fits in
+// kDefaultStashBudget, else that budget plus the partial-dQ buffer (or the
+// whole stash, if that is smaller).
+size_t default_bwd_bytes(const Shape& s, const Layout& L) {
+  if (!stash_addressable(s)) return L.total_min;
+  const long long per_block = (long long)s.Hkv * kStashBlockBytes;
+  const long long worst = stash_blocks_any_rank(s, L.nkt);
+  const size_t full = worst < (1LL << 31) ? L.total_min + align_up((size_t)(worst * per_block))
+                                          : SIZE_MAX;
+  if (worst * per_block <= kDefaultStashBudget) return full;
+  const long long blocks = std::min<long long>(kDefaultStashBudget / per_block, (1LL << 31) - 1);
+  return std::min(full, L.total_min + dq_part_bytes(s) + align_up((size_t)(blocks * per_block)));
 }
 
 Geo make_geo(const Shape& s, float scale) {
@@ -191,7 +267,7 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* doc_ids
   Shape s;
   int rc = check_shape(B, S, Skv, Hq, Hkv, D, cp_size, cp_rank, &s);
   if (rc != DMGQA_OK) return rc;
-  if (!std::isfinite(softmax_scale) || softmax_scale == 0.f) return DMGQA_ERR_INVALID_ARG;
+  if (!scale_ok(softmax_scale)) return DMGQA_ERR_INVALID_ARG;
   if (s.empty) return DMGQA_OK;
   if (!q || !k || !v || !out || !lse || !workspace) return DMGQA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
@@ -200,7 +276,7 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* doc_ids
   rc = check_mask_args(doc_ids, cu_seqlens, n_docs, bounds, s);
   if (rc != DMGQA_OK) return rc;
   const Layout L = layout(s, false);
-  if (workspace_bytes < L.total) return DMGQA_ERR_WORKSPACE;
+  if (workspace_bytes < L.total_min) return DMGQA_ERR_WORKSPACE;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
@@ -222,15 +298,28 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* doc_ids
   return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
 }
 
-// Shape of a cross-attention call: S query tokens (cp_size 1, so the local
-// rows are the S tokens in order) against Skv keys indexed on their own.
+// Shape of a cross-attention call: S query tokens against Skv keys indexed
+// on their own.  There is no context parallelism, so S may be any size: the
+// geometry is one "chunk" of c = S rows (the local row map is then the
+// identity) and no second chunk.
 int check_cross_shape(int B, int S, int Skv, int Hq, int Hkv, int D, Shape* s) {
-  int rc = check_shape(B, S, S, Hq, Hkv, D, 1, 0, s);
-  if (rc != DMGQA_OK) return rc;
-  if (Skv < 0 || (Skv == 0 && !s->empty)) return DMGQA_ERR_INVALID_ARG;
-  if ((long long)Skv * 2 >= (1LL << 31) || (long long)B * Skv * Hkv * D >= (1LL << 31))
+  if (B < 0 || S < 0 || Skv < 0 || Hq <= 0 || Hkv <= 0) return DMGQA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return DMGQA_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return DMGQA_ERR_UNSUPPORTED;
+  const bool empty = B == 0 || S == 0;
+  if (Skv == 0 && !empty) return DMGQA_ERR_INVALID_ARG;
+  const long long G = Hq / Hkv;
+  if ((long long)S * G >= (1LL << 30) || (long long)Skv * 2 >= (1LL << 31) ||
+      (long long)S * 2 >= (1LL << 31))
     return DMGQA_ERR_UNSUPPORTED;
-  s->Skv = Skv;
+  const long long tiles = ((long long)S * G + kFwdBM - 1) / kFwdBM * (long long)B * Hkv;
+  if (tiles >= (1LL << 31)) return DMGQA_ERR_UNSUPPORTED;
+  if ((long long)B * S * Hq * D >= (1LL << 31) || (long long)B * Skv * Hkv * D >= (1LL << 31) ||
+      G >= (1 << 15))
+    return DMGQA_ERR_UNSUPPORTED;
+  s->B = B; s->S = S; s->Skv = Skv; s->Hq = Hq; s->Hkv = Hkv; s->D = D;
+  s->cp = 1; s->rank = 0; s->G = (int)G; s->c = S; s->Sq = S;
+  s->empty = empty;
   return DMGQA_OK;
 }
 
@@ -254,7 +343,7 @@ size_t docmask_gqa_fwd_workspace_size(int32_t B, int32_t S, int32_t Skv, int32_t
   if (check_shape(B, S, S, Hq, Hkv, D, cp_size, 0, &s) != DMGQA_OK) return 0;
   s.Skv = Skv > 0 && Skv <= S ? Skv : S;
   if (s.empty) return 0;
-  return layout(s, false).total;
+  return layout(s, false).total_min;
 }
 
 size_t docmask_gqa_bwd_workspace_size(int32_t B, int32_t S, int32_t Skv, int32_t Hq, int32_t Hkv,
@@ -263,7 +352,7 @@ size_t docmask_gqa_bwd_workspace_size(int32_t B, int32_t S, int32_t Skv, int32_t
   if (check_shape(B, S, S, Hq, Hkv, D, cp_size, 0, &s) != DMGQA_OK) return 0;
   s.Skv = Skv > 0 && Skv <= S ? Skv : S;
   if (s.empty) return 0;
-  return layout(s, true).total;
+  return default_bwd_bytes(s, layout(s, true));
 }
 
 size_t docmask_gqa_bwd_workspace_size_min(int32_t B, int32_t S, int32_t Skv, int32_t Hq,
@@ -273,6 +362,33 @@ size_t docmask_gqa_bwd_workspace_size_min(int32_t B, int32_t S, int32_t Skv, int
   s.Skv = Skv > 0 && Skv <= S ? Skv : S;
   if (s.empty) return 0;
   return layout(s, true).total_min;
+}
+
+int docmask_gqa_bwd_path(int32_t B, int32_t S, int32_t Skv, int32_t Hq, int32_t Hkv, int32_t D,
+                         int32_t cp_size, int32_t cp_rank, size_t workspace_bytes) {
+  Shape s;
+  const int rc = check_shape(B, S, Skv, Hq, Hkv, D, cp_size, cp_rank, &s);
+  if (rc != DMGQA_OK) return rc;
+  if (s.empty) return DMGQA_BWD_PATH_RECOMPUTE;
+  const Layout L = layout(s, true);
+  if (workspace_bytes < L.total_min) return DMGQA_ERR_WORKSPACE;
+  switch (plan_stash(s, L, workspace_bytes).mode) {
+    case kStash: return DMGQA_BWD_PATH_STASH;
+    case kMixed: return DMGQA_BWD_PATH_MIXED;
+    default: return DMGQA_BWD_PATH_RECOMPUTE;
+  }
+}
+
+size_t docmask_gqa_bwd_workspace_size_full(int32_t B, int32_t S, int32_t Skv, int32_t Hq,
+                                           int32_t Hkv, int32_t D, int32_t cp_size) {
+  Shape s;
+  if (check_shape(B, S, S, Hq, Hkv, D, cp_size, 0, &s) != DMGQA_OK) return 0;
+  s.Skv = Skv > 0 && Skv <= S ? Skv : S;
+  if (s.empty) return 0;
+  const Layout L = layout(s, true);
+  const long long worst = stash_blocks_any_rank(s, L.nkt);
+  if (!stash_addressable(s) || worst >= (1LL << 31)) return L.total_min;
+  return L.total_min + align_up((size_t)worst * s.Hkv * kStashBlockBytes);
 }
 
 int docmask_gqa_attn_fwd(const void* q, const void* k, const void* v, const int32_t* doc_ids,
@@ -307,7 +423,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   Shape s;
   int rc = check_shape(B, S, Skv, Hq, Hkv, D, cp_size, cp_rank, &s);
   if (rc != DMGQA_OK) return rc;
-  if (!std::isfinite(softmax_scale) || softmax_scale == 0.f) return DMGQA_ERR_INVALID_ARG;
+  if (!scale_ok(softmax_scale)) return DMGQA_ERR_INVALID_ARG;
   if (s.empty) return DMGQA_OK;
   if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !workspace)
     return DMGQA_ERR_INVALID_ARG;
@@ -319,9 +435,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   if (rc != DMGQA_OK) return rc;
   const Layout L = layout(s, true);
   if (workspace_bytes < L.total_min) return DMGQA_ERR_WORKSPACE;
-  // With room for the dS stash the dK/dV kernel stores dS and dQ is one
-  // product per key tile; else dQ recomputes S, P and dP.
-  const bool use_stash = L.stash_kvh_blocks >= 0 && workspace_bytes >= L.total;
+  const StashPlan plan = plan_stash(s, L, workspace_bytes);
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
@@ -338,48 +452,123 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   int2* items = reinterpret_cast<int2*>(ws + L.items);
   int4* tile_rows = reinterpret_cast<int4*>(ws + L.tile_rows);
   float* partial = reinterpret_cast<float*>(ws + L.partial);
-  u16* stash = use_stash ? reinterpret_cast<u16*>(ws + L.stash) : nullptr;
   int32_t* dq_order = reinterpret_cast<int32_t*>(ws + L.order);
   const u16* qh = static_cast<const u16*>(q);
   const u16* kh = static_cast<const u16*>(k);
   const u16* vh = static_cast<const u16*>(v);
   const u16* oh = static_cast<const u16*>(out);
   const u16* doh = static_cast<const u16*>(dout);
+  u16* dqh = static_cast<u16*>(dq);
 
   hipError_t e;
-  if (use_stash) {
+  if (plan.mode != kRecompute) {
+    // The dK/dV kernel stores dS of the stashed key tiles; dQ is then one
+    // product per stashed key tile, and (mixed) the query tiles that also
+    // reach key tiles beyond the budget recompute those tiles' share.
+    u16* stash = reinterpret_cast<u16*>(ws + plan.stash);
+    float* dq_part =
+        plan.mode == kMixed ? reinterpret_cast<float*>(ws + plan.dq_part) : nullptr;
     timing_begin(kKSchedRowstat, st);
-    e = launch_sched_rowstat(D, dstart, dend, g, L.nkt, L.max_split_base, hdr, tile_info, items,
-                             tile_rows, dq_order, oh, doh, lse, Lbuf, Nbuf, st);
+    e = launch_sched_rowstat(D, dstart, dend, g, L.nkt, L.max_split_base, plan.budget, hdr,
+                             tile_info, items, tile_rows, dq_order, oh, doh, lse, Lbuf, Nbuf,
+                             st);
     timing_end(kKSchedRowstat, st);
     if (e != hipSuccess) return DMGQA_ERR_HIP;
     timing_begin(kKDkdv, st);
-    e = launch_bwd_dkdv(D, qh, kh, vh, doh, Lbuf, Nbuf, dend, hdr, tile_info, items, tile_rows,
-                        stash, L.stash_kvh_blocks, partial, dk, dv, g, L.nkt, st);
+    e = launch_bwd_dkdv(D, qh, kh, vh, doh, Lbuf, Nbuf, nullptr, dend, hdr, tile_info, items,
+                        tile_rows, stash, plan.budget, partial, dk, dv, g, L.nkt, st);
     timing_end(kKDkdv, st);
     if (e != hipSuccess) return DMGQA_ERR_HIP;
     timing_begin(kKDq, st);
-    e = launch_bwd_dq_stash(D, kh, dstart, tile_rows, stash, L.stash_kvh_blocks, dq_order,
-                            static_cast<u16*>(dq), tile_info, partial, dk, dv, g, L.nkt, st);
+    e = launch_bwd_dq_stash(D, kh, dstart, tile_rows, stash, plan.budget, dq_order, dqh, dq_part,
+                            tile_info, partial, dk, dv, g, L.nkt, st);
     timing_end(kKDq, st);
+    if (e != hipSuccess || plan.mode == kStash) return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
+    timing_begin(kKDqRest, st);
+    e = launch_bwd_dq(D, qh, kh, vh, oh, doh, lse, dstart, nullptr, dqh, nullptr, nullptr,
+                      tile_rows, dq_part, g, L.nkt, st);
+    timing_end(kKDqRest, st);
     return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
-  } else {
-    timing_begin(kKSched, st);
-    e = launch_sched_dkdv(dend, g, L.nkt, L.max_split_base, hdr, tile_info, items, tile_rows,
-                          st);
-    timing_end(kKSched, st);
-    if (e != hipSuccess) return DMGQA_ERR_HIP;
-    timing_begin(kKDq, st);
-    e = launch_bwd_dq(D, qh, kh, vh, oh, doh, lse, dstart, static_cast<u16*>(dq), Lbuf, Nbuf, g,
-                      st);
-    timing_end(kKDq, st);
-    if (e != hipSuccess) return DMGQA_ERR_HIP;
-    timing_begin(kKDkdv, st);
-    e = launch_bwd_dkdv(D, qh, kh, vh, doh, Lbuf, Nbuf, dend, hdr, tile_info, items, tile_rows,
-                        nullptr, 0, partial, dk, dv, g, L.nkt, st);
-    timing_end(kKDkdv, st);
-    if (e != hipSuccess) return DMGQA_ERR_HIP;
   }
+  timing_begin(kKSched, st);
+  e = launch_sched_dkdv(nullptr, dend, g, L.nkt, L.max_split_base, 0, hdr, tile_info, items,
+                        tile_rows, st);
+  timing_end(kKSched, st);
+  if (e != hipSuccess) return DMGQA_ERR_HIP;
+  timing_begin(kKDq, st);
+  e = launch_bwd_dq(D, qh, kh, vh, oh, doh, lse, dstart, nullptr, dqh, Lbuf, Nbuf, tile_rows,
+                    nullptr, g, L.nkt, st);
+  timing_end(kKDq, st);
+  if (e != hipSuccess) return DMGQA_ERR_HIP;
+  timing_begin(kKDkdv, st);
+  e = launch_bwd_dkdv(D, qh, kh, vh, doh, Lbuf, Nbuf, nullptr, dend, hdr, tile_info, items,
+                      tile_rows, nullptr, 0, partial, dk, dv, g, L.nkt, st);
+  timing_end(kKDkdv, st);
+  if (e != hipSuccess) return DMGQA_ERR_HIP;
+  timing_begin(kKReduce, st);
+  e = launch_bwd_reduce(D, tile_info, partial, dk, dv, g, L.nkt, st);
+  timing_end(kKReduce, st);
+  return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
+}
+
+// Cross-attention backward (recompute path): key ranges from lo / hi, the
+// schedule, dQ recomputing the scores (it also stores the row statistics),
+// dK/dV, and the sum of the split tiles' partial slots.
+int bwd_cross_impl(const void* q, const void* k, const void* v, const void* out,
+                   const void* dout, const float* lse, const int32_t* lo, const int32_t* hi,
+                   int32_t B, int32_t S, int32_t Skv, int32_t Hq, int32_t Hkv, int32_t D,
+                   float softmax_scale, void* dq, float* dk, float* dv, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  Shape s;
+  int rc = check_cross_shape(B, S, Skv, Hq, Hkv, D, &s);
+  if (rc != DMGQA_OK) return rc;
+  if (!scale_ok(softmax_scale)) return DMGQA_ERR_INVALID_ARG;
+  if (s.empty) return DMGQA_OK;
+  if (!q || !k || !v || !out || !dout || !lse || !lo || !hi || !dq || !dk || !dv || !workspace)
+    return DMGQA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(lse, 4) || !aligned(lo, 4) ||
+      !aligned(hi, 4) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 16))
+    return DMGQA_ERR_INVALID_ARG;
+  const Layout L = layout(s, true);
+  if (workspace_bytes < L.total_min) return DMGQA_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  // per key: the first query position that reaches it and one past the last
+  int32_t* kfirst = reinterpret_cast<int32_t*>(ws + L.dstart);
+  int32_t* kend = reinterpret_cast<int32_t*>(ws + L.dend);
+  float* Lbuf = reinterpret_cast<float*>(ws + L.rowstat);
+  float* Nbuf = Lbuf + (size_t)s.B * s.Sq * s.Hq;
+  SchedHeader* hdr = reinterpret_cast<SchedHeader*>(ws + L.hdr);
+  int2* tile_info = reinterpret_cast<int2*>(ws + L.tile_info);
+  int2* items = reinterpret_cast<int2*>(ws + L.items);
+  int4* tile_rows = reinterpret_cast<int4*>(ws + L.tile_rows);
+  float* partial = reinterpret_cast<float*>(ws + L.partial);
+  const u16* qh = static_cast<const u16*>(q);
+  const u16* kh = static_cast<const u16*>(k);
+  const u16* vh = static_cast<const u16*>(v);
+  const Geo g = make_geo(s, softmax_scale);
+
+  timing_begin(kKPrep, st);
+  hipError_t e = launch_prep_cross_keys(lo, hi, s.B, s.S, s.Skv, kfirst, kend, st);
+  timing_end(kKPrep, st);
+  if (e != hipSuccess) return DMGQA_ERR_HIP;
+  timing_begin(kKSched, st);
+  e = launch_sched_dkdv(kfirst, kend, g, L.nkt, L.max_split_base, 0, hdr, tile_info, items,
+                        tile_rows, st);
+  timing_end(kKSched, st);
+  if (e != hipSuccess) return DMGQA_ERR_HIP;
+  timing_begin(kKDq, st);
+  e = launch_bwd_dq(D, qh, kh, vh, static_cast<const u16*>(out), static_cast<const u16*>(dout),
+                    lse, lo, hi, static_cast<u16*>(dq), Lbuf, Nbuf, tile_rows, nullptr, g, L.nkt,
+                    st);
+  timing_end(kKDq, st);
+  if (e != hipSuccess) return DMGQA_ERR_HIP;
+  timing_begin(kKDkdv, st);
+  e = launch_bwd_dkdv(D, qh, kh, vh, static_cast<const u16*>(dout), Lbuf, Nbuf, kfirst, kend, hdr,
+                      tile_info, items, tile_rows, nullptr, 0, partial, dk, dv, g, L.nkt, st);
+  timing_end(kKDkdv, st);
+  if (e != hipSuccess) return DMGQA_ERR_HIP;
   timing_begin(kKReduce, st);
   e = launch_bwd_reduce(D, tile_info, partial, dk, dv, g, L.nkt, st);
   timing_end(kKReduce, st);
@@ -470,7 +659,7 @@ int docmask_gqa_attn_fwd_cross(const void* q, const void* k, const void* v, cons
   Shape s;
   int rc = check_cross_shape(B, S, Skv, Hq, Hkv, D, &s);
   if (rc != DMGQA_OK) return rc;
-  if (!std::isfinite(softmax_scale) || softmax_scale == 0.f) return DMGQA_ERR_INVALID_ARG;
+  if (!scale_ok(softmax_scale)) return DMGQA_ERR_INVALID_ARG;
   if (s.empty) return DMGQA_OK;
   if (!q || !k || !v || !lo || !hi || !out || !lse || !workspace) return DMGQA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
@@ -489,6 +678,23 @@ int docmask_gqa_attn_fwd_cross(const void* q, const void* k, const void* v, cons
                  static_cast<const u16*>(v), lo, hi, order, static_cast<u16*>(out), lse, g, st);
   timing_end(kKFwd, st);
   return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
+}
+
+size_t docmask_gqa_bwd_cross_workspace_size(int32_t B, int32_t S, int32_t Skv, int32_t Hq,
+                                            int32_t Hkv, int32_t D) {
+  Shape s;
+  if (check_cross_shape(B, S, Skv, Hq, Hkv, D, &s) != DMGQA_OK || s.empty) return 0;
+  return layout(s, true).total_min;
+}
+
+int docmask_gqa_attn_bwd_cross(const void* q, const void* k, const void* v, const void* out,
+                               const void* dout, const float* lse, const int32_t* lo,
+                               const int32_t* hi, int32_t B, int32_t S, int32_t Skv, int32_t Hq,
+                               int32_t Hkv, int32_t D, float softmax_scale, void* dq, float* dk,
+                               float* dv, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return bwd_cross_impl(q, k, v, out, dout, lse, lo, hi, B, S, Skv, Hq, Hkv, D, softmax_scale, dq,
+                        dk, dv, workspace, workspace_bytes, stream);
 }
 
 int docmask_gqa_check_cross_intervals(const int32_t* lo, const int32_t* hi, int32_t B, int32_t S,

@@ -16,7 +16,9 @@
 //
 // Two kernels here (the dK/dV kernel has its own file):
 //   bwd_dq    query-stationary, same tiling as the forward; it also stores
-//             -D and -lse/scale per row for the dK/dV kernel.
+//             -D and -lse/scale per row for the dK/dV kernel (recompute
+//             path), and finishes the query tiles the dS stash does not
+//             cover (stash with a budget).
 //   bwd_reduce adds the partial sums of split key tiles in item order, so the
 //             result does not depend on which workgroup ran which item.
 #include "common.hpp"
@@ -27,12 +29,19 @@
 
 namespace dmgqa {
 
-template <int D>
+// CROSS: query position p reaches keys dstart[p] .. dhi[p]-1 (both [B, S]);
+// else keys dstart[p] .. p (dstart [B, Skv]).
+// Mixed stash mode (dq_part != null): only query tiles whose last 128-key
+// tile has no stash run (the same test as the stash kernel, which then left
+// its unscaled sums in dq_part), over the 64-key tiles whose 128-key tile
+// has no stash, starting from dq_part.
+template <int D, bool CROSS>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ out, const u16* __restrict__ dout, const float* __restrict__ lse,
-    const int32_t* __restrict__ dstart, u16* __restrict__ dq, float* __restrict__ Lbuf,
-    float* __restrict__ Nbuf, Geo g) {
+    const int32_t* __restrict__ dstart, const int32_t* __restrict__ dhi, u16* __restrict__ dq,
+    float* __restrict__ Lbuf, float* __restrict__ Nbuf, const int4* __restrict__ tile_rows,
+    const float* __restrict__ dq_part, Geo g, int nkt) {
   constexpr int BM = kFwdBM, BN = kFwdBN, LD = D, KK = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) u16 sK[2][BN * LD];
   __shared__ __attribute__((aligned(16))) u16 sV[2][BN * LD];
@@ -47,14 +56,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const int h = lane >> 5, i = lane & 31;
 
   const int row0 = tile * BM;
+  const int32_t* ds = dstart + (size_t)b * (CROSS ? g.S : g.Skv);
+  const int32_t* dh = CROSS ? dhi + (size_t)b * g.S : nullptr;
+  const int4* trow_b = tile_rows + (size_t)b * nkt;
+  if (dq_part != nullptr) {
+    const QTileKeys k2 = qtile_keys<BM, kDkdvBN>(row0, ds, g);
+    const int kt_last = k2.nb > 0 ? k2.b0 + k2.nb - 1 : k2.a0 + k2.na - 1;
+    if (k2.na + k2.nb == 0 || trow_b[kt_last].w >= 0) return;
+  }
   const int row = row0 + wave * 32 + i;
   const bool valid = row < nrows;
   const int rr = valid ? row : nrows - 1;
   const int tok = rr / g.G;
   const int head = kvh * g.G + rr % g.G;
   const int pos = local_pos(tok, g.c, g.cp, g.rank);
-  const int32_t* ds = dstart + (size_t)b * g.Skv;
   const int lo = ds[pos];
+  // last key this row reaches
+  const int last = CROSS ? dh[pos] - 1 : pos;
 
   const size_t roff = ((size_t)b * g.Sq + tok) * g.Hq + head;
   const size_t qoff = roff * D;
@@ -70,18 +88,32 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   }
   const float Dv = dsum + xor32(dsum);
   const float lse_v = lse[roff];
-  if (valid && h == 0) {   // row statistics for the dK/dV kernel
+  if (Lbuf != nullptr && valid && h == 0) {   // row statistics for the dK/dV kernel
     Nbuf[roff] = -Dv;
     Lbuf[roff] = -lse_v / g.scale;
   }
   const float lse2 = lse_v * kLog2e;
 
-  const QTileKeys kr = qtile_keys<BM, BN>(row0, ds, g);
+  const QTileKeys kr =
+      CROSS ? qtile_keys_iv<BM, BN>(row0, ds, dh, g) : qtile_keys<BM, BN>(row0, ds, g);
   const int ntiles = kr.na + kr.nb;
 
+  // accumulator layout: register r of d block db holds column
+  // 32 db + 8 (r / 4) + 4 h + r % 4 of this lane's row
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = zero16();
+  if (dq_part != nullptr) {
+    const float* prow = dq_part + qoff;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(prow + 32 * db + 8 * r4 + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[db][4 * r4 + e] = w[e];
+      }
+  }
 
   const size_t kvstride = (size_t)g.Hkv * D;
   const u16* kbase = k + (size_t)b * g.Skv * kvstride + (size_t)kvh * D;
@@ -104,8 +136,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const u16* cK = sK[cur];
     const u16* cV = sV[cur];
 
-    const bool full = kr.max_lo <= t0 && t0 + BN - 1 <= kr.min_pos;
+    // in mixed stash mode the stash kernel has covered the stashed tiles
+    const bool skip = dq_part != nullptr && trow_b[t0 / kDkdvBN].w >= 0;
+    const bool full = qtile_full(kr, t0, BN);
     // two 32-key halves, to keep the score/dP accumulators at 32 registers
+    if (!skip) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       f32x16 s0 = zero16(), p0 = zero16();
@@ -119,7 +154,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         float e0 = __builtin_amdgcn_exp2f(fmaf(s0[r], g.scale_log2, -lse2));
         if (!full) {
           const int kv = t0 + 32 * half + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (kv < lo || kv > pos) e0 = 0.f;
+          if (kv < lo || kv > last) e0 = 0.f;
         }
         s0[r] = e0 * (p0[r] - Dv);
       }
@@ -130,6 +165,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         for (int db = 0; db < DB; ++db)
           acc[db] = mfma32(tr_operand<D>(cK, 0, 2 * half + kh, 32 * db, lane), dsop, acc[db]);
       }
+    }
     }
     if (it + 1 < ntiles) {
       rk.store(sK[cur ^ 1]);
@@ -162,14 +198,21 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const int2* __restrict_
 }
 
 hipError_t launch_bwd_dq(int D, const u16* q, const u16* k, const u16* v, const u16* out,
-                         const u16* dout, const float* lse, const int32_t* dstart, u16* dq,
-                         float* Lbuf, float* Nbuf, const Geo& g, hipStream_t st) {
+                         const u16* dout, const float* lse, const int32_t* dstart,
+                         const int32_t* dhi, u16* dq, float* Lbuf, float* Nbuf,
+                         const int4* tile_rows, const float* dq_part, const Geo& g, int nkt,
+                         hipStream_t st) {
   const int nt = (g.Sq * g.G + kFwdBM - 1) / kFwdBM;
   const unsigned grid = (unsigned)nt * g.B * g.Hkv;
-  if (D == 128)
-    bwd_dq_kernel<128><<<grid, 256, 0, st>>>(q, k, v, out, dout, lse, dstart, dq, Lbuf, Nbuf, g);
-  else
-    bwd_dq_kernel<64><<<grid, 256, 0, st>>>(q, k, v, out, dout, lse, dstart, dq, Lbuf, Nbuf, g);
+#define DMGQA_DQ(DD, CC)                                                                     \
+  bwd_dq_kernel<DD, CC><<<grid, 256, 0, st>>>(q, k, v, out, dout, lse, dstart, dhi, dq, Lbuf, \
+                                              Nbuf, tile_rows, dq_part, g, nkt)
+  if (D == 128) {
+    if (dhi) DMGQA_DQ(128, true); else DMGQA_DQ(128, false);
+  } else {
+    if (dhi) DMGQA_DQ(64, true); else DMGQA_DQ(64, false);
+  }
+#undef DMGQA_DQ
   return hipGetLastError();
 }
 

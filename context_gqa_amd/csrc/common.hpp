@@ -16,6 +16,8 @@
 #include <stdint.h>
 #include <type_traits>
 
+#include "index.hpp"
+
 namespace dmgqa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -171,20 +173,6 @@ __device__ __forceinline__ void sched_reads_ahead() {
   }
   __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
 }
-
-// Global position of local row j (chunk layout of the rank).
-__device__ __forceinline__ int local_pos(int j, int c, int cp, int rank) {
-  return j < c ? rank * c + j : (2 * cp - 1 - rank) * c + (j - c);
-}
-
-// Per-call geometry shared by every kernel.
-struct Geo {
-  int B, S, Skv, Hq, Hkv, G, Sq, c, cp, rank;
-  int g_log2;        // log2(G) if G is a power of two, else -1
-  unsigned g_magic;  // ceil(2^32 / G) for G >= 2 (see div_small)
-  float scale;       // softmax scale
-  float scale_log2;  // scale * log2(e)
-};
 
 // x / G and x % G (x >= 0); shifts when G is a power of two.
 __device__ __forceinline__ int div_g(int x, const Geo& g) {

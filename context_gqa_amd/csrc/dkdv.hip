@@ -128,21 +128,6 @@ __device__ __forceinline__ bf16x8 tr_pair(const char* p) {
 
 }  // namespace
 
-// Token ranges of the query rows that reach key tile kt (same rule as the
-// scheduler): positions [t0, dend(last key of the tile)).
-__device__ __forceinline__ void dkdv_ranges(const int32_t* dend_b, int kt, const Geo& g, int& a0,
-                                            int& na, int& b0, int& nb) {
-  const int t0 = kt * kDkdvBN;
-  const int tl = min(t0 + kDkdvBN - 1, g.Skv - 1);
-  const int p1 = dend_b[tl];
-  const int baseA = g.rank * g.c;
-  const int baseB = (2 * g.cp - 1 - g.rank) * g.c;
-  const int la = min(max(t0 - baseA, 0), g.c), ha = min(max(p1 - baseA, 0), g.c);
-  const int lb = min(max(t0 - baseB, 0), g.c), hb = min(max(p1 - baseB, 0), g.c);
-  a0 = la; na = max(0, ha - la);
-  b0 = g.c + lb; nb = max(0, hb - lb);
-}
-
 // STASH: also store dS (bf16) for the dQ product kernel.  Each wave's
 // 32 rows x 16 keys of dS are transposed through LDS (written key-major,
 // read with the transposed read) into one 16-byte chunk per lane: chunk
@@ -153,7 +138,8 @@ template <int D, bool STASH>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ dout, const float* __restrict__ Lbuf, const float* __restrict__ Nbuf,
-    const int32_t* __restrict__ dend, SchedHeader* __restrict__ hdr,
+    const int32_t* __restrict__ kfirst, const int32_t* __restrict__ dend,
+    SchedHeader* __restrict__ hdr,
     const int2* __restrict__ tile_info, const int2* __restrict__ items,
     const int4* __restrict__ tile_rows, u16* __restrict__ stash, int stash_kvh_blocks,
     float* __restrict__ partial, float* __restrict__ dk, float* __restrict__ dv, Geo g, int nkt) {
@@ -210,8 +196,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const int b = x / nkt, kt = x % nkt;
     const int t0 = kt * BN;
     const int32_t* de = dend + (size_t)b * g.Skv;
+    const int32_t* kf = kfirst ? kfirst + (size_t)b * g.Skv : nullptr;
     int a0, na, b0, nb;
-    dkdv_ranges(de, kt, g, a0, na, b0, nb);
+    key_tile_tokens(kf, de, kt, g, a0, na, b0, nb);
     const int rows_total = (na + nb) * g.G;
     const int r_begin = split * rps;
     const int r_end = min(r_begin + rps, rows_total);
@@ -230,24 +217,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       vop[ks] = ld_bf16x8(vrow + 32 * ks + 8 * g4);
     }
 
-    // Rows allowed for this key: local tokens with position in
-    // [key, dend(key)), a contiguous run [ti_lo, ti_hi) of the tile's token
-    // list (run A then run B, positions increasing), i.e. virtual rows
-    // [G*ti_lo, G*ti_hi), clipped to the item's rows.  Both ends grow with
-    // the key, so the wave's common range is [lo of its last key, hi of its
-    // first key).
-    int vr_lo = r_end, vr_hi = r_end;
-    {
-      const int A = g.rank * g.c + a0;
-      const int Bb = (2 * g.cp - 1 - g.rank) * g.c + (b0 - g.c);
-      if (key < g.Skv) {
-        const int e = de[key];
-        const int ti_lo = min(max(key - A, 0), na) + min(max(key - Bb, 0), nb);
-        const int ti_hi = min(max(e - A, 0), na) + min(max(e - Bb, 0), nb);
-        vr_lo = min(max(ti_lo * g.G, r_begin), r_end);
-        vr_hi = min(max(ti_hi * g.G, r_begin), r_end);
-      }
-    }
+    // Rows allowed for this key (key_rows: a contiguous range of the item's
+    // virtual rows).  Both ends grow with the key, so the wave's common
+    // range is [lo of its last key, hi of its first key).
+    int vr_lo, vr_hi;
+    key_rows(key, kf, de, a0, na, b0, nb, g, r_begin, r_end, vr_lo, vr_hi);
     const int w_lo = __builtin_amdgcn_readlane(vr_lo, kWaveKeys - 1);
     const int w_hi = __builtin_amdgcn_readlane(vr_hi, 0);
 
@@ -329,13 +303,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     // Stores go through a buffer resource spanning exactly the tile's
     // blocks: a lane whose row lies past the item's end gets an offset
     // beyond that range, which the hardware drops (no divergent branch).
+    // A tile left out of the stash (trow.w < 0: its blocks did not fit in
+    // the budget) gets an empty range, so its stores are all dropped.
     const int4 trow = tile_rows[x];
-    const int tr_z = uniform(trow.z), tr_x = uniform(trow.x);
-    const int tile_blocks = uniform((trow.y * g.G + kStashRows - 1) / kStashRows - trow.z);
+    const int tr_z = uniform(trow.z), tr_x = uniform(trow.x), tr_w = uniform(trow.w);
+    const int tile_blocks =
+        tr_w >= 0 ? uniform((trow.y * g.G + kStashRows - 1) / kStashRows - trow.z) : 0;
     __amdgpu_buffer_rsrc_t srs;
     if constexpr (STASH)
       srs = __builtin_amdgcn_make_buffer_rsrc(
-          stash + ((size_t)kvh * stash_kvh_blocks + uniform(trow.w)) * (kStashBlockBytes / 2), 0,
+          stash + ((size_t)kvh * stash_kvh_blocks + max(tr_w, 0)) * (kStashBlockBytes / 2), 0,
           tile_blocks * kStashBlockBytes, 0x00020000);
     // (1) dS to this wave's transpose scratch, key-major: lane (g4, j) holds
     // key j at rows 16t + 4*g4 + 0..3.
@@ -542,14 +519,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 }
 
 hipError_t launch_bwd_dkdv(int D, const u16* q, const u16* k, const u16* v, const u16* dout,
-                           const float* Lbuf, const float* Nbuf, const int32_t* dend,
-                           SchedHeader* hdr, const int2* tile_info, const int2* items,
+                           const float* Lbuf, const float* Nbuf, const int32_t* kfirst,
+                           const int32_t* dend, SchedHeader* hdr, const int2* tile_info, const int2* items,
                            const int4* tile_rows, u16* stash, int stash_kvh_blocks,
                            float* partial, float* dk, float* dv, const Geo& g, int nkt,
                            hipStream_t st) {
 #define DMGQA_DKDV(DD, SS)                                                                  \
   bwd_dkdv_kernel<DD, SS><<<kDkdvGrid, kWaves * 64, 0, st>>>(                               \
-      q, k, v, dout, Lbuf, Nbuf, dend, hdr, tile_info, items, tile_rows, stash,             \
+      q, k, v, dout, Lbuf, Nbuf, kfirst, dend, hdr, tile_info, items, tile_rows, stash,             \
       stash_kvh_blocks, partial, dk, dv, g, nkt)
   if (D == 128) {
     if (stash) DMGQA_DKDV(128, true); else DMGQA_DKDV(128, false);

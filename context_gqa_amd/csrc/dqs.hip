@@ -75,7 +75,8 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
     const u16* __restrict__ k, const int32_t* __restrict__ dstart,
     const int4* __restrict__ tile_rows, const u16* __restrict__ stash, int stash_kvh_blocks,
-    const int32_t* __restrict__ order, u16* __restrict__ dq, const int2* __restrict__ tile_info, const float* __restrict__ partial,
+    const int32_t* __restrict__ order, u16* __restrict__ dq, float* __restrict__ dq_part,
+    const int2* __restrict__ tile_info, const float* __restrict__ partial,
     float* __restrict__ dk, float* __restrict__ dv, Geo g, int nkt, int dq_grid) {
   if ((int)blockIdx.x >= dq_grid) {
     reduce_partials<D>(tile_info, partial, dk, dv, g, nkt, (int)blockIdx.x - dq_grid);
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
     d.in = it < ntiles;
     const int nblk = tr.y > tr.x ? (tr.y * g.G + kStashRows - 1) / kStashRows - tr.z : 0;
     const int rel = J - tr.z;
-    const bool have = d.in && rel >= 0 && rel < nblk;
+    const bool have = d.in && tr.w >= 0 && rel >= 0 && rel < nblk;
     // one block through a buffer resource (wave-uniform base) and a fixed
     // per-lane offset; non-temporal (the stash is read once: keeping it out
     // of the caches took the kernel from 138 to 117 us on the 405B share)
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
     const int4 tr = dc.tr;
     const int nblk = tr.y > tr.x ? (tr.y * g.G + kStashRows - 1) / kStashRows - tr.z : 0;
     const int rel = J - tr.z;
-    const bool have = dc.in && rel >= 0 && rel < nblk;
+    const bool have = dc.in && tr.w >= 0 && rel >= 0 && rel < nblk;
     // rows of the block outside the tile's reach: never written, zeroed here
     const bool part = !(tr.x * g.G <= 32 * J && 32 * J + 32 <= tr.y * g.G);
     const bool ok = grow >= tr.x * g.G && grow < tr.y * g.G;
@@ -241,7 +242,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
     wait_vmcnt<0>();
   }
 
-  if (grow < nrows) {
+  // Stashed tiles are a prefix in (batch row, key tile) order, so the
+  // query tile reaches a tile without stash iff its last key tile has none;
+  // then the recompute kernel adds those tiles' share to the unscaled fp32
+  // sums left here and writes dq.
+  const int kt_last = kr.nb > 0 ? kr.b0 + kr.nb - 1 : kr.a0 + kr.na - 1;
+  const bool mixed = dq_part != nullptr && ntiles > 0 && trow_b[kt_last].w < 0;
+  if (mixed) {
+    if (grow < nrows) {
+      const int tok = grow / g.G, hh = grow - tok * g.G;
+      float* prow = dq_part + (((size_t)b * g.Sq + tok) * g.Hq + kvh * g.G + hh) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 w = {acc[db][4 * r4], acc[db][4 * r4 + 1], acc[db][4 * r4 + 2],
+                           acc[db][4 * r4 + 3]};
+          *reinterpret_cast<f32x4*>(prow + 32 * db + 8 * r4 + 4 * h) = w;
+        }
+    }
+  } else if (grow < nrows) {
     const int tok = grow / g.G, hh = grow - tok * g.G;
     u16* orow = dq + (((size_t)b * g.Sq + tok) * g.Hq + kvh * g.G + hh) * D;
 #pragma unroll
@@ -258,18 +278,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
 
 hipError_t launch_bwd_dq_stash(int D, const u16* k, const int32_t* dstart, const int4* tile_rows,
                                const u16* stash, int stash_kvh_blocks, const int32_t* order,
-                               u16* dq, const int2* tile_info, const float* partial, float* dk,
-                               float* dv, const Geo& g, int nkt, hipStream_t st) {
+                               u16* dq, float* dq_part, const int2* tile_info,
+                               const float* partial, float* dk, float* dv, const Geo& g, int nkt,
+                               hipStream_t st) {
   const int nqb = (g.Sq * g.G + 127) / 128;
   const unsigned grid = (unsigned)nqb * g.B * g.Hkv;
   if (D == 128)
     bwd_dq_stash_kernel<128><<<grid + reduce_grid<128>(g, nkt), 256, 0, st>>>(
-        k, dstart, tile_rows, stash, stash_kvh_blocks, order, dq, tile_info, partial, dk, dv, g,
+        k, dstart, tile_rows, stash, stash_kvh_blocks, order, dq, dq_part, tile_info, partial, dk,
+        dv, g,
         nkt,
         (int)grid);
   else
     bwd_dq_stash_kernel<64><<<grid + reduce_grid<64>(g, nkt), 256, 0, st>>>(
-        k, dstart, tile_rows, stash, stash_kvh_blocks, order, dq, tile_info, partial, dk, dv, g,
+        k, dstart, tile_rows, stash, stash_kvh_blocks, order, dq, dq_part, tile_info, partial, dk,
+        dv, g,
         nkt,
         (int)grid);
   return hipGetLastError();

@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict
     sched_reads_ahead<2 * KK, KK, 2>();
     // the next tile's V DMA, while the score products run
     mid();
-    const bool full = kr.max_lo <= t0 && t0 + BN - 1 <= kr.min_pos;
+    const bool full = qtile_full(kr, t0, BN);
     if (!full) {
       // allowed keys lo..last relative to this lane's first key t0 + 4h;
       // register r holds key offset 8*(r/4) + r%4 (+32 for s1)

@@ -166,43 +166,13 @@ __global__ __launch_bounds__(256) void prep_interval(const int32_t* __restrict__
   dend[(size_t)b * Skv + t] = min(a, Skv);
 }
 
-// Local token range(s) whose positions fall in [p0, p1): at most one range
-// in each of the rank's two chunks.
-__device__ __forceinline__ void token_ranges(int p0, int p1, const Geo& g, int& a0, int& na,
-                                             int& b0, int& nb) {
-  const int baseA = g.rank * g.c;
-  const int baseB = (2 * g.cp - 1 - g.rank) * g.c;
-  const int la = min(max(p0 - baseA, 0), g.c), ha = min(max(p1 - baseA, 0), g.c);
-  const int lb = min(max(p0 - baseB, 0), g.c), hb = min(max(p1 - baseB, 0), g.c);
-  a0 = la; na = max(0, ha - la);
-  b0 = g.c + lb; nb = max(0, hb - lb);
-}
-
-__device__ void dkdv_tile_tokens(const int32_t* dend_b, int kt, const Geo& g, int& a0, int& na,
-                                 int& b0, int& nb) {
-  const int t0 = kt * kDkdvBN;
-  const int tl = min(t0 + kDkdvBN - 1, g.Skv - 1);
-  const int pe = dend_b[tl];
-  token_ranges(t0, pe, g, a0, na, b0, nb);
-}
-
-// Stash blocks (kStashRows query rows x kDkdvBN keys of dS) of a key tile:
-// the tile reaches one contiguous range of local tokens [tlo, thi) (when it
-// reaches both chunks the first part runs to the end of the rank's first
-// chunk and the second starts at the beginning of the second), i.e. the
-// query rows [tlo*G, thi*G), which the blocks cover aligned to kStashRows.
-__device__ __forceinline__ int stash_blocks(int a0, int na, int b0, int nb, const Geo& g) {
-  const int tlo = na > 0 ? a0 : b0, thi = nb > 0 ? b0 + nb : a0 + na;
-  if (thi <= tlo) return 0;
-  return (thi * g.G + kStashRows - 1) / kStashRows - tlo * g.G / kStashRows;
-}
-
 // One block (kScanThreads threads).  For every (batch, key tile): the
 // number of query rows (local tokens x group heads) that reach it; then a
 // split of those rows into pieces of `rows_per_split` (chosen so the total
 // stays under kMaxSplitBase), the work-item list and the partial-sum slots.
-__device__ void sched_body(const int32_t* __restrict__ dend, const Geo& g, int nkt,
-                           int max_split_base, SchedHeader* __restrict__ hdr,
+__device__ void sched_body(const int32_t* __restrict__ kfirst, const int32_t* __restrict__ dend,
+                           const Geo& g, int nkt, int max_split_base, int stash_budget,
+                           SchedHeader* __restrict__ hdr,
                            int2* __restrict__ tile_info, int2* __restrict__ items,
                            int4* __restrict__ tile_rows) {
   __shared__ int sh[32];
@@ -215,7 +185,8 @@ __device__ void sched_body(const int32_t* __restrict__ dend, const Geo& g, int n
   for (int x = first; x < min(first + per, ntiles); ++x) {
     const int b = x / nkt, kt = x % nkt;
     int a0, na, b0, nb;
-    dkdv_tile_tokens(dend + (size_t)b * g.Skv, kt, g, a0, na, b0, nb);
+    key_tile_tokens(kfirst ? kfirst + (size_t)b * g.Skv : nullptr, dend + (size_t)b * g.Skv, kt,
+                    g, a0, na, b0, nb);
     tot += (long long)(na + nb) * g.G;
   }
 #pragma unroll
@@ -242,14 +213,17 @@ __device__ void sched_body(const int32_t* __restrict__ dend, const Geo& g, int n
   for (int x = first; x < min(first + per, ntiles); ++x) {
     const int b = x / nkt, kt = x % nkt;
     int a0, na, b0, nb;
-    dkdv_tile_tokens(dend + (size_t)b * g.Skv, kt, g, a0, na, b0, nb);
+    key_tile_tokens(kfirst ? kfirst + (size_t)b * g.Skv : nullptr, dend + (size_t)b * g.Skv, kt,
+                    g, a0, na, b0, nb);
     const long long rows = (long long)(na + nb) * g.G;
     const int nf = (int)(rows / rps);
     const long long rem = rows - (long long)nf * rps;
     const int ns = nf + ((rem > 0 || rows == 0) ? 1 : 0);
     my_full += nf;
     my_slots += ns > 1 ? ns : 0;
-    my_blocks += stash_blocks(a0, na, b0, nb, g);
+    // (without a stash nothing is counted: the host bounds the block sums
+    // below 2^31 only when it reserves one)
+    if (stash_budget > 0) my_blocks += stash_blocks(a0, na, b0, nb, g);
     if (rem > 0 || rows == 0) atomicAdd(&bucket_cnt[remainder_class(rem)], 1);
   }
   __shared__ int scan_i[kScanThreads], scan_s[kScanThreads], scan_b[kScanThreads];
@@ -284,7 +258,8 @@ __device__ void sched_body(const int32_t* __restrict__ dend, const Geo& g, int n
   for (int x = first; x < min(first + per, ntiles); ++x) {
     const int b = x / nkt, kt = x % nkt;
     int a0, na, b0, nb;
-    dkdv_tile_tokens(dend + (size_t)b * g.Skv, kt, g, a0, na, b0, nb);
+    key_tile_tokens(kfirst ? kfirst + (size_t)b * g.Skv : nullptr, dend + (size_t)b * g.Skv, kt,
+                    g, a0, na, b0, nb);
     const long long rows = (long long)(na + nb) * g.G;
     const int nf = (int)(rows / rps);
     const long long rem = rows - (long long)nf * rps;
@@ -292,9 +267,13 @@ __device__ void sched_body(const int32_t* __restrict__ dend, const Geo& g, int n
     const int ns = nf + (has_rem ? 1 : 0);
     tile_info[x] = make_int2(ns, ns > 1 ? slot : -1);
     {
+      // stashed while the tile's blocks fit in the budget: a prefix of the
+      // tiles in (batch row, key tile) order, since sblk only grows
       const int tlo = na > 0 ? a0 : b0, thi = nb > 0 ? b0 + nb : a0 + na;
-      tile_rows[x] = make_int4(tlo, thi, tlo * g.G / kStashRows, sblk);
-      sblk += stash_blocks(a0, na, b0, nb, g);
+      const int nblk = stash_budget > 0 ? stash_blocks(a0, na, b0, nb, g) : 0;
+      const bool fits = stash_budget > 0 && (long long)sblk + nblk <= (long long)stash_budget;
+      tile_rows[x] = make_int4(tlo, thi, tlo * g.G / kStashRows, fits ? sblk : -1);
+      sblk += nblk;
     }
     for (int s = 0; s < nf; ++s) items[item + s] = make_int2(x, s);
     item += nf;
@@ -321,13 +300,43 @@ __device__ void sched_body(const int32_t* __restrict__ dend, const Geo& g, int n
   (void)sh;
 }
 
-__global__ __launch_bounds__(kScanThreads) void sched_dkdv(const int32_t* __restrict__ dend, Geo g,
-                                                           int nkt, int max_split_base,
-                                                           SchedHeader* __restrict__ hdr,
-                                                           int2* __restrict__ tile_info,
-                                                           int2* __restrict__ items,
-                                                           int4* __restrict__ tile_rows) {
-  sched_body(dend, g, nkt, max_split_base, hdr, tile_info, items, tile_rows);
+__global__ __launch_bounds__(kScanThreads) void sched_dkdv(
+    const int32_t* __restrict__ kfirst, const int32_t* __restrict__ dend, Geo g, int nkt,
+    int max_split_base, int stash_budget, SchedHeader* __restrict__ hdr,
+    int2* __restrict__ tile_info, int2* __restrict__ items, int4* __restrict__ tile_rows) {
+  sched_body(kfirst, dend, g, nkt, max_split_base, stash_budget, hdr, tile_info, items,
+             tile_rows);
+}
+
+// Cross-attention: query position p attends to keys lo[p] .. hi[p]-1 with lo
+// and hi non-decreasing and lo[p] < hi[p] (keys indexed apart from the
+// queries).  The positions that reach key t are then one contiguous run:
+// {p : hi[p] > t} is a suffix of the positions and {p : lo[p] <= t} a
+// prefix, so the run is [kfirst[t], kend[t]) with kfirst[t] the first p with
+// hi[p] > t and kend[t] the first p with lo[p] > t (S if none); empty when
+// kfirst[t] >= kend[t].  Two binary searches per key.  grid = (ceil(Skv /
+// 256), B).
+__global__ __launch_bounds__(256) void prep_cross_keys(const int32_t* __restrict__ lo,
+                                                       const int32_t* __restrict__ hi, int S,
+                                                       int Skv, int32_t* __restrict__ kfirst,
+                                                       int32_t* __restrict__ kend) {
+  const int b = blockIdx.y;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= Skv) return;
+  const int32_t* l = lo + (size_t)b * S;
+  const int32_t* h = hi + (size_t)b * S;
+  int a = 0, z = S;   // first p with h[p] > t
+  while (a < z) {
+    const int mid = (a + z) >> 1;
+    if (h[mid] > t) z = mid; else a = mid + 1;
+  }
+  kfirst[(size_t)b * Skv + t] = a;
+  a = 0; z = S;       // first p with l[p] > t
+  while (a < z) {
+    const int mid = (a + z) >> 1;
+    if (l[mid] > t) z = mid; else a = mid + 1;
+  }
+  kend[(size_t)b * Skv + t] = a;
 }
 
 // Per query row: -lse/scale (start value of the S accumulators of the dK/dV
@@ -465,12 +474,14 @@ __global__ __launch_bounds__(kScanThreads) void tile_order_fwd_iv(
 template <int D>
 __global__ __launch_bounds__(kScanThreads) void sched_rowstat(
     const int32_t* __restrict__ dstart, const int32_t* __restrict__ dend, Geo g, int nkt,
-    int max_split_base, SchedHeader* __restrict__ hdr, int2* __restrict__ tile_info,
+    int max_split_base, int stash_budget, SchedHeader* __restrict__ hdr,
+    int2* __restrict__ tile_info,
     int2* __restrict__ items, int4* __restrict__ tile_rows, int32_t* __restrict__ dq_order,
     const u16* __restrict__ out, const u16* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ Lbuf, float* __restrict__ Nbuf) {
   if (blockIdx.x == 0)
-    sched_body(dend, g, nkt, max_split_base, hdr, tile_info, items, tile_rows);
+    sched_body(nullptr, dend, g, nkt, max_split_base, stash_budget, hdr, tile_info, items,
+               tile_rows);
   else if (blockIdx.x == 1)
     tile_order_body<kDkdvBN>(dstart, g, dq_order);
   else
@@ -504,16 +515,24 @@ hipError_t launch_prep_cu(const int32_t* cu, int n_docs, int Skv, int32_t* dstar
   return hipGetLastError();
 }
 
-hipError_t launch_sched_dkdv(const int32_t* dend, const Geo& g, int nkt, int max_split_base,
-                             SchedHeader* hdr, int2* tile_info, int2* items, int4* tile_rows,
-                             hipStream_t st) {
-  sched_dkdv<<<1, kScanThreads, 0, st>>>(dend, g, nkt, max_split_base, hdr, tile_info, items,
-                                         tile_rows);
+hipError_t launch_sched_dkdv(const int32_t* kfirst, const int32_t* dend, const Geo& g, int nkt,
+                             int max_split_base, int stash_budget, SchedHeader* hdr,
+                             int2* tile_info, int2* items, int4* tile_rows, hipStream_t st) {
+  sched_dkdv<<<1, kScanThreads, 0, st>>>(kfirst, dend, g, nkt, max_split_base, stash_budget, hdr,
+                                         tile_info, items, tile_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_cross_keys(const int32_t* lo, const int32_t* hi, int B, int S, int Skv,
+                                  int32_t* kfirst, int32_t* kend, hipStream_t st) {
+  dim3 grid((Skv + 255) / 256, B);
+  prep_cross_keys<<<grid, 256, 0, st>>>(lo, hi, S, Skv, kfirst, kend);
   return hipGetLastError();
 }
 
 hipError_t launch_sched_rowstat(int D, const int32_t* dstart, const int32_t* dend, const Geo& g,
-                                int nkt, int max_split_base, SchedHeader* hdr, int2* tile_info,
+                                int nkt, int max_split_base, int stash_budget,
+                                SchedHeader* hdr, int2* tile_info,
                                 int2* items, int4* tile_rows, int32_t* dq_order, const u16* out,
                                 const u16* dout, const float* lse, float* Lbuf, float* Nbuf,
                                 hipStream_t st) {
@@ -521,12 +540,12 @@ hipError_t launch_sched_rowstat(int D, const int32_t* dstart, const int32_t* den
   const int rows_per_block = kScanThreads / (D / 8);
   const unsigned grid = 2u + (unsigned)((nrows + rows_per_block - 1) / rows_per_block);
   if (D == 128)
-    sched_rowstat<128><<<grid, kScanThreads, 0, st>>>(dstart, dend, g, nkt, max_split_base, hdr,
-                                                      tile_info, items, tile_rows, dq_order, out,
+    sched_rowstat<128><<<grid, kScanThreads, 0, st>>>(dstart, dend, g, nkt, max_split_base,
+                                                      stash_budget, hdr, tile_info, items, tile_rows, dq_order, out,
                                                       dout, lse, Lbuf, Nbuf);
   else
-    sched_rowstat<64><<<grid, kScanThreads, 0, st>>>(dstart, dend, g, nkt, max_split_base, hdr,
-                                                     tile_info, items, tile_rows, dq_order, out,
+    sched_rowstat<64><<<grid, kScanThreads, 0, st>>>(dstart, dend, g, nkt, max_split_base,
+                                                     stash_budget, hdr, tile_info, items, tile_rows, dq_order, out,
                                                      dout, lse, Lbuf, Nbuf);
   return hipGetLastError();
 }

@@ -28,7 +28,7 @@ int g_open[kNumKernels];
 
 const char* kNames[kNumKernels] = {"prep",       "fwd",           "sched_dkdv", "bwd_dq",
                                    "bwd_dkdv",   "bwd_reduce",    "sched_rowstat",
-                                   "tile_order"};
+                                   "tile_order", "bwd_dq_rest"};
 
 hipEvent_t take_event() {
   if (g_used == g_pool.size()) {

@@ -72,8 +72,9 @@ enum {
   DMGQA_ERR_INVALID_ARG = -1,  /* null pointer, misalignment, bad rank,
                                   S % (2*cp_size) != 0, Hq % Hkv != 0, Skv
                                   outside [(2*cp_size-cp_rank)*c, S], both or
-                                  neither of doc_ids / cu_seqlens, non-finite
-                                  or zero softmax_scale, negative sizes */
+                                  neither of doc_ids / cu_seqlens,
+                                  softmax_scale not finite and positive,
+                                  negative sizes */
   DMGQA_ERR_UNSUPPORTED = -2,  /* D not in {64, 128}; cu_seqlens with B > 1;
                                   sizes whose element offsets overflow */
   DMGQA_ERR_WORKSPACE = -3,    /* workspace_bytes below the required size
@@ -87,28 +88,63 @@ size_t docmask_gqa_fwd_workspace_size(int32_t B, int32_t S, int32_t Skv,
                                       int32_t Hq, int32_t Hkv, int32_t D,
                                       int32_t cp_size);
 
-/* Bytes of workspace for the fastest backward.  Besides the scheduling
- * arrays it reserves a stash for dS in bf16 (blocks of 32 query rows x 128
- * keys, for every key tile and the query rows that may reach it): the dK/dV
- * kernel stores dS there and dQ = scale * dS K becomes one product per key
- * tile instead of recomputing the scores.  The size is an upper bound over
- * all document layouts (at most about Sq * Hq * Skv bytes; the layouts of a
- * real batch use a fraction of it) and depends only on the sizes. */
+/* Backward workspace.  Besides the scheduling arrays (the minimum below),
+ * the backward can use a stash for dS in bf16 (blocks of 32 query rows x 128
+ * keys of one key tile): the dK/dV kernel, which forms dS anyway, stores it,
+ * and dQ = scale * dS K becomes one product per key tile instead of
+ * recomputing the scores, P and dP.  The stash a batch needs depends on its
+ * documents (about 2 bytes per allowed (query row, key) pair and query head),
+ * so the call plans it from the workspace it is given:
+ *  - room for the worst case over all document layouts of this rank's shape
+ *    (docmask_gqa_bwd_workspace_size_full): every key tile is stashed;
+ *  - less, but more than the minimum plus an fp32 buffer of B*Sq*Hq*D floats
+ *    (partial dQ) and one stash block per KV head: key tiles are stashed in
+ *    order (batch row, then key position) while their blocks fit, and the
+ *    query tiles that reach the others recompute those tiles' share of dQ;
+ *  - otherwise no stash: dQ recomputes the scores for every key tile.
+ * All three give the same results up to the order of rounding.
+ *
+ * docmask_gqa_bwd_workspace_size: the default.  The worst-case stash if it
+ * fits in a budget of 2 GiB (all KV heads together), else the smaller of
+ * that worst case and the minimum plus the partial-dQ buffer plus a 2 GiB
+ * stash.  For an 8K-token share with 16
+ * query heads per KV head (d = 128) that is about 1.1 GiB; the stash does
+ * not grow past the budget for longer sequences.
+ * docmask_gqa_bwd_workspace_size_full: the minimum plus the worst-case stash
+ * (quadratic in the sequence: about Sq * Hq * Skv bytes).
+ * docmask_gqa_bwd_workspace_size_min: the smallest workspace the backward
+ * accepts (no stash).
+ * The sizes depend only on the arguments; they hold for every cp_rank
+ * whose K/V prefix fits in Skv.  0 when there is nothing to compute or the
+ * sizes are invalid. */
 size_t docmask_gqa_bwd_workspace_size(int32_t B, int32_t S, int32_t Skv,
                                       int32_t Hq, int32_t Hkv, int32_t D,
                                       int32_t cp_size);
-
-/* Smallest workspace the backward accepts: without the dS stash, dQ
- * recomputes the scores, P and dP (slower, same results up to rounding
- * order).  Callers that cannot spare the stash pass any size from this one
- * up to, but not including, docmask_gqa_bwd_workspace_size(). */
+size_t docmask_gqa_bwd_workspace_size_full(int32_t B, int32_t S, int32_t Skv,
+                                           int32_t Hq, int32_t Hkv, int32_t D,
+                                           int32_t cp_size);
 size_t docmask_gqa_bwd_workspace_size_min(int32_t B, int32_t S, int32_t Skv,
                                           int32_t Hq, int32_t Hkv, int32_t D,
                                           int32_t cp_size);
 
+/* Which way the backward will form dQ with a workspace of workspace_bytes
+ * for these arguments (no HIP call): DMGQA_BWD_PATH_STASH (every key tile
+ * stashed), DMGQA_BWD_PATH_MIXED (stash with a budget, the rest
+ * recomputed), DMGQA_BWD_PATH_RECOMPUTE, or a negative status for arguments
+ * the backward would reject (DMGQA_ERR_WORKSPACE below the minimum). */
+enum {
+  DMGQA_BWD_PATH_RECOMPUTE = 0,
+  DMGQA_BWD_PATH_STASH = 1,
+  DMGQA_BWD_PATH_MIXED = 2
+};
+int docmask_gqa_bwd_path(int32_t B, int32_t S, int32_t Skv, int32_t Hq,
+                         int32_t Hkv, int32_t D, int32_t cp_size,
+                         int32_t cp_rank, size_t workspace_bytes);
+
 /* Forward: out = softmax(scale * q k^T, masked) v and lse for the rank's
  * local rows.  Exactly one of doc_ids / cu_seqlens is non-NULL; n_docs is
- * read only with cu_seqlens.  softmax_scale is normally 1/sqrt(D). */
+ * read only with cu_seqlens.  softmax_scale must be finite and positive,
+ * normally 1/sqrt(D). */
 int docmask_gqa_attn_fwd(const void* q, const void* k, const void* v,
                          const int32_t* doc_ids, const int32_t* cu_seqlens,
                          int32_t n_docs, int32_t B, int32_t S, int32_t Skv,
@@ -164,7 +200,8 @@ int docmask_gqa_interval_bounds(const int32_t* lo, int32_t B, int32_t S,
                                 int32_t Skv, int32_t* bounds,
                                 size_t bounds_bytes, void* stream);
 
-/* Cross-attention forward: non-causal intervals with explicit ends.  From
+/* Cross-attention forward and backward: non-causal intervals with explicit
+ * ends.  From
  * "Scaling Llama 3 Training with Efficient Parallelism Strategies", the
  * section on pipeline parallelism for multimodal training (Figure 5 and its
  * second challenge): cross-attention layers take image sequences of 1.2K-3K
@@ -172,14 +209,22 @@ int docmask_gqa_interval_bounds(const int32_t* lo, int32_t B, int32_t S,
  * parallelism: the rows of q are the S tokens in order) attends to keys
  * lo[b][p] .. hi[b][p]-1 of k and v, whose rows are indexed on their own
  * (for example the image tokens of p's sample).
- *   q, out : bf16 [B, S, Hq, D], S even;  k, v : bf16 [B, Skv, Hkv, D];
+ *   q, out, dout, dq : bf16 [B, S, Hq, D] (any S >= 0);
+ *   k, v : bf16 [B, Skv, Hkv, D];  dk, dv : fp32 [B, Skv, Hkv, D];
  *   lse    : fp32 [B, S, Hq];
  *   lo, hi : int32 [B, S] device arrays, non-decreasing in p, with
  *            0 <= lo[b][p] < hi[b][p] <= Skv.  These are preconditions the
  *            call does not check; docmask_gqa_check_cross_intervals checks
  *            them synchronously and returns 0 (valid) or 1.
- * Workspace: docmask_gqa_fwd_cross_workspace_size bytes (the tile order).
- * There is no backward for this form yet.  Errors and ownership as above. */
+ * Forward workspace: docmask_gqa_fwd_cross_workspace_size bytes (the tile
+ * order).  The backward takes the forward's out and lse and dout, and writes
+ * dq and dk, dv (summed over each KV head's query heads, zero for keys no
+ * query reaches) as the causal backward does; its dQ always recomputes the
+ * scores (no stash).  Workspace: docmask_gqa_bwd_cross_workspace_size bytes
+ * (the keys' query ranges, the schedule, the row statistics and the partial
+ * sums).  Only the image encoder and the cross-attention layers are trained
+ * in that setting (same section), so this is the backward that runs.
+ * Errors and ownership as above. */
 size_t docmask_gqa_fwd_cross_workspace_size(int32_t B, int32_t S, int32_t Skv,
                                             int32_t Hq, int32_t Hkv, int32_t D);
 int docmask_gqa_attn_fwd_cross(const void* q, const void* k, const void* v,
@@ -187,6 +232,16 @@ int docmask_gqa_attn_fwd_cross(const void* q, const void* k, const void* v,
                                int32_t S, int32_t Skv, int32_t Hq, int32_t Hkv,
                                int32_t D, float softmax_scale, void* out,
                                float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream);
+size_t docmask_gqa_bwd_cross_workspace_size(int32_t B, int32_t S, int32_t Skv,
+                                            int32_t Hq, int32_t Hkv, int32_t D);
+int docmask_gqa_attn_bwd_cross(const void* q, const void* k, const void* v,
+                               const void* out, const void* dout,
+                               const float* lse, const int32_t* lo,
+                               const int32_t* hi, int32_t B, int32_t S,
+                               int32_t Skv, int32_t Hq, int32_t Hkv, int32_t D,
+                               float softmax_scale, void* dq, float* dk,
+                               float* dv, void* workspace,
                                size_t workspace_bytes, void* stream);
 int docmask_gqa_check_cross_intervals(const int32_t* lo, const int32_t* hi,
                                       int32_t B, int32_t S, int32_t Skv,

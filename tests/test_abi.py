@@ -59,6 +59,52 @@ def test_workspace_sizes():
     assert b(*one_tile) - bm(*one_tile) >= 128 * 128 * 2
 
 
+GiB = 1 << 30
+PATH_R, PATH_S, PATH_M = (M.DMGQA_BWD_PATH_RECOMPUTE, M.DMGQA_BWD_PATH_STASH,
+                          M.DMGQA_BWD_PATH_MIXED)
+
+
+@pytest.mark.parametrize("S,cp,Hq,Hkv,D", [(8192, 1, 16, 1, 128), (8192, 1, 32, 8, 128),
+                                          (131072, 16, 16, 1, 128), (32768, 4, 16, 1, 128),
+                                          (1200, 3, 12, 4, 128), (768, 3, 16, 1, 128),
+                                          (1024, 2, 8, 1, 128), (1000, 2, 6, 2, 64)])
+def test_bwd_workspace_covers_every_rank(S, cp, Hq, Hkv, D):
+    """The size queries take no rank: the full size must give every rank the
+    whole stash, whichever Skv from its own prefix to S it passes, and the
+    default must give every rank a stash (whole, or with a budget)."""
+    b, bm = M.docmask_gqa_bwd_workspace_size, M.docmask_gqa_bwd_workspace_size_min
+    bf = M.docmask_gqa_bwd_workspace_size_full
+    c = S // (2 * cp)
+    for r in range(cp):
+        for Skv in sorted({(2 * cp - r) * c, S}):
+            shape = (1, S, Skv, Hq, Hkv, D, cp)
+            assert bm(*shape) < b(*shape) <= bf(*shape)
+            assert M.docmask_gqa_bwd_path(*shape, r, bf(*shape)) == PATH_S, (r, Skv)
+            assert M.docmask_gqa_bwd_path(*shape, r, b(*shape)) in (PATH_S, PATH_M), (r, Skv)
+            assert M.docmask_gqa_bwd_path(*shape, r, bm(*shape)) == PATH_R
+            assert M.docmask_gqa_bwd_path(*shape, r, bm(*shape) - 1) == WS
+
+
+def test_default_stash_budget():
+    """The default backward workspace holds at most a 2 GiB stash plus the
+    fp32 partial-dQ buffer; shapes whose worst case fits get all of it."""
+    b, bm = M.docmask_gqa_bwd_workspace_size, M.docmask_gqa_bwd_workspace_size_min
+    bf = M.docmask_gqa_bwd_workspace_size_full
+    tp405b = (1, 8192, 8192, 16, 1, 128, 1)
+    assert b(*tp405b) == bf(*tp405b) and M.docmask_gqa_bwd_path(*tp405b, 0, b(*tp405b)) == PATH_S
+    for shape in ((1, 131072, 131072, 16, 1, 128, 16), (1, 32768, 32768, 16, 1, 128, 4)):
+        dq_part = 8192 * 16 * 128 * 4
+        assert b(*shape) <= bm(*shape) + dq_part + 2 * GiB + 256
+        assert bf(*shape) > 3 * GiB
+        for r in (0, shape[-1] - 1):
+            assert M.docmask_gqa_bwd_path(*shape, r, b(*shape)) == PATH_M
+    # a workspace with room for the partial-dQ buffer but not one stash block
+    # per KV head falls back to recomputing
+    shape = (1, 32768, 32768, 16, 1, 128, 4)
+    assert M.docmask_gqa_bwd_path(*shape, 0, bm(*shape) + 8192 * 16 * 128 * 4) == PATH_R
+    assert M.docmask_gqa_bwd_path(*shape, 0, bm(*shape) + 8192 * 16 * 128 * 4 + 8192) == PATH_M
+
+
 class _Buf:
     """16-byte aligned host memory standing in for device pointers: every call
     below is rejected before any pointer is dereferenced."""
@@ -116,6 +162,8 @@ CASES = [
     (dict(scale=float("nan")), INV),
     (dict(scale=float("inf")), INV),
     (dict(scale=0.0), INV),
+    (dict(scale=-0.125), INV),                  # the kernels assume a positive scale
+    (dict(scale=-1e-30), INV),
     (dict(B=-1), INV),
     (dict(wsb=0), WS),                          # all valid but workspace too small
 ]
@@ -216,7 +264,7 @@ def test_cross_workspace_size():
     # the tile order: B * ceil(S * G / 128) int32, 256-byte aligned
     assert f(1, 4870, 66775, 16, 1, 128) == -(-(-(-4870 * 16 // 128) * 4) // 256) * 256
     assert f(2, 64, 3000, 4, 4, 64) == 256
-    assert f(1, 63, 100, 4, 1, 64) == 0          # S odd
+    assert f(1, 63, 100, 4, 1, 64) == 256        # any S (no context parallelism)
     assert f(1, 64, 0, 4, 1, 64) == 0            # no keys
     assert f(1, 64, 100, 4, 1, 96) == 0          # D unsupported
     assert f(0, 64, 100, 4, 1, 64) == 0          # empty
@@ -236,12 +284,13 @@ def _cross_call(**kw):
 @pytest.mark.parametrize("kw,want", [
     (dict(lo=None), INV),
     (dict(hi=None), INV),
-    (dict(S=63), INV),                 # S must be even
+    (dict(S=-1), INV),
     (dict(Skv=0), INV),
     (dict(Hq=6, Hkv=4), INV),          # Hq % Hkv
     (dict(D=96), UNS),
     (dict(scale=0.0), INV),
     (dict(scale=float("inf")), INV),
+    (dict(scale=-0.125), INV),
     (dict(nbytes=4), WS),
     (dict(ws=None), INV),
 ])
@@ -255,3 +304,48 @@ def test_cross_checker_rejects_sizes():
     assert L.docmask_gqa_check_cross_intervals(None, None, -1, 4, 4, None) == INV
     assert L.docmask_gqa_check_cross_intervals(None, None, 0, 4, 4, None) == 0
     assert L.docmask_gqa_check_cross_intervals(None, None, 1, 4, 4, None) == INV
+
+
+# ---------------------------------------------------------------- cross-attention backward
+
+def _cross_bwd(**kw):
+    b = _Buf(1 << 16)
+    a = dict(q=b.p, k=b.p, v=b.p, out=b.p, dout=b.p, lse=b.p, lo=b.p, hi=b.p, B=1, S=63,
+             Skv=300, Hq=4, Hkv=1, D=64, scale=0.125, dq=b.p, dk=b.p, dv=b.p, ws=b.p, nbytes=0)
+    a.update(kw)
+    return M.lib().docmask_gqa_attn_bwd_cross(a["q"], a["k"], a["v"], a["out"], a["dout"],
+                                              a["lse"], a["lo"], a["hi"], a["B"], a["S"],
+                                              a["Skv"], a["Hq"], a["Hkv"], a["D"], a["scale"],
+                                              a["dq"], a["dk"], a["dv"], a["ws"], a["nbytes"],
+                                              None)
+
+
+def test_cross_bwd_workspace_size():
+    f = M.lib().docmask_gqa_bwd_cross_workspace_size
+    n = f(1, 63, 300, 4, 1, 64)
+    # the keys' query ranges (2 x Skv int32) come first, then the schedule,
+    # the row statistics (2 x S x Hq fp32) and the partial-sum slots
+    assert n >= 2 * 300 * 4 + 2 * 63 * 4 * 4
+    assert f(1, 4870, 66775, 16, 1, 128) > f(1, 4870, 6000, 16, 1, 128)
+    assert f(0, 63, 300, 4, 1, 64) == 0
+    assert f(1, 63, 0, 4, 1, 64) == 0
+    assert f(1, 63, 300, 6, 4, 64) == 0
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INV), (dict(out=None), INV), (dict(dout=None), INV), (dict(lse=None), INV),
+    (dict(lo=None), INV), (dict(hi=None), INV), (dict(dq=None), INV), (dict(dk=None), INV),
+    (dict(dv=None), INV), (dict(ws=None), INV),
+    (dict(S=-1), INV), (dict(Skv=0), INV), (dict(Hq=6, Hkv=4), INV), (dict(D=96), UNS),
+    (dict(scale=0.0), INV), (dict(scale=-1.0), INV), (dict(scale=float("nan")), INV),
+    (dict(nbytes=16), WS),
+])
+def test_cross_bwd_rejects(kw, want):
+    """Every check happens before any HIP call, so these run without a GPU."""
+    kw.setdefault("nbytes", 1 << 16)
+    assert _cross_bwd(**kw) == want
+
+
+def test_cross_bwd_empty_is_noop():
+    assert _cross_bwd(B=0, q=None, lo=None, nbytes=0) == 0
+    assert _cross_bwd(S=0, nbytes=0) == 0

@@ -1,9 +1,10 @@
-"""GPU parity of the cross-attention forward (query token p attends to keys
-lo[p] .. hi[p]-1, keys indexed apart from the queries) against the CPU
-oracle: packed samples of text queries over their own image tokens, GQA
-group sizes 1 / 4 / 16, D 64 and 128, batch rows with different layouts,
-fewer keys than queries, one image spanning many key tiles; the interval
-checker; sampled rows at the multimodal sizes."""
+"""GPU parity of the cross-attention forward and backward (query token p
+attends to keys lo[p] .. hi[p]-1, keys indexed apart from the queries)
+against the CPU oracle: packed samples of text queries over their own image
+tokens, GQA group sizes 1 / 4 / 16, D 64 and 128, batch rows with different
+layouts, fewer keys than queries, one image spanning many key tiles, an odd
+number of text tokens, an image no text attends to; the interval checker;
+every element at the multimodal size."""
 from __future__ import annotations
 
 import numpy as np
@@ -26,6 +27,8 @@ CASES = [
     ("fewer_keys", [[100, 60]], [[20, 30]], 16, 1, 128, 4),
     ("one_long_image", [[64]], [[3000]], 16, 1, 128, 5),
     ("batch2", [[20, 36], [50, 6]], [[300, 150], [99, 351]], 16, 1, 128, 6),
+    ("odd_text", [[33, 50, 18]], [[400, 129, 333]], 16, 1, 128, 7),
+    ("unreached_image", [[21, 0, 40]], [[150, 260, 90]], 8, 1, 64, 8),
 ]
 
 
@@ -35,13 +38,13 @@ def _case(texts, images, Hq, Hkv, D, seed):
     assert all(sum(t) == S for t in texts) and all(sum(i) == Skv for i in images)
     lo = np.stack([W.cross_bounds(t, i)[0] for t, i in zip(texts, images)])
     hi = np.stack([W.cross_bounds(t, i)[1] for t, i in zip(texts, images)])
-    q, k, v = W.cross_tensors(len(texts), S, Skv, Hq, Hkv, D, seed)
-    return lo, hi, q, k, v
+    q, k, v, do = W.cross_tensors(len(texts), S, Skv, Hq, Hkv, D, seed, dout=True)
+    return lo, hi, q, k, v, do
 
 
 @pytest.mark.parametrize("cid,texts,images,Hq,Hkv,D,seed", CASES, ids=[c[0] for c in CASES])
 def test_cross_fwd_full_oracle(cid, texts, images, Hq, Hkv, D, seed):
-    lo, hi, q, k, v = _case(texts, images, Hq, Hkv, D, seed)
+    lo, hi, q, k, v, _ = _case(texts, images, Hq, Hkv, D, seed)
     B, S = lo.shape
     Skv = k.shape[1]
     say(f"[cross {cid}] B={B} S={S} Skv={Skv} Hq={Hq} Hkv={Hkv} D={D}")
@@ -54,6 +57,63 @@ def test_cross_fwd_full_oracle(cid, texts, images, Hq, Hkv, D, seed):
     rout, rlse = oracle.attn_fwd(q, k, v, None, 1, 0, scale, lo=lo, hi=hi)
     compare("out", host(out), rout)
     compare("lse", host(lse), rlse)
+
+
+def _cross_fwd_bwd(q, k, v, do, lo, hi, scale):
+    lo_d, hi_d = torch.from_numpy(lo).cuda(), torch.from_numpy(hi).cuda()
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    out, lse = M.docmask_gqa_attn_fwd_cross(qd, kd, vd, lo_d, hi_d, softmax_scale=scale)
+    dq, dk, dv = M.docmask_gqa_attn_bwd_cross(qd, kd, vd, out, dod, lse, lo_d, hi_d,
+                                              softmax_scale=scale)
+    torch.cuda.synchronize()
+    return out, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("cid,texts,images,Hq,Hkv,D,seed", CASES, ids=[c[0] for c in CASES])
+def test_cross_bwd_full_oracle(cid, texts, images, Hq, Hkv, D, seed):
+    """Every element of the backward against the oracle; image tokens no
+    text token attends to get exactly zero dk / dv."""
+    lo, hi, q, k, v, do = _case(texts, images, Hq, Hkv, D, seed)
+    B, S = lo.shape
+    Skv = k.shape[1]
+    say(f"[cross bwd {cid}] B={B} S={S} Skv={Skv} Hq={Hq} Hkv={Hkv} D={D}")
+    scale = 1.0 / np.sqrt(D)
+    out, lse, dq, dk, dv = _cross_fwd_bwd(q, k, v, do, lo, hi, scale)
+    rdq, rdk, rdv, rout, rlse = oracle.attn_bwd(q, k, v, do, None, 1, 0, scale,
+                                                return_fwd=True, lo=lo, hi=hi)
+    compare("out", host(out), rout)
+    compare("lse", host(lse), rlse)
+    compare("dq", host(dq), rdq)
+    compare("dk", host(dk), rdk)
+    compare("dv", host(dv), rdv)
+    t = np.arange(Skv)
+    for b in range(B):
+        reached = ((t[None, :] >= lo[b][:, None]) & (t[None, :] < hi[b][:, None])).any(0)
+        unreached = torch.from_numpy(~reached).cuda()
+        assert torch.all(dk[b, unreached] == 0) and torch.all(dv[b, unreached] == 0)
+        if cid == "unreached_image":
+            assert not reached.all()
+
+
+def test_cross_bwd_multimodal_elementwise():
+    """32 samples of 100-199 text tokens against 1200-3000 image tokens each
+    (an odd text total), 16 query heads on 1 KV head, d = 128: every element
+    of out, lse, dq, dk and dv against the oracle."""
+    text, image = W.cross_lengths(32, seed=11)
+    lo, hi = W.cross_bounds(text, image)
+    S, Skv = sum(text), sum(image)
+    q, k, v, do = W.cross_tensors(1, S, Skv, 16, 1, 128, seed=12, dout=True)
+    say(f"[cross bwd multimodal] S={S} Skv={Skv}")
+    scale = 1.0 / np.sqrt(128)
+    out, lse, dq, dk, dv = _cross_fwd_bwd(q, k, v, do, lo[None], hi[None], scale)
+    rdq, rdk, rdv, rout, rlse = oracle.attn_bwd(q, k, v, do, None, 1, 0, scale,
+                                                return_fwd=True, lo=lo[None], hi=hi[None])
+    tag = f"cross multimodal S={S} Skv={Skv}"
+    compare("out", host(out), rout, tag=tag)
+    compare("lse", host(lse), rlse, tag=tag)
+    compare("dq", host(dq), rdq, tag=tag)
+    compare("dk", host(dk), rdk, tag=tag)
+    compare("dv", host(dv), rdv, tag=tag)
 
 
 def test_check_cross_intervals():
@@ -83,7 +143,7 @@ def test_cross_fwd_multimodal_sampled():
     lo, hi = W.cross_bounds(text, image)
     S, Skv = sum(text), sum(image)
     q, k, v = W.cross_tensors(1, S, Skv, 16, 1, 128, seed=12)
-    say(f"[cross multimodal] S={S} Skv={Skv}")
+    say(f"[cross multimodal] S={S} Skv={Skv} (odd text total: {S % 2 == 1})")
     scale = 1.0 / np.sqrt(128)
     out, lse = M.docmask_gqa_attn_fwd_cross(q.cuda(), k.cuda(), v.cuda(),
                                             torch.from_numpy(lo[None]).cuda(),

@@ -14,7 +14,7 @@ import torch
 import context_gqa_amd as M
 import oracle
 import workloads as W
-from tests.gpu_util import compare, host, local_positions, say
+from tests.gpu_util import EXPECT_PATH, bwd_workspace_bytes, compare, host, say
 from tests.test_gpu_parity import _cfg, _rng_lengths
 
 pytestmark = pytest.mark.gpu
@@ -75,19 +75,21 @@ def _run(case, lo, ws):
     bounds = M.docmask_gqa_interval_bounds(torch.from_numpy(lo).cuda(), Skv=case.Skv)
     out, lse = M.docmask_gqa_attn_fwd(q, k, v, cp_size=cfg.cp_size, cp_rank=case.rank,
                                       softmax_scale=case.scale, bounds=bounds)
-    kw = {}
-    if ws == "recompute":
-        B, Sq, Hq, D = case.q.shape
-        n = M.docmask_gqa_bwd_workspace_size_min(B, cfg.S, case.Skv, Hq, cfg.Hkv, D, cfg.cp_size)
-        kw["workspace"] = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    n = bwd_workspace_bytes(case, ws)
+    if n < 0:
+        pytest.skip("no budgeted-stash workspace for this shape")
+    B, Sq, Hq, D = case.q.shape
+    path = M.docmask_gqa_bwd_path(B, cfg.S, case.Skv, Hq, cfg.Hkv, D, cfg.cp_size, case.rank, n)
+    assert path in EXPECT_PATH[ws], (ws, path)
+    ws_t = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
     dq, dk, dv = M.docmask_gqa_attn_bwd(q, k, v, out, do, lse, cp_size=cfg.cp_size,
                                         cp_rank=case.rank, softmax_scale=case.scale,
-                                        bounds=bounds, **kw)
+                                        bounds=bounds, workspace=ws_t)
     torch.cuda.synchronize()
     return out, lse, dq, dk, dv
 
 
-@pytest.mark.parametrize("ws", ["stash", "recompute"])
+@pytest.mark.parametrize("ws", ["default", "mixed", "recompute"])
 @pytest.mark.parametrize("cid,cfg,seed,rank,lengths,masks", CASES, ids=[c[0] for c in CASES])
 def test_interval_small_full_oracle(cid, cfg, seed, rank, lengths, masks, ws):
     case, lo = _case(cfg, seed, rank, lengths, masks)
@@ -140,51 +142,25 @@ def test_check_intervals():
         assert M.docmask_gqa_check_intervals(torch.from_numpy(bad[None]).cuda()) == 1
 
 
-def _sample_kv_interval(lo, pos, Skv, max_reach=128, n=6, seed=0):
-    """Keys whose reaching local rows are few (the oracle computes those
-    rows' full forward), and a few keys no local row reaches."""
-    t = np.arange(Skv)
-    sp = np.sort(pos)
-    end = dend_from_lo(lo, Skv)
-    reach = np.searchsorted(sp, end, side="left") - np.searchsorted(sp, t, side="left")
-    ok = np.flatnonzero((reach > 0) & (reach <= max_reach))
-    zero = np.flatnonzero(reach == 0)
-    rng = np.random.default_rng(seed)
-    kv = sorted(rng.choice(ok, min(n, ok.size), replace=False).tolist()) if ok.size else []
-    z = sorted(rng.choice(zero, min(4, zero.size), replace=False).tolist()) if zero.size else []
-    return kv, z
-
-
-@pytest.mark.parametrize("name,rank,wn,ws", [("tp405b", 0, 2048, "stash"),
+@pytest.mark.parametrize("name,rank,wn,ws", [("tp405b", 0, 2048, "default"),
                                              ("tp405b", 0, 300, "recompute"),
-                                             ("long_cp", 7, 4096, "stash")])
-def test_interval_full_size_sampled(name, rank, wn, ws):
-    """At the workloads' full sizes, with a sliding window inside the
-    documents: sampled rows (out, lse, dq) and keys (dk, dv) against the
-    oracle's per-row and per-key forms."""
+                                             ("tp405b", 0, 1024, "mixed"),
+                                             ("long_cp", 7, 4096, "default")])
+def test_interval_full_size_elementwise(name, rank, wn, ws):
+    """At the workloads' full sizes, with a sliding window of wn keys inside
+    the documents: every element of out, lse, dq, dk and dv against the
+    oracle's full tensors."""
     cfg = W.CONFIGS[name]
     case = W.make_case(cfg, 0, rank)
     lo = window_lo(case.lengths[0], wn)[None]
     say(f"[{name} rank {rank} window {wn} {ws}] S={cfg.S} cp={cfg.cp_size} Skv={case.Skv}")
     out, lse, dq, dk, dv = _run(case, lo, ws)
-    for nm, t in (("out", out), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
-        assert torch.isfinite(t.float()).all(), nm
-    c = cfg.S // (2 * cfg.cp_size)
-    rng = np.random.default_rng(0)
-    rows = sorted({0, 1, c - 1, c, 2 * c - 1, *rng.integers(0, 2 * c, 16).tolist()})
-    ro, rl = oracle.attn_fwd_rows(case.q, case.k, case.v, None, cfg.cp_size, rank, case.scale, 0,
-                                  rows, lo=lo)
-    compare("out[rows]", host(out[0, rows]), ro)
-    compare("lse[rows]", host(lse[0, rows]), rl)
-    rdq = oracle.attn_bwd_rows(case.q, case.k, case.v, case.dout, None, cfg.cp_size, rank,
-                               case.scale, 0, rows, lo=lo)
-    compare("dq[rows]", host(dq[0, rows]), rdq)
-    pos = local_positions(cfg.S, cfg.cp_size, rank)
-    kv, zero = _sample_kv_interval(lo[0], pos, case.Skv)
-    if kv:
-        rdk, rdv = oracle.attn_bwd_kv_rows(case.q, case.k, case.v, case.dout, None, cfg.cp_size,
-                                           rank, case.scale, 0, kv, max_query_rows=6 * 128, lo=lo)
-        compare("dk[kv]", host(dk[0, kv]), rdk)
-        compare("dv[kv]", host(dv[0, kv]), rdv)
-    if zero:
-        assert torch.all(dk[0, zero] == 0) and torch.all(dv[0, zero] == 0)
+    rdq, rdk, rdv, rout, rlse = oracle.attn_bwd(case.q, case.k, case.v, case.dout, None,
+                                                cfg.cp_size, rank, case.scale, return_fwd=True,
+                                                lo=lo)
+    tag = f"{name} window {wn} rank {rank} {ws}"
+    compare("out", host(out), rout, tag=tag)
+    compare("lse", host(lse), rlse, tag=tag)
+    compare("dq", host(dq), rdq, tag=tag)
+    compare("dk", host(dk), rdk, tag=tag)
+    compare("dv", host(dv), rdv, tag=tag)

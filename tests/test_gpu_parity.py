@@ -59,9 +59,16 @@ def _small_case(cfg, seed, rank, lengths, Skv):
     return W.make_case(cfg, seed, rank, Skv=Skv, lengths=lengths)
 
 
-@pytest.mark.parametrize("ws", ["stash", "recompute"])
+_small_ref = {}
+
+
+@pytest.mark.parametrize("ws", ["default", "mixed", "recompute"])
 @pytest.mark.parametrize("cid,cfg,seed,rank,lengths,Skv", SMALL, ids=[c[0] for c in SMALL])
 def test_small_full_oracle(cid, cfg, seed, rank, lengths, Skv, ws):
+    """Every output element against the oracle, for each way the backward
+    forms dQ: the whole dS stash (default for these sizes), a stash with a
+    budget of about a third of the worst case (key tiles past it recomputed)
+    and no stash."""
     case = _small_case(cfg, seed, rank, lengths, Skv)
     say(f"[{cid} {ws}] B={case.cfg.B} S={case.cfg.S} cp={case.cfg.cp_size} rank={rank} "
         f"Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} Skv={case.Skv}")
@@ -69,9 +76,11 @@ def test_small_full_oracle(cid, cfg, seed, rank, lengths, Skv, ws):
     out, lse = gpu_fwd(case, d)
     dq, dk, dv = gpu_bwd(case, d, out, lse, ws=ws)
     torch.cuda.synchronize()
-    rdq, rdk, rdv, rout, rlse = oracle.attn_bwd(case.q, case.k, case.v, case.dout, case.doc_ids,
-                                                case.cfg.cp_size, rank, case.scale,
-                                                return_fwd=True)
+    if cid not in _small_ref:
+        _small_ref.clear()
+        _small_ref[cid] = oracle.attn_bwd(case.q, case.k, case.v, case.dout, case.doc_ids,
+                                          case.cfg.cp_size, rank, case.scale, return_fwd=True)
+    rdq, rdk, rdv, rout, rlse = _small_ref[cid]
     compare("out", host(out), rout)
     compare("lse", host(lse), rlse)
     compare("dq", host(dq), rdq)
@@ -119,11 +128,51 @@ def test_empty_inputs():
 
 # ----------------------------------------------------------- full sizes
 
-FULL = [("llama8b", 0, "stash"), ("tp405b", 0, "stash"), ("long_cp", 0, "stash"),
-        ("long_cp", 7, "stash")] + \
-       [("short_docs", r, "stash") for r in range(4)] + \
-       [("single_doc", r, "stash") for r in range(4)] + \
-       [("tp405b", 0, "recompute"), ("long_cp", 7, "recompute"), ("single_doc", 3, "recompute")]
+# Every output element of every listed configuration, rank and seed against
+# the oracle's full tensors, for the backward's dQ paths: the five headline
+# seeds of the 405B share, every rank of each workload's rank list.
+FULL_ELEMENTWISE = (
+    [("llama8b", 0, 0, ws) for ws in ("default", "recompute")] +
+    [("tp405b", s, 0, ws) for s in range(5) for ws in ("default", "recompute")] +
+    [("long_cp", 0, r, ws) for r in (0, 7) for ws in ("default", "full", "recompute")] +
+    [("short_docs", 0, r, ws) for r in range(4) for ws in ("default", "full", "recompute")] +
+    [("single_doc", 0, r, ws) for r in range(4) for ws in ("default", "recompute")])
+
+_full_ref = {}
+
+
+def _full_reference(name, seed, rank, case):
+    key = (name, seed, rank)
+    if key not in _full_ref:
+        _full_ref.clear()
+        _full_ref[key] = oracle.attn_bwd(case.q, case.k, case.v, case.dout, case.doc_ids,
+                                         case.cfg.cp_size, rank, case.scale, return_fwd=True)
+    return _full_ref[key]
+
+
+@pytest.mark.parametrize("name,seed,rank,ws", FULL_ELEMENTWISE,
+                         ids=[f"{n}_s{s}_r{r}_{w}" for n, s, r, w in FULL_ELEMENTWISE])
+def test_full_size_elementwise(name, seed, rank, ws):
+    cfg = W.CONFIGS[name]
+    case = W.make_case(cfg, seed, rank, full=_full_tensors(name, seed))
+    say(f"[{name} seed {seed} rank {rank} {ws}] S={cfg.S} cp={cfg.cp_size} Hq={cfg.Hq} "
+        f"Hkv={cfg.Hkv} D={cfg.D} Skv={case.Skv} docs={len(case.lengths[0])}")
+    d = dev(case)
+    out, lse = gpu_fwd(case, d)
+    dq, dk, dv = gpu_bwd(case, d, out, lse, ws=ws)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, rout, rlse = _full_reference(name, seed, rank, case)
+    tag = f"{name} seed {seed} rank {rank} {ws}"
+    compare("out", host(out), rout, tag=tag)
+    compare("lse", host(lse), rlse, tag=tag)
+    compare("dq", host(dq), rdq, tag=tag)
+    compare("dk", host(dk), rdk, tag=tag)
+    compare("dv", host(dv), rdv, tag=tag)
+
+
+# Sampled extras: rows and keys picked at chunk edges and document starts.
+FULL = [("tp405b", 0, "default"), ("long_cp", 7, "default"), ("short_docs", 2, "default"),
+        ("single_doc", 3, "recompute")]
 
 _full_cache = {}
 
