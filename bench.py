@@ -85,28 +85,48 @@ COPY_CALIBRATION_BYTES = 512 << 20
 FLUSH_BYTES = 512 << 20
 
 
-def sample_clocks(delay_s: float = 0.5):
-    """Current shader and memory clocks (MHz) from rocm-smi, read delay_s
-    seconds into a phase in which the GPU is busy with steps (returns a
-    dict, or None with the reason when rocm-smi is unavailable)."""
-    import re
-    import subprocess
-    if "rocprof" in os.environ.get("LD_PRELOAD", ""):
-        # under a profiler every new process loads its library, and the
-        # rocm-smi launcher would replace itself with python after that
-        return {"error": "skipped under a profiler"}
-    time.sleep(delay_s)
+def _gpu_sysfs_dir():
+    """The amdgpu sysfs directory of cuda:0: its PCI address from the device
+    properties, else the only GPU listed under /sys/class/drm."""
+    import glob
+    import torch
     try:
-        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
-                             timeout=30).stdout
-    except Exception as e:  # noqa: BLE001 - reported, not fatal
-        return {"error": f"rocm-smi: {e}"}
-    res = {}
+        p = torch.cuda.get_device_properties(0)
+        hits = glob.glob("/sys/bus/pci/devices/%04x:%02x:%02x.*" % (
+            p.pci_domain_id, p.pci_bus_id, p.pci_device_id))
+        hits = [h for h in hits if os.path.exists(os.path.join(h, "pp_dpm_sclk"))]
+        if len(hits) == 1:
+            return hits[0], None
+    except Exception:  # noqa: BLE001 - fall back to the listing below
+        pass
+    cards = sorted({os.path.realpath(os.path.dirname(f))
+                    for f in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")})
+    if len(cards) == 1:
+        return cards[0], None
+    return None, f"{len(cards)} GPUs with clock files and none matched by PCI address"
+
+
+def sample_clocks(delay_s: float = 0.5):
+    """Current shader, memory and fabric clocks (MHz) of the GPU, read in
+    this process from the amdgpu driver's pp_dpm_* files (the current level
+    is the line marked '*') delay_s seconds into a phase in which the GPU is
+    busy with steps.  Returns a dict, with "error" when unreadable."""
+    import re
+    time.sleep(delay_s)
+    d, err = _gpu_sysfs_dir()
+    if d is None:
+        return {"error": err}
+    res = {"source": d}
     for key in ("sclk", "mclk", "fclk"):
-        m = re.search(key + r"[^\n]*?\((\d+)\s*Mhz\)", out, re.IGNORECASE)
+        try:
+            with open(os.path.join(d, f"pp_dpm_{key}")) as f:
+                txt = f.read()
+        except OSError:
+            continue
+        m = re.search(r"(\d+)\s*Mhz\s*\*", txt, re.IGNORECASE)
         if m:
             res[key + "_mhz"] = int(m.group(1))
-    return res or {"error": "no clock lines in rocm-smi output"}
+    return res if len(res) > 1 else {"error": f"no current level in {d}/pp_dpm_*"}
 
 
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
@@ -213,10 +233,11 @@ def cpu_baseline(runs, min_s: float = 10.0, max_s: float = 30.0) -> dict:
 
 
 def cross_study(args) -> int:
-    """Forward-only measurement of the cross-attention form: 32 packed
-    samples of 100-199 text tokens against 1200-3000 image tokens each
-    (query token p attends to its own sample's image tokens), 16 query heads
-    on 1 KV head, d = 128, one JSON line per seed."""
+    """Forward and backward of the cross-attention form: 32 packed samples of
+    100-199 text tokens against 1200-3000 image tokens each (query token p
+    attends to its own sample's image tokens), 16 query heads on 1 KV head,
+    d = 128; one JSON line with every seed.  Useful FLOPs as for the main
+    line: 4*D per allowed pair and query head forward, 8*D backward."""
     import torch
     import context_gqa_amd as M
     import workloads as W
@@ -226,36 +247,53 @@ def cross_study(args) -> int:
         text, image = W.cross_lengths(32, seed=seed)
         lo, hi = W.cross_bounds(text, image)
         S, Skv, Hq, Hkv, D = sum(text), sum(image), 16, 1, 128
-        q, k, v = (x.cuda() for x in W.cross_tensors(1, S, Skv, Hq, Hkv, D, seed=seed + 100))
+        q, k, v, do = (x.cuda() for x in W.cross_tensors(1, S, Skv, Hq, Hkv, D, seed=seed + 100,
+                                                         dout=True))
         lo_d = torch.from_numpy(lo[None]).cuda()
         hi_d = torch.from_numpy(hi[None]).cuda()
         out = torch.empty_like(q)
         lse = torch.empty(1, S, Hq, dtype=torch.float32, device="cuda")
-        ws = torch.empty(max(M.lib().docmask_gqa_fwd_cross_workspace_size(1, S, Skv, Hq, Hkv, D), 1),
-                         dtype=torch.uint8, device="cuda")
+        dq = torch.empty_like(q)
+        dk = torch.empty(k.shape, dtype=torch.float32, device="cuda")
+        dv = torch.empty_like(dk)
+        wsf = torch.empty(max(M.lib().docmask_gqa_fwd_cross_workspace_size(1, S, Skv, Hq, Hkv, D),
+                              1), dtype=torch.uint8, device="cuda")
+        wsb = torch.empty(max(M.lib().docmask_gqa_bwd_cross_workspace_size(1, S, Skv, Hq, Hkv, D),
+                              1), dtype=torch.uint8, device="cuda")
 
-        def call():
-            M.docmask_gqa_attn_fwd_cross(q, k, v, lo_d, hi_d, out=out, lse=lse, workspace=ws)
+        def fwd():
+            M.docmask_gqa_attn_fwd_cross(q, k, v, lo_d, hi_d, out=out, lse=lse, workspace=wsf)
 
-        for _ in range(args.warmup):
-            call()
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(args.steps):
-            call()
-        b.record()
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / args.steps
+        def bwd():
+            M.docmask_gqa_attn_bwd_cross(q, k, v, out, do, lse, lo_d, hi_d, dq=dq, dk=dk, dv=dv,
+                                         workspace=wsb)
+
+        def timed(fn):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(args.steps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / args.steps
+
+        fms = timed(fwd)
+        bms = timed(bwd)
         pairs = int(np.dot(np.asarray(text, dtype=np.int64), np.asarray(image, dtype=np.int64)))
-        flops = 4.0 * D * pairs * Hq
-        res.append({"seed": seed, "S": S, "Skv": Skv, "fwd_ms": round(ms, 4),
-                    "tflops": round(flops / (ms * 1e-3) / 1e12, 2)})
-        print(f"cross seed {seed}: S={S} Skv={Skv} {ms:.4f} ms {res[-1]['tflops']} TFLOP/s",
-              file=sys.stderr, flush=True)
-    print(json.dumps({"study": "cross-attention forward", "heads": "16/1", "head_dim": 128,
-                      "samples": 32, "text": "100-199", "image": "1200-3000",
+        ff, bf = 4.0 * D * pairs * Hq, 8.0 * D * pairs * Hq
+        res.append({"seed": seed, "S": S, "Skv": Skv, "fwd_ms": round(fms, 4),
+                    "bwd_ms": round(bms, 4),
+                    "fwd_tflops": round(ff / (fms * 1e-3) / 1e12, 2),
+                    "bwd_tflops": round(bf / (bms * 1e-3) / 1e12, 2),
+                    "tflops": round((ff + bf) / ((fms + bms) * 1e-3) / 1e12, 2)})
+        print(f"cross seed {seed}: S={S} Skv={Skv} fwd {fms:.4f} ms bwd {bms:.4f} ms "
+              f"{res[-1]['tflops']} TFLOP/s", file=sys.stderr, flush=True)
+    print(json.dumps({"study": "cross-attention forward + backward", "heads": "16/1",
+                      "head_dim": 128, "samples": 32, "text": "100-199", "image": "1200-3000",
                       "steps": args.steps, "warmup": args.warmup, "per_seed": res}))
     return 0
 
@@ -378,13 +416,15 @@ def main(argv=None) -> int:
                     help="per-rank study instead of the benchmark line: every CP rank of the "
                          "workload, document and single-document masks (see all_ranks)")
     ap.add_argument("--cross", action="store_true",
-                    help="forward-only measurement of the cross-attention form (text queries "
+                    help="forward and backward of the cross-attention form (text queries "
                          "over their own sample's image tokens) instead of the benchmark line")
     ap.add_argument("--no-clocks", action="store_true",
-                    help="skip reading the GPU clocks with rocm-smi during a busy phase")
-    ap.add_argument("--recompute", action="store_true",
-                    help="give the backward its minimum workspace (no dS stash: dQ recomputes "
-                         "the scores)")
+                    help="skip reading the GPU clocks (sysfs) during a busy phase")
+    ap.add_argument("--stash", choices=("default", "full", "recompute"), default="default",
+                    help="backward workspace: the library's default (the whole dS stash, or a "
+                         "2 GiB stash budget for long shares), the whole worst-case stash, "
+                         "or the minimum (no stash: dQ recomputes the scores)")
+    ap.add_argument("--recompute", action="store_true", help="same as --stash recompute")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run three device-to-device copies of 512 MiB (the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -425,6 +465,7 @@ def main(argv=None) -> int:
         return all_ranks(args)
     if args.cross:
         return cross_study(args)
+    stash_kind = "recompute" if args.recompute else args.stash
     cfg = W.CONFIGS[args.workload]
     rank = cfg.ranks[0] if args.rank is None else args.rank
     seeds = [int(s) for s in args.seeds.split(",") if s != ""]
@@ -450,8 +491,9 @@ def main(argv=None) -> int:
                                dtype=torch.uint8, device=dev)
         t["bounds"] = torch.empty(M.docmask_gqa_doc_bounds_size(B, S, Skv) // 4,
                                   dtype=torch.int32, device=dev)
-        wsb_size = (M.docmask_gqa_bwd_workspace_size_min if args.recompute
-                    else M.docmask_gqa_bwd_workspace_size)
+        wsb_size = {"default": M.docmask_gqa_bwd_workspace_size,
+                    "full": M.docmask_gqa_bwd_workspace_size_full,
+                    "recompute": M.docmask_gqa_bwd_workspace_size_min}[stash_kind]
         t["wsb"] = torch.empty(max(1, wsb_size(B, S, Skv, Hq, Hkv, D, cfg.cp_size)),
                                dtype=torch.uint8, device=dev)
         pairs = sum(allowed_pairs(l, S, cfg.cp_size, rank, cfg.window) for l in case.lengths)
@@ -575,8 +617,8 @@ def main(argv=None) -> int:
         detail.append(d)
     del flush
 
-    # Clocks while the GPU is busy with steps (rocm-smi from a second thread,
-    # after the timed measurements so that it cannot disturb them).
+    # Clocks while the GPU is busy with steps (read from sysfs by a second
+    # thread, after the timed measurements so that it cannot disturb them).
     clocks = None
     if not args.no_clocks:
         import threading
@@ -648,8 +690,12 @@ def main(argv=None) -> int:
                    "head_dim": cfg.D, "global_batch": cfg.B, "seeds": seeds,
                    "parallelism": "one CP rank's share on one GPU",
                    "launch": "hip graph per seed" if args.graph else "eager",
-                   "backward": "recompute (minimum workspace)" if args.recompute
-                               else "dS stash",
+                   "backward": {"default": "default workspace (dS stash, 2 GiB budget)",
+                                "full": "whole worst-case dS stash",
+                                "recompute": "recompute (minimum workspace)"}[stash_kind],
+                   "bwd_path": sorted({M.docmask_gqa_bwd_path(
+                       r["case"].cfg.B, cfg.S, r["case"].Skv, cfg.Hq, cfg.Hkv, cfg.D,
+                       cfg.cp_size, rank, r["t"]["wsb"].numel()) for r in runs}),
                    "masking": ("sliding window of %d keys inside the documents: interval "
                                "bounds from the window starts once per step" % cfg.window)
                               if cfg.window is not None else

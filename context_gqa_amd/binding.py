@@ -15,7 +15,9 @@ import os
 from typing import Optional, Tuple
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdocmask_gqa.so")
+# DMGQA_LIBRARY selects another build of the same library (the host
+# sanitizer build of the tests); there is no fallback either way.
+LIB_PATH = os.environ.get("DMGQA_LIBRARY") or os.path.join(HERE, "libdocmask_gqa.so")
 
 DMGQA_OK = 0
 DMGQA_ERR_INVALID_ARG = -1
