@@ -179,17 +179,22 @@ def cross_bounds(text: List[int], image: List[int]):
 
 
 def cross_tensors(B: int, S: int, Skv: int, Hq: int, Hkv: int, D: int, seed: int,
-                  value_scale: float = 0.5):
+                  value_scale: float = 0.5, dout: bool = False):
     """q [B,S,Hq,D] and k, v [B,Skv,Hkv,D], drawn in that order from one CPU
     torch.Generator seeded with `seed` as fp32 N(0,1), scaled, rounded to
-    bf16."""
+    bf16; with dout, also the output gradient [B,S,Hq,D] drawn next as
+    unscaled N(0,1) (as for the self-attention workloads)."""
     import torch
     g = torch.Generator(device="cpu")
     g.manual_seed(seed)
     q = torch.randn(B, S, Hq, D, generator=g, dtype=torch.float32) * value_scale
     k = torch.randn(B, Skv, Hkv, D, generator=g, dtype=torch.float32) * value_scale
     v = torch.randn(B, Skv, Hkv, D, generator=g, dtype=torch.float32) * value_scale
-    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    res = (q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16))
+    if dout:
+        do = torch.randn(B, S, Hq, D, generator=g, dtype=torch.float32)
+        res = res + (do.to(torch.bfloat16),)
+    return res
 
 
 def take_local_rows(x, S: int, cp_size: int, cp_rank: int):
