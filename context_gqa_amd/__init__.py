@@ -11,5 +11,5 @@ from .binding import (  # noqa: F401
     docmask_gqa_kernel_times, docmask_gqa_interval_bounds, docmask_gqa_check_intervals,
     docmask_gqa_attn_fwd_cross, docmask_gqa_check_cross_intervals, docmask_gqa_attn_bwd_cross,
     docmask_gqa_bwd_workspace_size_full, docmask_gqa_bwd_path, DMGQA_BWD_PATH_RECOMPUTE,
-    DMGQA_BWD_PATH_STASH, DMGQA_BWD_PATH_MIXED,
+    DMGQA_BWD_PATH_STASH, DMGQA_BWD_PATH_MIXED, docmask_gqa_attn_fwd_noalloc,
 )

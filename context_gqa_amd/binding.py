@@ -49,6 +49,9 @@ SIGNATURES = {
     "docmask_gqa_attn_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                             _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                             _vp, _vp, _vp, _sz, _vp]),
+    "docmask_gqa_attn_fwd_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                                    _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
+                                                    _vp, _vp]),
     "docmask_gqa_attn_fwd_bounds": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                                    _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp,
                                                    _sz, _vp]),
@@ -247,6 +250,36 @@ def docmask_gqa_attn_fwd(q, k, v, doc_ids=None, cu_seqlens=None, *, cp_size: int
             workspace.numel() * workspace.element_size(), _stream(stream))
     if rc != DMGQA_OK:
         raise DocmaskGQAError(rc, "docmask_gqa_attn_fwd")
+    return out, lse
+
+
+def docmask_gqa_attn_fwd_noalloc(q, k, v, doc_ids=None, cu_seqlens=None, *, cp_size: int,
+                                 cp_rank: int, out, lse, softmax_scale: Optional[float] = None,
+                                 stream=None) -> Tuple["object", "object"]:
+    """The forward with the library's fixed per-GPU scratch instead of a
+    workspace (no allocation in the call; out and lse are the caller's).
+    Calls overlapping on one GPU race."""
+    import torch
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(out, "out", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k and v must be [B, Skv, Hkv, D] matching q")
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Sq, Hq):
+        raise ValueError("out must match q and lse be [B, Sq, Hq]")
+    S = Sq * cp_size
+    doc_ids, cu_seqlens, n_docs = _docs(doc_ids, cu_seqlens, B, S)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    rc = lib().docmask_gqa_attn_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(doc_ids), _ptr(cu_seqlens), n_docs, B, S, Skv, Hq, Hkv,
+        D, cp_size, cp_rank, float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream))
+    if rc != DMGQA_OK:
+        raise DocmaskGQAError(rc, "docmask_gqa_attn_fwd_noalloc")
     return out, lse
 
 

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <unordered_set>
 #include <vector>
 
@@ -328,6 +329,44 @@ size_t cross_workspace_bytes(const Shape& s) {
   return align_up((size_t)s.B * nt * sizeof(int32_t));
 }
 
+// Scratch of the allocation-free forward (docmask_gqa_attn_fwd_noalloc): the
+// forward's workspace (document bounds, scan aggregates, tile order) in a
+// fixed device array instead of caller memory.  Each GPU the library runs on
+// holds its own copy until the process ends.  In host code `scratch` is only
+// a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr size_t kNoAllocScratchBytes = 8u << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch (the device of `st`, or the
+// current one for the null stream), looked up on the device's first call.
+int scratch_for(hipStream_t st, char** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return DMGQA_ERR_HIP;
+  int dev = cur;
+  if (st != nullptr) {
+    hipDevice_t d;
+    if (hipStreamGetDevice(st, &d) != hipSuccess) return DMGQA_ERR_HIP;
+    dev = (int)d;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return DMGQA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return DMGQA_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return DMGQA_ERR_HIP;
+    if (e != hipSuccess || p == nullptr) return DMGQA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return DMGQA_OK;
+}
+
 }  // namespace
 }  // namespace dmgqa
 
@@ -398,6 +437,27 @@ int docmask_gqa_attn_fwd(const void* q, const void* k, const void* v, const int3
                          void* workspace, size_t workspace_bytes, void* stream) {
   return fwd_impl(q, k, v, doc_ids, cu_seqlens, n_docs, nullptr, B, S, Skv, Hq, Hkv, D, cp_size,
                   cp_rank, softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+int docmask_gqa_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                                 const int32_t* doc_ids, const int32_t* cu_seqlens,
+                                 int32_t n_docs, int32_t B, int32_t S, int32_t Skv, int32_t Hq,
+                                 int32_t Hkv, int32_t D, int32_t cp_size, int32_t cp_rank,
+                                 float softmax_scale, void* out, float* lse, void* stream) {
+  // The scalar checks of the forward, and the size limit of the scratch,
+  // come before any HIP call.
+  Shape s;
+  int rc = check_shape(B, S, Skv, Hq, Hkv, D, cp_size, cp_rank, &s);
+  if (rc != DMGQA_OK) return rc;
+  if (!scale_ok(softmax_scale)) return DMGQA_ERR_INVALID_ARG;
+  if (s.empty) return DMGQA_OK;
+  const size_t need = layout(s, false).total_min;
+  if (need > kNoAllocScratchBytes) return DMGQA_ERR_WORKSPACE;
+  char* ws = nullptr;
+  rc = scratch_for(reinterpret_cast<hipStream_t>(stream), &ws);
+  if (rc != DMGQA_OK) return rc;
+  return fwd_impl(q, k, v, doc_ids, cu_seqlens, n_docs, nullptr, B, S, Skv, Hq, Hkv, D, cp_size,
+                  cp_rank, softmax_scale, out, lse, ws, kNoAllocScratchBytes, stream);
 }
 
 int docmask_gqa_attn_fwd_bounds(const void* q, const void* k, const void* v,

@@ -88,6 +88,26 @@ size_t docmask_gqa_fwd_workspace_size(int32_t B, int32_t S, int32_t Skv,
                                       int32_t Hq, int32_t Hkv, int32_t D,
                                       int32_t cp_size);
 
+/* The forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation and arguments as
+ * docmask_gqa_attn_fwd, with the workspace in a fixed array of 8 MiB that
+ * the library holds on each GPU it runs on until the process ends.  The
+ * call allocates nothing; its first call on a device looks up that device's
+ * array.  Shapes whose forward workspace (docmask_gqa_fwd_workspace_size)
+ * exceeds 8 MiB are rejected with DMGQA_ERR_WORKSPACE before any HIP call
+ * (about B * Skv <= 10^6 key positions at 16 query heads per KV head).
+ * Every call on one GPU uses that GPU's single array, so calls that overlap
+ * in time on one GPU (different streams or host threads) race and must be
+ * ordered by the caller. */
+int docmask_gqa_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                                 const int32_t* doc_ids,
+                                 const int32_t* cu_seqlens, int32_t n_docs,
+                                 int32_t B, int32_t S, int32_t Skv, int32_t Hq,
+                                 int32_t Hkv, int32_t D, int32_t cp_size,
+                                 int32_t cp_rank, float softmax_scale,
+                                 void* out, float* lse, void* stream);
+
 /* Backward workspace.  Besides the scheduling arrays (the minimum below),
  * the backward can use a stash for dS in bf16 (blocks of 32 query rows x 128
  * keys of one key tile): the dK/dV kernel, which forms dS anyway, stores it,

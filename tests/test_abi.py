@@ -349,3 +349,30 @@ def test_cross_bwd_rejects(kw, want):
 def test_cross_bwd_empty_is_noop():
     assert _cross_bwd(B=0, q=None, lo=None, nbytes=0) == 0
     assert _cross_bwd(S=0, nbytes=0) == 0
+
+
+# ---------------------------------------------------------------- allocation-free forward
+
+def _noalloc(**kw):
+    b = _Buf()
+    a = dict(q=b.p, k=b.p, v=b.p, doc=b.p, cu=None, n_docs=0, B=1, S=512, Skv=512, Hq=4, Hkv=1,
+             D=64, cp=1, rank=0, scale=0.125, out=b.p, lse=b.p)
+    a.update(kw)
+    return M.lib().docmask_gqa_attn_fwd_noalloc(a["q"], a["k"], a["v"], a["doc"], a["cu"],
+                                                a["n_docs"], a["B"], a["S"], a["Skv"], a["Hq"],
+                                                a["Hkv"], a["D"], a["cp"], a["rank"], a["scale"],
+                                                a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(B=8, S=131072, Skv=131072, Hq=16, Hkv=1, D=128, cp=16), WS),   # beyond 8 MiB
+    (dict(scale=-0.5), INV), (dict(scale=0.0), INV), (dict(Hq=6, Hkv=4), INV),
+    (dict(S=500, Skv=500, cp=3), INV), (dict(D=96), UNS), (dict(rank=1), INV),
+])
+def test_noalloc_rejects_before_hip(kw, want):
+    """Scalar checks and the scratch limit come before any HIP call."""
+    assert _noalloc(**kw) == want
+
+
+def test_noalloc_empty_is_noop():
+    assert _noalloc(B=0, q=None, out=None) == 0
