@@ -59,6 +59,21 @@ __device__ __forceinline__ void dma_lds16(const void* sbase, unsigned voff, unsi
                : "memory");
 }
 
+// The value of lane l ^ 32 (the other half of the wave), by
+// v_permlane32_swap on two copies: it moves lanes 0-31 of the second
+// register into lanes 32-63 of the first and lanes 32-63 of the first into
+// lanes 0-31 of the second.  Written as assembly on two distinct operands,
+// with wait states around it (measured on gfx950: without them, lanes 32-63
+// of the first register read a stale value; the compiler builtin, given the
+// same value twice, returned the first result for both).  No LDS round trip,
+// unlike a shuffle through ds_bpermute.
+__device__ __forceinline__ float other_half(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 4\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 4" : "+v"(a), "+v"(b));
+  // lanes 0-31: a = own, b = lane + 32; lanes 32-63: a = lane - 32, b = own
+  return (threadIdx.x & 32) ? a : b;
+}
+
 __device__ __forceinline__ bf16x8 ld_lds_b128(const char* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
@@ -222,11 +237,15 @@ __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict
         if ((unsigned)(c + 32 - lo_rel) > span) s1[r] = -INFINITY;
       }
     }
-    float mx = max3f(s0[0], s1[0], s0[1]);
+    // row maximum: two independent max3 chains, then the other half-wave
+    float ma = max3f(s0[0], s0[1], s0[2]), mb = max3f(s1[0], s1[1], s1[2]);
 #pragma unroll
-    for (int r = 1; r < 15; ++r) mx = max3f(mx, s1[r], s0[r + 1]);
-    mx = max3f(mx, s1[15], s1[15]);
-    mx = fmaxf(mx, xor32(mx));
+    for (int r = 3; r < 15; r += 2) {
+      ma = max3f(ma, s0[r], s0[r + 1]);
+      mb = max3f(mb, s1[r], s1[r + 1]);
+    }
+    float mx = max3f(ma, mb, fmaxf(s0[15], s1[15]));
+    mx = fmaxf(mx, other_half(mx));
     const bool need = mx != -INFINITY && (m == -INFINITY || (mx - m) * g.scale_log2 > kRescaleLog2);
     if (__any(need)) {
       const float mnew = need ? mx : m;
@@ -286,7 +305,7 @@ __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict
     }
   }
 
-  const float lt = l + xor32(l);
+  const float lt = l + other_half(l);
   if (valid) {
     const float inv = 1.f / lt;
     u16* orow = out + qoff;
