@@ -74,8 +74,8 @@ int check_docs_args(const int32_t* doc_ids, const int32_t* cu, int n_docs, const
 // bounds, the schedule, the row statistics and the partial-sum slots); the
 // dS stash and the partial dQ buffer follow (see plan_stash).
 struct Layout {
-  size_t dstart, dend, agg, order, rowstat, hdr, tile_info, items, tile_rows, partial,
-      total_min;
+  size_t dstart, dend, agg, order, rowstat, hdr, tile_info, items, tile_rows, partial, dout16,
+      scale_parts, total_min;
   int nkt, max_split_base;
 };
 
@@ -141,6 +141,9 @@ Layout layout(const Shape& s, bool backward) {
     L.tile_rows = off; off = align_up(off + ntiles * sizeof(int4));
     const size_t slots = 2 * (size_t)L.max_split_base * s.Hkv;
     L.partial = off; off = align_up(off + slots * 2 * kDkdvBN * s.D * sizeof(float));
+    // dO' = dO * 2^eo in fp16, and the partial maxima of the exponent scan
+    L.dout16 = off; off = align_up(off + (size_t)s.B * s.Sq * s.Hq * s.D * 2);
+    L.scale_parts = off; off = align_up(off + kScaleParts * sizeof(int2));
   }
   L.total_min = off;
   return L;
@@ -520,7 +523,23 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   const u16* doh = static_cast<const u16*>(dout);
   u16* dqh = static_cast<u16*>(dq);
 
-  hipError_t e;
+  u16* dout16 = reinterpret_cast<u16*>(ws + L.dout16);
+  int2* scale_parts = reinterpret_cast<int2*>(ws + L.scale_parts);
+
+  // Every path: the exponent scan of dO and V, then the schedule with the
+  // row statistics (and dO' in fp16) for the dK/dV kernel.
+  timing_begin(kKScale, st);
+  hipError_t e = launch_scale_scan(doh, (long long)s.B * s.Sq * s.Hq * D, vh,
+                                   (long long)s.B * s.Skv * s.Hkv * D, scale_parts, st);
+  timing_end(kKScale, st);
+  if (e != hipSuccess) return DMGQA_ERR_HIP;
+  timing_begin(kKSchedRowstat, st);
+  e = launch_sched_rowstat(D, nullptr, dstart, dend, g, L.nkt, L.max_split_base,
+                           plan.mode == kRecompute ? 0 : plan.budget, hdr, tile_info, items,
+                           tile_rows, plan.mode == kRecompute ? nullptr : dq_order, oh, doh, lse,
+                           scale_parts, Lbuf, Nbuf, dout16, st);
+  timing_end(kKSchedRowstat, st);
+  if (e != hipSuccess) return DMGQA_ERR_HIP;
   if (plan.mode != kRecompute) {
     // The dK/dV kernel stores dS of the stashed key tiles; dQ is then one
     // product per stashed key tile, and (mixed) the query tiles that also
@@ -528,45 +547,34 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
     u16* stash = reinterpret_cast<u16*>(ws + plan.stash);
     float* dq_part =
         plan.mode == kMixed ? reinterpret_cast<float*>(ws + plan.dq_part) : nullptr;
-    timing_begin(kKSchedRowstat, st);
-    e = launch_sched_rowstat(D, dstart, dend, g, L.nkt, L.max_split_base, plan.budget, hdr,
-                             tile_info, items, tile_rows, dq_order, oh, doh, lse, Lbuf, Nbuf,
-                             st);
-    timing_end(kKSchedRowstat, st);
-    if (e != hipSuccess) return DMGQA_ERR_HIP;
     timing_begin(kKDkdv, st);
-    e = launch_bwd_dkdv(D, qh, kh, vh, doh, Lbuf, Nbuf, nullptr, dend, hdr, tile_info, items,
+    e = launch_bwd_dkdv(D, qh, kh, vh, dout16, Lbuf, Nbuf, nullptr, dend, hdr, tile_info, items,
                         tile_rows, stash, plan.budget, partial, dk, dv, g, L.nkt, st);
     timing_end(kKDkdv, st);
     if (e != hipSuccess) return DMGQA_ERR_HIP;
     timing_begin(kKDq, st);
     e = launch_bwd_dq_stash(D, kh, dstart, tile_rows, stash, plan.budget, dq_order, dqh, dq_part,
-                            tile_info, partial, dk, dv, g, L.nkt, st);
+                            tile_info, partial, dk, dv, hdr, g, L.nkt, st);
     timing_end(kKDq, st);
     if (e != hipSuccess || plan.mode == kStash) return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
     timing_begin(kKDqRest, st);
-    e = launch_bwd_dq(D, qh, kh, vh, oh, doh, lse, dstart, nullptr, dqh, nullptr, nullptr,
-                      tile_rows, dq_part, g, L.nkt, st);
+    e = launch_bwd_dq(D, qh, kh, vh, oh, doh, lse, dstart, nullptr, dqh, tile_rows, dq_part, g,
+                      L.nkt, st);
     timing_end(kKDqRest, st);
     return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
   }
-  timing_begin(kKSched, st);
-  e = launch_sched_dkdv(nullptr, dend, g, L.nkt, L.max_split_base, 0, hdr, tile_info, items,
-                        tile_rows, st);
-  timing_end(kKSched, st);
-  if (e != hipSuccess) return DMGQA_ERR_HIP;
   timing_begin(kKDq, st);
-  e = launch_bwd_dq(D, qh, kh, vh, oh, doh, lse, dstart, nullptr, dqh, Lbuf, Nbuf, tile_rows,
-                    nullptr, g, L.nkt, st);
+  e = launch_bwd_dq(D, qh, kh, vh, oh, doh, lse, dstart, nullptr, dqh, tile_rows, nullptr, g,
+                    L.nkt, st);
   timing_end(kKDq, st);
   if (e != hipSuccess) return DMGQA_ERR_HIP;
   timing_begin(kKDkdv, st);
-  e = launch_bwd_dkdv(D, qh, kh, vh, doh, Lbuf, Nbuf, nullptr, dend, hdr, tile_info, items,
+  e = launch_bwd_dkdv(D, qh, kh, vh, dout16, Lbuf, Nbuf, nullptr, dend, hdr, tile_info, items,
                       tile_rows, nullptr, 0, partial, dk, dv, g, L.nkt, st);
   timing_end(kKDkdv, st);
   if (e != hipSuccess) return DMGQA_ERR_HIP;
   timing_begin(kKReduce, st);
-  e = launch_bwd_reduce(D, tile_info, partial, dk, dv, g, L.nkt, st);
+  e = launch_bwd_reduce(D, tile_info, partial, dk, dv, hdr, g, L.nkt, st);
   timing_end(kKReduce, st);
   return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
 }
@@ -609,28 +617,38 @@ int bwd_cross_impl(const void* q, const void* k, const void* v, const void* out,
   const u16* vh = static_cast<const u16*>(v);
   const Geo g = make_geo(s, softmax_scale);
 
+  const u16* oh = static_cast<const u16*>(out);
+  const u16* doh = static_cast<const u16*>(dout);
+  u16* dout16 = reinterpret_cast<u16*>(ws + L.dout16);
+  int2* scale_parts = reinterpret_cast<int2*>(ws + L.scale_parts);
+
   timing_begin(kKPrep, st);
   hipError_t e = launch_prep_cross_keys(lo, hi, s.B, s.S, s.Skv, kfirst, kend, st);
   timing_end(kKPrep, st);
   if (e != hipSuccess) return DMGQA_ERR_HIP;
-  timing_begin(kKSched, st);
-  e = launch_sched_dkdv(kfirst, kend, g, L.nkt, L.max_split_base, 0, hdr, tile_info, items,
-                        tile_rows, st);
-  timing_end(kKSched, st);
+  timing_begin(kKScale, st);
+  e = launch_scale_scan(doh, (long long)s.B * s.Sq * s.Hq * D, vh,
+                        (long long)s.B * s.Skv * s.Hkv * D, scale_parts, st);
+  timing_end(kKScale, st);
+  if (e != hipSuccess) return DMGQA_ERR_HIP;
+  timing_begin(kKSchedRowstat, st);
+  e = launch_sched_rowstat(D, kfirst, lo, kend, g, L.nkt, L.max_split_base, 0, hdr, tile_info,
+                           items, tile_rows, nullptr, oh, doh, lse, scale_parts, Lbuf, Nbuf,
+                           dout16, st);
+  timing_end(kKSchedRowstat, st);
   if (e != hipSuccess) return DMGQA_ERR_HIP;
   timing_begin(kKDq, st);
-  e = launch_bwd_dq(D, qh, kh, vh, static_cast<const u16*>(out), static_cast<const u16*>(dout),
-                    lse, lo, hi, static_cast<u16*>(dq), Lbuf, Nbuf, tile_rows, nullptr, g, L.nkt,
-                    st);
+  e = launch_bwd_dq(D, qh, kh, vh, oh, doh, lse, lo, hi, static_cast<u16*>(dq), tile_rows,
+                    nullptr, g, L.nkt, st);
   timing_end(kKDq, st);
   if (e != hipSuccess) return DMGQA_ERR_HIP;
   timing_begin(kKDkdv, st);
-  e = launch_bwd_dkdv(D, qh, kh, vh, static_cast<const u16*>(dout), Lbuf, Nbuf, kfirst, kend, hdr,
-                      tile_info, items, tile_rows, nullptr, 0, partial, dk, dv, g, L.nkt, st);
+  e = launch_bwd_dkdv(D, qh, kh, vh, dout16, Lbuf, Nbuf, kfirst, kend, hdr, tile_info, items,
+                      tile_rows, nullptr, 0, partial, dk, dv, g, L.nkt, st);
   timing_end(kKDkdv, st);
   if (e != hipSuccess) return DMGQA_ERR_HIP;
   timing_begin(kKReduce, st);
-  e = launch_bwd_reduce(D, tile_info, partial, dk, dv, g, L.nkt, st);
+  e = launch_bwd_reduce(D, tile_info, partial, dk, dv, hdr, g, L.nkt, st);
   timing_end(kKReduce, st);
   return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
 }

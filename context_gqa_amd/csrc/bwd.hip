@@ -15,10 +15,9 @@
 // "Numerical stability").
 //
 // Two kernels here (the dK/dV kernel has its own file):
-//   bwd_dq    query-stationary, same tiling as the forward; it also stores
-//             -D and -lse/scale per row for the dK/dV kernel (recompute
-//             path), and finishes the query tiles the dS stash does not
-//             cover (stash with a budget).
+//   bwd_dq    query-stationary, same tiling as the forward: dQ of every
+//             query tile (no stash), or of the key tiles the dS stash does
+//             not cover (stash with a budget).
 //   bwd_reduce adds the partial sums of split key tiles in item order, so the
 //             result does not depend on which workgroup ran which item.
 #include "common.hpp"
@@ -40,7 +39,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ out, const u16* __restrict__ dout, const float* __restrict__ lse,
     const int32_t* __restrict__ dstart, const int32_t* __restrict__ dhi, u16* __restrict__ dq,
-    float* __restrict__ Lbuf, float* __restrict__ Nbuf, const int4* __restrict__ tile_rows,
+    const int4* __restrict__ tile_rows,
     const float* __restrict__ dq_part, Geo g, int nkt) {
   constexpr int BM = kFwdBM, BN = kFwdBN, LD = D, KK = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) u16 sK[2][BN * LD];
@@ -87,12 +86,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     for (int e = 0; e < 8; ++e) dsum = fmaf((float)dop[kk][e], (float)ov[e], dsum);
   }
   const float Dv = dsum + xor32(dsum);
-  const float lse_v = lse[roff];
-  if (Lbuf != nullptr && valid && h == 0) {   // row statistics for the dK/dV kernel
-    Nbuf[roff] = -Dv;
-    Lbuf[roff] = -lse_v / g.scale;
-  }
-  const float lse2 = lse_v * kLog2e;
+  const float lse2 = lse[roff] * kLog2e;
 
   const QTileKeys kr =
       CROSS ? qtile_keys_iv<BM, BN>(row0, ds, dh, g) : qtile_keys<BM, BN>(row0, ds, g);
@@ -193,20 +187,22 @@ template <int D>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const int2* __restrict__ tile_info,
                                                          const float* __restrict__ partial,
                                                          float* __restrict__ dk,
-                                                         float* __restrict__ dv, Geo g, int nkt) {
-  reduce_partials<D>(tile_info, partial, dk, dv, g, nkt, (int)blockIdx.x);
+                                                         float* __restrict__ dv,
+                                                         const SchedHeader* __restrict__ hdr,
+                                                         Geo g, int nkt) {
+  reduce_partials<D>(tile_info, partial, dk, dv, hdr, g, nkt, (int)blockIdx.x);
 }
 
 hipError_t launch_bwd_dq(int D, const u16* q, const u16* k, const u16* v, const u16* out,
                          const u16* dout, const float* lse, const int32_t* dstart,
-                         const int32_t* dhi, u16* dq, float* Lbuf, float* Nbuf,
+                         const int32_t* dhi, u16* dq,
                          const int4* tile_rows, const float* dq_part, const Geo& g, int nkt,
                          hipStream_t st) {
   const int nt = (g.Sq * g.G + kFwdBM - 1) / kFwdBM;
   const unsigned grid = (unsigned)nt * g.B * g.Hkv;
 #define DMGQA_DQ(DD, CC)                                                                     \
-  bwd_dq_kernel<DD, CC><<<grid, 256, 0, st>>>(q, k, v, out, dout, lse, dstart, dhi, dq, Lbuf, \
-                                              Nbuf, tile_rows, dq_part, g, nkt)
+  bwd_dq_kernel<DD, CC><<<grid, 256, 0, st>>>(q, k, v, out, dout, lse, dstart, dhi, dq,       \
+                                              tile_rows, dq_part, g, nkt)
   if (D == 128) {
     if (dhi) DMGQA_DQ(128, true); else DMGQA_DQ(128, false);
   } else {
@@ -217,13 +213,14 @@ hipError_t launch_bwd_dq(int D, const u16* q, const u16* k, const u16* v, const 
 }
 
 hipError_t launch_bwd_reduce(int D, const int2* tile_info, const float* partial, float* dk,
-                             float* dv, const Geo& g, int nkt, hipStream_t st) {
+                             float* dv, const SchedHeader* hdr, const Geo& g, int nkt,
+                             hipStream_t st) {
   if (D == 128)
     bwd_reduce_kernel<128><<<reduce_grid<128>(g, nkt), 256, 0, st>>>(tile_info, partial, dk, dv,
-                                                                      g, nkt);
+                                                                      hdr, g, nkt);
   else
-    bwd_reduce_kernel<64><<<reduce_grid<64>(g, nkt), 256, 0, st>>>(tile_info, partial, dk, dv, g,
-                                                                    nkt);
+    bwd_reduce_kernel<64><<<reduce_grid<64>(g, nkt), 256, 0, st>>>(tile_info, partial, dk, dv,
+                                                                    hdr, g, nkt);
   return hipGetLastError();
 }
 

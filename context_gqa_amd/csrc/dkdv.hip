@@ -17,22 +17,26 @@
 // 4 stages, filled by global->LDS DMA two blocks ahead, the DMA
 // instructions spread over the sub-blocks) and processed in sub-blocks of
 // 32.  Per sub-block and wave:
-//   S = Q K^T and dP = dO V^T      (MFMA; the accumulators start from
-//       -lse/scale and -D, so P = exp2(scale*log2e * S) and dS = P * dP
-//       take one multiply each)
-//   P, dS and their bf16 operands  (VALU)
-//   dV += P^T dO, dK += dS^T Q     (MFMA, transposed LDS reads)
+//   S = Q K^T and dP' = dO' V'^T   (MFMA; the accumulators start from
+//       -lse/scale and -D' = -D * 2^(eo+ev), so P = exp2(scale*log2e * S)
+//       and dS' = P * dP' take one multiply each)
+//   P (fp16), dS' (bf16)           (VALU)
+//   dV' += P^T dO', dK += dS'^T Q  (MFMA, transposed LDS reads)
 //
 // Lane layout (lane l = 16*g4 + j): the S / dP tiles are C[row][key] with
 // key = j; lane group g4 holds the rows 16t + 4*g4 + r (t = 0, 1, r = 0..3).
 // Those 8 values are the A operand (P^T, dS^T: key j, k-slot 8*g4 + e <->
 // row 16(e/4) + 4*g4 + e%4) of the dV / dK products with no data movement.
 //
-// P enters dV as a bf16 hi + lo pair (16 significant bits): dV sums P over
-// every row of the group, and one bf16 rounding of P is not accurate enough
-// for the fp32 result there.
+// dP' and dV' are fp16 products: dV sums P over every row of the group, and
+// one bf16 rounding of P (8 significant bits) is not accurate enough for the
+// fp32 result there; fp16 carries 11.  dO and V enter as dO' = dO * 2^eo (in
+// fp16 from the row-statistics pass) and V' = V * 2^ev (converted per work
+// item), exact power-of-two scales chosen per call so that fp16's exponent
+// range holds them (the exponent scan in prep.hip); dK, dV and the dS stash
+// are scaled back exactly at the end.
 //
-// LDS stage layout (bytes): [Q tile][dO tile][-lse/scale: 64 fp32][-D: 64 fp32].
+// LDS stage layout (bytes): [Q tile][dO' tile][-lse/scale: 64 fp32][-D': 64 fp32].
 // A tile holds 64 rows x D bf16 in groups of 4 sixteen-byte chunks (32
 // elements): group c/4 of row r occupies the 64 bytes at
 // (c/4) * 4096 + 64 * r, and inside them chunk c sits in slot
@@ -112,6 +116,16 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// The same product with fp16 operands (the bits of the bf16-typed registers
+// that hold them reinterpreted).
+__device__ __forceinline__ f32x4 mfma16h(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                               __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
 // B operand of 32 rows x 16 columns from a tile in the grouped layout: two
 // transposed reads, at p (rows 4*g4 + 0..3 of the sub-block) and 16 rows
 // further.
@@ -137,7 +151,7 @@ __device__ __forceinline__ bf16x8 tr_pair(const char* p) {
 template <int D, bool STASH>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
-    const u16* __restrict__ dout, const float* __restrict__ Lbuf, const float* __restrict__ Nbuf,
+    const u16* __restrict__ dout16, const float* __restrict__ Lbuf, const float* __restrict__ Nbuf,
     const int32_t* __restrict__ kfirst, const int32_t* __restrict__ dend,
     SchedHeader* __restrict__ hdr,
     const int2* __restrict__ tile_info, const int2* __restrict__ items,
@@ -210,11 +224,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const int kc = min(key, g.Skv - 1);
     const u16* krow = k + ((size_t)b * g.Skv + kc) * kvstride + (size_t)kvh * D;
     const u16* vrow = v + ((size_t)b * g.Skv + kc) * kvstride + (size_t)kvh * D;
+    // V' = V * 2^ev in fp16 (exact power-of-two scale), for dP' = dO' V'^T
     bf16x8 kop[KS], vop[KS];
+    const float sv = __builtin_amdgcn_ldexpf(1.f, hdr->ev);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       kop[ks] = ld_bf16x8(krow + 32 * ks + 8 * g4);
-      vop[ks] = ld_bf16x8(vrow + 32 * ks + 8 * g4);
+      const bf16x8 vb = ld_bf16x8(vrow + 32 * ks + 8 * g4);
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f16x2 hv = {(_Float16)((float)vb[2 * e] * sv), (_Float16)((float)vb[2 * e + 1] * sv)};
+        w[e] = __builtin_bit_cast(unsigned, hv);
+      }
+      vop[ks] = __builtin_bit_cast(bf16x8, w);
     }
 
     // Rows allowed for this key (key_rows: a contiguous range of the item's
@@ -293,7 +316,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       char* tq = st + Lds::kTile + 64 * 16 * rq + c0 * kGroupBytes;
       static_for<D / 64>([&](auto m) __attribute__((always_inline)) {
         constexpr int M = decltype(m)::value;
-        dma_lds16<128 * M>(dout, nx_qoff, lds_of(tq) + 2 * M * kGroupBytes);
+        dma_lds16<128 * M>(dout16, nx_qoff, lds_of(tq) + 2 * M * kGroupBytes);
       });
     };
 
@@ -375,7 +398,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) pc[t] = mfma16(oa[t][ks], vop[ks], pc[t]);
+        for (int t = 0; t < 2; ++t) pc[t] = mfma16h(oa[t][ks], vop[ks], pc[t]);
     };
 
     // The rest of a sub-block (virtual rows from R, rows q0.. of stage st)
@@ -395,31 +418,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
           if ((unsigned)(cr - lo_rel) >= span) p[e] = 0.f;
         }
       }
-      // hi = bf16(P) (round to nearest even, one conversion per pair), lo =
-      // bf16(P - hi), with hi widened back to fp32 by a shift / mask
-      bf16x8 pop, plo;
+      // P in fp16 (round to nearest even, one conversion per pair) for
+      // dV' += P^T dO' (the dO' tile is fp16)
+      u32x4 pw;
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float p0 = p[e], p1 = p[e + 1];
-        const bf16x2 hp = {(__bf16)p0, (__bf16)p1};
-        const unsigned hw = __builtin_bit_cast(unsigned, hp);
-        const float h0 = __builtin_bit_cast(float, hw << 16);
-        const float h1 = __builtin_bit_cast(float, hw & 0xffff0000u);
-        pop[e] = hp[0];
-        pop[e + 1] = hp[1];
-        plo[e] = (__bf16)(p0 - h0);
-        plo[e + 1] = (__bf16)(p1 - h1);
+      for (int e = 0; e < 4; ++e) {
+        const f16x2 hp = {(_Float16)p[2 * e], (_Float16)p[2 * e + 1]};
+        pw[e] = __builtin_bit_cast(unsigned, hp);
       }
+      const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
       const char* tQ = st + 64 * q0;
       const char* tO = st + Lds::kTile + 64 * q0;
       bf16x8 dot[ND];
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) dot[nd] = tr_pair(tO + (nd >> 1) * kGroupBytes + off_t[nd & 1]);
 #pragma unroll
-      for (int nd = 0; nd < ND; ++nd) {
-        dva[nd] = mfma16(pop, dot[nd], dva[nd]);
-        dva[nd] = mfma16(plo, dot[nd], dva[nd]);
-      }
+      for (int nd = 0; nd < ND; ++nd) dva[nd] = mfma16h(pop, dot[nd], dva[nd]);
       bf16x8 dsop;
 #pragma unroll
       for (int e = 0; e < 8; ++e) dsop[e] = (__bf16)(p[e] * pc[e >> 2][e & 3]);
@@ -504,7 +518,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       dst_v = dv + ((size_t)b * g.Skv + t0) * kvstride + (size_t)kvh * D;
       rstride = kvstride;
     }
-    const float kscale = split_tile ? 1.f : g.scale;
+    // dS' and dV' carry 2^(eo+ev) and 2^eo (fp16 scales); split tiles'
+    // partial sums are scaled by the reduce
+    const float kscale = split_tile ? 1.f : g.scale * hdr->dk_mul;
+    const float vscale = split_tile ? 1.f : hdr->dv_mul;
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd)
 #pragma unroll
@@ -512,13 +529,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
         const int kvloc = wave * kWaveKeys + 4 * g4 + r;
         if (split_tile || t0 + kvloc < g.Skv) {
           dst_k[(size_t)kvloc * rstride + 16 * nd + j] = dka[nd][r] * kscale;
-          dst_v[(size_t)kvloc * rstride + 16 * nd + j] = dva[nd][r];
+          dst_v[(size_t)kvloc * rstride + 16 * nd + j] = dva[nd][r] * vscale;
         }
       }
   }
 }
 
-hipError_t launch_bwd_dkdv(int D, const u16* q, const u16* k, const u16* v, const u16* dout,
+hipError_t launch_bwd_dkdv(int D, const u16* q, const u16* k, const u16* v, const u16* dout16,
                            const float* Lbuf, const float* Nbuf, const int32_t* kfirst,
                            const int32_t* dend, SchedHeader* hdr, const int2* tile_info, const int2* items,
                            const int4* tile_rows, u16* stash, int stash_kvh_blocks,
@@ -526,7 +543,7 @@ hipError_t launch_bwd_dkdv(int D, const u16* q, const u16* k, const u16* v, cons
                            hipStream_t st) {
 #define DMGQA_DKDV(DD, SS)                                                                  \
   bwd_dkdv_kernel<DD, SS><<<kDkdvGrid, kWaves * 64, 0, st>>>(                               \
-      q, k, v, dout, Lbuf, Nbuf, kfirst, dend, hdr, tile_info, items, tile_rows, stash,             \
+      q, k, v, dout16, Lbuf, Nbuf, kfirst, dend, hdr, tile_info, items, tile_rows, stash,             \
       stash_kvh_blocks, partial, dk, dv, g, nkt)
   if (D == 128) {
     if (stash) DMGQA_DKDV(128, true); else DMGQA_DKDV(128, false);

@@ -77,9 +77,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
     const int4* __restrict__ tile_rows, const u16* __restrict__ stash, int stash_kvh_blocks,
     const int32_t* __restrict__ order, u16* __restrict__ dq, float* __restrict__ dq_part,
     const int2* __restrict__ tile_info, const float* __restrict__ partial,
-    float* __restrict__ dk, float* __restrict__ dv, Geo g, int nkt, int dq_grid) {
+    float* __restrict__ dk, float* __restrict__ dv, const SchedHeader* __restrict__ hdr, Geo g,
+    int nkt, int dq_grid) {
   if ((int)blockIdx.x >= dq_grid) {
-    reduce_partials<D>(tile_info, partial, dk, dv, g, nkt, (int)blockIdx.x - dq_grid);
+    reduce_partials<D>(tile_info, partial, dk, dv, hdr, g, nkt, (int)blockIdx.x - dq_grid);
     return;
   }
   using KT = KTile<D>;
@@ -248,6 +249,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
   // sums left here and writes dq.
   const int kt_last = kr.nb > 0 ? kr.b0 + kr.nb - 1 : kr.a0 + kr.na - 1;
   const bool mixed = dq_part != nullptr && ntiles > 0 && trow_b[kt_last].w < 0;
+  // the stash holds dS * 2^(eo+ev) (fp16 scales of the dK/dV kernel)
+  const float dsmul = hdr->dk_mul;
   if (mixed) {
     if (grow < nrows) {
       const int tok = grow / g.G, hh = grow - tok * g.G;
@@ -256,8 +259,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 w = {acc[db][4 * r4], acc[db][4 * r4 + 1], acc[db][4 * r4 + 2],
-                           acc[db][4 * r4 + 3]};
+          const f32x4 w = {acc[db][4 * r4] * dsmul, acc[db][4 * r4 + 1] * dsmul,
+                           acc[db][4 * r4 + 2] * dsmul, acc[db][4 * r4 + 3] * dsmul};
           *reinterpret_cast<f32x4*>(prow + 32 * db + 8 * r4 + 4 * h) = w;
         }
     }
@@ -270,7 +273,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
       for (int r4 = 0; r4 < 4; ++r4) {
         bf16x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[db][4 * r4 + e] * g.scale);
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[db][4 * r4 + e] * (g.scale * dsmul));
         *reinterpret_cast<uint2*>(orow + 32 * db + 8 * r4 + 4 * h) = __builtin_bit_cast(uint2, w);
       }
   }
@@ -279,20 +282,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
 hipError_t launch_bwd_dq_stash(int D, const u16* k, const int32_t* dstart, const int4* tile_rows,
                                const u16* stash, int stash_kvh_blocks, const int32_t* order,
                                u16* dq, float* dq_part, const int2* tile_info,
-                               const float* partial, float* dk, float* dv, const Geo& g, int nkt,
-                               hipStream_t st) {
+                               const float* partial, float* dk, float* dv,
+                               const SchedHeader* hdr, const Geo& g, int nkt, hipStream_t st) {
   const int nqb = (g.Sq * g.G + 127) / 128;
   const unsigned grid = (unsigned)nqb * g.B * g.Hkv;
   if (D == 128)
     bwd_dq_stash_kernel<128><<<grid + reduce_grid<128>(g, nkt), 256, 0, st>>>(
         k, dstart, tile_rows, stash, stash_kvh_blocks, order, dq, dq_part, tile_info, partial, dk,
-        dv, g,
+        dv, hdr, g,
         nkt,
         (int)grid);
   else
     bwd_dq_stash_kernel<64><<<grid + reduce_grid<64>(g, nkt), 256, 0, st>>>(
         k, dstart, tile_rows, stash, stash_kvh_blocks, order, dq, dq_part, tile_info, partial, dk,
-        dv, g,
+        dv, hdr, g,
         nkt,
         (int)grid);
   return hipGetLastError();

@@ -30,8 +30,21 @@ struct SchedHeader {
   int rows_per_split;  // query rows per item
   int n_slots_base;    // partial-sum slots per KV head
   int counter;         // work counter of the persistent dK/dV kernel
-  int pad[12];
+  // Power-of-two scales of the backward's fp16 operands (see
+  // launch_scale_scan): dO' = dO * 2^eo and V' = V * 2^ev, so dP' = dO' V'^T
+  // and dS' = P (dP' - D') carry 2^(eo+ev); dk_mul = 2^-(eo+ev) and
+  // dv_mul = 2^-eo undo them (dK, dQ from dS'; dV from P dO').
+  int eo, ev;
+  float dk_mul, dv_mul;
+  int pad[8];
 };
+
+// Per-call exponent scan of the backward: partial maxima of |dO| and |V|
+// (bf16 magnitude bits), one int2 per block of kScaleParts blocks; the
+// consumers reduce them (scale_exponents in prep.hip).
+constexpr int kScaleParts = 256;
+hipError_t launch_scale_scan(const u16* dout, long long n_dout, const u16* v, long long n_v,
+                             int2* parts, hipStream_t st);
 
 hipError_t launch_prep_docs(const int32_t* doc, int B, int S, int Skv, int32_t* dstart,
                             int32_t* dend, int32_t* agg, hipStream_t st);
@@ -45,29 +58,28 @@ hipError_t launch_prep_interval(const int32_t* lo, int B, int S, int Skv, int32_
 // hi[p] > t, kend = the first p with lo[p] > t; lo, hi [B, S] non-decreasing).
 hipError_t launch_prep_cross_keys(const int32_t* lo, const int32_t* hi, int B, int S, int Skv,
                                   int32_t* kfirst, int32_t* kend, hipStream_t st);
-// dK/dV schedule.  The query positions that reach key t are [t, dend[t])
-// (causal interval masks, kfirst == nullptr) or [kfirst[t], dend[t]).
-// stash_budget: dS stash blocks per KV head; key tiles are stashed in tile
-// order while their blocks fit (tile_rows[x].w = first block, else -1).
-hipError_t launch_sched_dkdv(const int32_t* kfirst, const int32_t* dend, const Geo& g, int nkt,
-                             int max_split_base, int stash_budget, SchedHeader* hdr,
-                             int2* tile_info, int2* items, int4* tile_rows, hipStream_t st);
+// The dK/dV schedule (launch_sched_rowstat, block 0) takes the query
+// positions that reach key t as [t, dend[t]) (causal interval masks, kfirst
+// == nullptr) or [kfirst[t], dend[t]).  stash_budget: dS stash blocks per KV
+// head; key tiles are stashed in tile order while their blocks fit
+// (tile_rows[x].w = first block, else -1).
 // dhi == nullptr: causal interval masks (keys dstart[p] .. p, dstart [B, Skv]);
 // else keys dstart[p] .. dhi[p]-1 with dstart, dhi [B, S].
 hipError_t launch_fwd(int D, const u16* q, const u16* k, const u16* v, const int32_t* dstart,
                       const int32_t* dhi, const int32_t* order, u16* out, float* lse,
                       const Geo& g, hipStream_t st);
-// dQ recomputing S, P and dP.  dhi as for launch_fwd.  Lbuf / Nbuf (may be
-// null): the row statistics for the dK/dV kernel are stored there.  With
+// dQ recomputing S, P and dP.  dhi as for launch_fwd.  With
 // dq_part != null only the query tiles that reach a key tile without stash
 // (tile_rows[b*nkt + kt].w < 0) run, over those key tiles only, adding to
 // the partial sums the stash kernel left in dq_part (fp32 [B, Sq, Hq, D]).
 hipError_t launch_bwd_dq(int D, const u16* q, const u16* k, const u16* v, const u16* out,
                          const u16* dout, const float* lse, const int32_t* dstart,
-                         const int32_t* dhi, u16* dq, float* Lbuf, float* Nbuf,
+                         const int32_t* dhi, u16* dq,
                          const int4* tile_rows, const float* dq_part, const Geo& g, int nkt,
                          hipStream_t st);
-hipError_t launch_bwd_dkdv(int D, const u16* q, const u16* k, const u16* v, const u16* dout,
+// dout16: dO' in fp16 (the row-statistics pass writes it); Nbuf holds
+// -D * 2^(eo+ev).
+hipError_t launch_bwd_dkdv(int D, const u16* q, const u16* k, const u16* v, const u16* dout16,
                            const float* Lbuf, const float* Nbuf, const int32_t* kfirst,
                            const int32_t* dend,
                            SchedHeader* hdr, const int2* tile_info, const int2* items,
@@ -75,12 +87,16 @@ hipError_t launch_bwd_dkdv(int D, const u16* q, const u16* k, const u16* v, cons
                            float* partial, float* dk, float* dv, const Geo& g, int nkt,
                            hipStream_t st);
 // Schedule (one block) and per-row statistics (stash path) in one launch.
-hipError_t launch_sched_rowstat(int D, const int32_t* dstart, const int32_t* dend, const Geo& g,
-                                int nkt, int max_split_base, int stash_budget,
-                                SchedHeader* hdr, int2* tile_info,
-                                int2* items, int4* tile_rows, int32_t* dq_order, const u16* out,
-                                const u16* dout, const float* lse, float* Lbuf, float* Nbuf,
-                                hipStream_t st);
+// Schedule (block 0, with the fp16 scales into hdr), the dQ tile order
+// (block 1; skipped when dq_order is null) and the row statistics (the other
+// blocks: -lse/scale, -D * 2^(eo+ev), and dO' = dO * 2^eo in fp16 into
+// dout16) in one launch.  kfirst: see the schedule note above.
+hipError_t launch_sched_rowstat(int D, const int32_t* kfirst, const int32_t* dstart,
+                                const int32_t* dend, const Geo& g, int nkt, int max_split_base,
+                                int stash_budget, SchedHeader* hdr, int2* tile_info, int2* items,
+                                int4* tile_rows, int32_t* dq_order, const u16* out,
+                                const u16* dout, const float* lse, const int2* scale_parts,
+                                float* Lbuf, float* Nbuf, u16* dout16, hipStream_t st);
 // Heaviest-first dispatch order of the forward's query tiles (one block):
 // order[i] = b * nt + tile for B * nt items, nt = ceil(Sq * G / kFwdBM).
 hipError_t launch_tile_order_fwd(const int32_t* dstart, const int32_t* dhi, const Geo& g,
@@ -92,15 +108,18 @@ hipError_t launch_tile_order_fwd(const int32_t* dstart, const int32_t* dhi, cons
 hipError_t launch_bwd_dq_stash(int D, const u16* k, const int32_t* dstart, const int4* tile_rows,
                                const u16* stash, int stash_kvh_blocks, const int32_t* order, u16* dq,
                                float* dq_part, const int2* tile_info, const float* partial,
-                               float* dk, float* dv, const Geo& g, int nkt, hipStream_t st);
+                               float* dk, float* dv, const SchedHeader* hdr, const Geo& g, int nkt,
+                               hipStream_t st);
 hipError_t launch_bwd_reduce(int D, const int2* tile_info, const float* partial, float* dk,
-                             float* dv, const Geo& g, int nkt, hipStream_t st);
+                             float* dv, const SchedHeader* hdr, const Geo& g, int nkt,
+                             hipStream_t st);
 
 // Kernel timing (benchmark use): when enabled, each launch below is
 // bracketed by HIP events recorded on the launch stream.
 enum KernelId {
-  kKPrep = 0, kKFwd, kKSched, kKDq, kKDkdv, kKReduce, kKSchedRowstat, kKOrder,
+  kKPrep = 0, kKFwd, kKDq, kKDkdv, kKReduce, kKSchedRowstat, kKOrder,
   kKDqRest,   // dQ of the key tiles beyond the stash budget (recomputed)
+  kKScale,    // exponent scan of dO and V (fp16 scales)
   kNumKernels
 };
 void timing_begin(int kernel, hipStream_t st);

@@ -300,14 +300,6 @@ __device__ void sched_body(const int32_t* __restrict__ kfirst, const int32_t* __
   (void)sh;
 }
 
-__global__ __launch_bounds__(kScanThreads) void sched_dkdv(
-    const int32_t* __restrict__ kfirst, const int32_t* __restrict__ dend, Geo g, int nkt,
-    int max_split_base, int stash_budget, SchedHeader* __restrict__ hdr,
-    int2* __restrict__ tile_info, int2* __restrict__ items, int4* __restrict__ tile_rows) {
-  sched_body(kfirst, dend, g, nkt, max_split_base, stash_budget, hdr, tile_info, items,
-             tile_rows);
-}
-
 // Cross-attention: query position p attends to keys lo[p] .. hi[p]-1 with lo
 // and hi non-decreasing and lo[p] < hi[p] (keys indexed apart from the
 // queries).  The positions that reach key t are then one contiguous run:
@@ -339,29 +331,163 @@ __global__ __launch_bounds__(256) void prep_cross_keys(const int32_t* __restrict
   kend[(size_t)b * Skv + t] = a;
 }
 
+// ---------------------------------------------------------------- fp16 scales
+//
+// The dK/dV kernel multiplies dO with V (dP) and P with dO (dV) in fp16:
+// fp16 carries 11 significant bits (bf16: 8), enough for P in the dV sum
+// over every row of a KV group, but only 5 exponent bits.  dO and V are
+// therefore scaled by powers of two chosen per call, eo and ev, so that the
+// largest magnitude of each lies in [2^14, 2^15): bf16 values down to
+// 2^-28 of the maximum stay exact, smaller ones keep an absolute error
+// below 2^-39 of the maximum.  The scales are exact, and undone exactly at
+// the end (dk_mul, dv_mul of SchedHeader).
+
+// Partial maxima of the bf16 magnitude bits (sign cleared: for finite values
+// the bit order is the value order) of dO and V: kScaleParts blocks of
+// kScaleThreads threads, each thread keeping eight 16-byte loads in flight
+// over its strided share of each tensor.
+constexpr int kScaleThreads = 256;
+constexpr int kScaleUnroll = 8;
+
+__device__ __forceinline__ unsigned max_mag8(uint4 w, unsigned m) {
+  const unsigned ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) m = max(m, max(ws[e] & 0x7fffu, (ws[e] >> 16) & 0x7fffu));
+  return m;
+}
+
+__global__ __launch_bounds__(kScaleThreads) void scale_scan(const u16* __restrict__ dout,
+                                                            long long n_dout,
+                                                            const u16* __restrict__ v,
+                                                            long long n_v,
+                                                            int2* __restrict__ parts) {
+  __shared__ int red[2][kScaleThreads / 64];
+  const long long step = (long long)kScaleParts * kScaleThreads * 8;   // elements per pass
+  const long long first = ((long long)blockIdx.x * kScaleThreads + threadIdx.x) * 8;
+  auto scan = [&](const u16* x, long long n) {
+    unsigned m = 0;
+    long long i = first;
+    // whole groups of kScaleUnroll loads
+    for (; i + (kScaleUnroll - 1) * step + 8 <= n; i += kScaleUnroll * step) {
+      uint4 w[kScaleUnroll];
+#pragma unroll
+      for (int u = 0; u < kScaleUnroll; ++u)
+        w[u] = *reinterpret_cast<const uint4*>(x + i + u * step);
+#pragma unroll
+      for (int u = 0; u < kScaleUnroll; ++u) m = max_mag8(w[u], m);
+    }
+    for (; i < n; i += step) {
+      if (i + 8 <= n)
+        m = max_mag8(*reinterpret_cast<const uint4*>(x + i), m);
+      else
+        for (long long t = i; t < n; ++t) m = max(m, (unsigned)(x[t] & 0x7fffu));
+    }
+    return m;
+  };
+  unsigned mo = scan(dout, n_dout);
+  unsigned mv = scan(v, n_v);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mo = max(mo, (unsigned)__shfl_xor((int)mo, o));
+    mv = max(mv, (unsigned)__shfl_xor((int)mv, o));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = (int)mo;
+    red[1][threadIdx.x >> 6] = (int)mv;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int a = 0, b = 0;
+    for (int w = 0; w < kScaleThreads / 64; ++w) { a = max(a, red[0][w]); b = max(b, red[1][w]); }
+    parts[blockIdx.x] = make_int2(a, b);
+  }
+}
+
+// 2^e placing the largest magnitude (bf16 bits m, sign cleared) in
+// [2^14, 2^15): e = 14 - floor(log2 max); 0 for an all-zero tensor; the
+// exponent field of a subnormal counts as -126.  Kept within [-100, 100].
+__device__ __forceinline__ int scale_exp(unsigned m) {
+  if (m == 0) return 0;
+  const int e = (int)(m >> 7) - 127;
+  return min(max(14 - max(e, -126), -100), 100);
+}
+
+// (eo, ev) from the partial maxima, reduced by the first wave; every thread
+// of the block gets them.
+static_assert(kScaleParts % 64 == 0, "partial maxima per lane");
+__device__ int2 scale_exponents(const int2* __restrict__ parts) {
+  __shared__ int2 ex;
+  if (threadIdx.x < 64) {
+    unsigned mo = 0, mv = 0;
+#pragma unroll
+    for (int k = 0; k < kScaleParts / 64; ++k) {
+      const int2 p = parts[threadIdx.x + 64 * k];
+      mo = max(mo, (unsigned)p.x);
+      mv = max(mv, (unsigned)p.y);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      mo = max(mo, (unsigned)__shfl_xor((int)mo, o));
+      mv = max(mv, (unsigned)__shfl_xor((int)mv, o));
+    }
+    if (threadIdx.x == 0) ex = make_int2(scale_exp(mo), scale_exp(mv));
+  }
+  __syncthreads();
+  return ex;
+}
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 // Per query row: -lse/scale (start value of the S accumulators of the dK/dV
-// kernel, so that P = exp2(scale*log2e * S)) and -D, D = <dO, O> (start
-// value of its dP accumulators, so that dS = P * dP).  D/8 lanes per row,
-// one 16-byte chunk of out and dout each; `blk` indexes groups of
-// kScanThreads / (D/8) rows.
+// kernel, so that P = exp2(scale*log2e * S)), -D * 2^(eo+ev) with
+// D = <dO, O> (start value of its dP' accumulators, so that dS' = P * dP'),
+// and the row of dO' = dO * 2^eo in fp16.  D/8 lanes per row, one 16-byte
+// chunk of out and dout each, kRowstatPasses rows per lane; `blk` indexes
+// groups of kRowstatPasses * kScanThreads / (D/8) rows.
+constexpr int kRowstatPasses = 4;
 template <int D>
 __device__ void rowstat_rows(const u16* __restrict__ out, const u16* __restrict__ dout,
                              const float* __restrict__ lse, float* __restrict__ Lbuf,
-                             float* __restrict__ Nbuf, int nrows, float inv_scale, int blk) {
+                             float* __restrict__ Nbuf, u16* __restrict__ dout16, int nrows,
+                             float inv_scale, const int2* __restrict__ scale_parts, int blk) {
   constexpr int kLanes = D / 8;
-  const int row = blk * (kScanThreads / kLanes) + (int)(threadIdx.x / kLanes);
+  constexpr int kRowsPass = kScanThreads / kLanes;
   const int j = threadIdx.x % kLanes;
-  const int rr = min(row, nrows - 1);
-  const bf16x8 o = ld_bf16x8(out + (size_t)rr * D + 8 * j);
-  const bf16x8 d = ld_bf16x8(dout + (size_t)rr * D + 8 * j);
-  float acc = 0.f;
+  const int row0 = blk * (kRowsPass * kRowstatPasses) + (int)(threadIdx.x / kLanes);
+  // every load of the block's rows is issued before the exponents are read
+  bf16x8 o[kRowstatPasses], d[kRowstatPasses];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)d[e], acc);
+  for (int p = 0; p < kRowstatPasses; ++p) {
+    const int rr = min(row0 + p * kRowsPass, nrows - 1);
+    o[p] = ld_bf16x8(out + (size_t)rr * D + 8 * j);
+    d[p] = ld_bf16x8(dout + (size_t)rr * D + 8 * j);
+  }
+  const int2 ex = scale_exponents(scale_parts);
+  const float so = __builtin_amdgcn_ldexpf(1.f, ex.x);
+  const float sn = -__builtin_amdgcn_ldexpf(1.f, ex.x + ex.y);
 #pragma unroll
-  for (int o2 = kLanes / 2; o2 > 0; o2 >>= 1) acc += __shfl_xor(acc, o2, kLanes);
-  if (j == 0 && row < nrows) {
-    Nbuf[row] = -acc;
-    Lbuf[row] = -lse[row] * inv_scale;
+  for (int p = 0; p < kRowstatPasses; ++p) {
+    const int row = row0 + p * kRowsPass;
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)o[p][e], (float)d[p][e], acc);
+#pragma unroll
+    for (int o2 = kLanes / 2; o2 > 0; o2 >>= 1) acc += __shfl_xor(acc, o2, kLanes);
+    if (row < nrows) {
+      unsigned w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f16x2 hp = {(_Float16)((float)d[p][2 * e] * so),
+                          (_Float16)((float)d[p][2 * e + 1] * so)};
+        w[e] = __builtin_bit_cast(unsigned, hp);
+      }
+      *reinterpret_cast<uint4*>(dout16 + (size_t)row * D + 8 * j) =
+          make_uint4(w[0], w[1], w[2], w[3]);
+      if (j == 0) {
+        Nbuf[row] = acc * sn;
+        Lbuf[row] = -lse[row] * inv_scale;
+      }
+    }
   }
 }
 
@@ -468,25 +594,35 @@ __global__ __launch_bounds__(kScanThreads) void tile_order_fwd_iv(
   tile_order_body<kFwdBN, true>(dstart, g, order, dhi);
 }
 
-// The dK/dV schedule (block 0), the dQ tile order (block 1) and the row
-// statistics (the other blocks) in one launch: the single-block parts then
-// run beside the row statistics.
+// The dK/dV schedule and the fp16 scales (block 0), the dQ tile order
+// (block 1, unless dq_order is null) and the row statistics (the other
+// blocks) in one launch: the single-block parts run beside the row
+// statistics.
 template <int D>
 __global__ __launch_bounds__(kScanThreads) void sched_rowstat(
-    const int32_t* __restrict__ dstart, const int32_t* __restrict__ dend, Geo g, int nkt,
-    int max_split_base, int stash_budget, SchedHeader* __restrict__ hdr,
-    int2* __restrict__ tile_info,
-    int2* __restrict__ items, int4* __restrict__ tile_rows, int32_t* __restrict__ dq_order,
-    const u16* __restrict__ out, const u16* __restrict__ dout, const float* __restrict__ lse,
-    float* __restrict__ Lbuf, float* __restrict__ Nbuf) {
-  if (blockIdx.x == 0)
-    sched_body(nullptr, dend, g, nkt, max_split_base, stash_budget, hdr, tile_info, items,
+    const int32_t* __restrict__ kfirst, const int32_t* __restrict__ dstart,
+    const int32_t* __restrict__ dend, Geo g, int nkt, int max_split_base, int stash_budget,
+    SchedHeader* __restrict__ hdr, int2* __restrict__ tile_info, int2* __restrict__ items,
+    int4* __restrict__ tile_rows, int32_t* __restrict__ dq_order, const u16* __restrict__ out,
+    const u16* __restrict__ dout, const float* __restrict__ lse,
+    const int2* __restrict__ scale_parts, float* __restrict__ Lbuf, float* __restrict__ Nbuf,
+    u16* __restrict__ dout16) {
+  if (blockIdx.x == 0) {
+    const int2 ex = scale_exponents(scale_parts);
+    sched_body(kfirst, dend, g, nkt, max_split_base, stash_budget, hdr, tile_info, items,
                tile_rows);
-  else if (blockIdx.x == 1)
-    tile_order_body<kDkdvBN>(dstart, g, dq_order);
-  else
-    rowstat_rows<D>(out, dout, lse, Lbuf, Nbuf, g.B * g.Sq * g.Hq, 1.f / g.scale,
-                    (int)blockIdx.x - 2);
+    if (threadIdx.x == 0) {
+      hdr->eo = ex.x;
+      hdr->ev = ex.y;
+      hdr->dk_mul = __builtin_amdgcn_ldexpf(1.f, -(ex.x + ex.y));
+      hdr->dv_mul = __builtin_amdgcn_ldexpf(1.f, -ex.x);
+    }
+  } else if (blockIdx.x == 1) {
+    if (dq_order != nullptr) tile_order_body<kDkdvBN>(dstart, g, dq_order);
+  } else {
+    rowstat_rows<D>(out, dout, lse, Lbuf, Nbuf, dout16, g.B * g.Sq * g.Hq, 1.f / g.scale,
+                    scale_parts, (int)blockIdx.x - 2);
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -515,14 +651,6 @@ hipError_t launch_prep_cu(const int32_t* cu, int n_docs, int Skv, int32_t* dstar
   return hipGetLastError();
 }
 
-hipError_t launch_sched_dkdv(const int32_t* kfirst, const int32_t* dend, const Geo& g, int nkt,
-                             int max_split_base, int stash_budget, SchedHeader* hdr,
-                             int2* tile_info, int2* items, int4* tile_rows, hipStream_t st) {
-  sched_dkdv<<<1, kScanThreads, 0, st>>>(kfirst, dend, g, nkt, max_split_base, stash_budget, hdr,
-                                         tile_info, items, tile_rows);
-  return hipGetLastError();
-}
-
 hipError_t launch_prep_cross_keys(const int32_t* lo, const int32_t* hi, int B, int S, int Skv,
                                   int32_t* kfirst, int32_t* kend, hipStream_t st) {
   dim3 grid((Skv + 255) / 256, B);
@@ -530,23 +658,28 @@ hipError_t launch_prep_cross_keys(const int32_t* lo, const int32_t* hi, int B, i
   return hipGetLastError();
 }
 
-hipError_t launch_sched_rowstat(int D, const int32_t* dstart, const int32_t* dend, const Geo& g,
-                                int nkt, int max_split_base, int stash_budget,
-                                SchedHeader* hdr, int2* tile_info,
-                                int2* items, int4* tile_rows, int32_t* dq_order, const u16* out,
-                                const u16* dout, const float* lse, float* Lbuf, float* Nbuf,
-                                hipStream_t st) {
+hipError_t launch_sched_rowstat(int D, const int32_t* kfirst, const int32_t* dstart,
+                                const int32_t* dend, const Geo& g, int nkt, int max_split_base,
+                                int stash_budget, SchedHeader* hdr, int2* tile_info, int2* items,
+                                int4* tile_rows, int32_t* dq_order, const u16* out,
+                                const u16* dout, const float* lse, const int2* scale_parts,
+                                float* Lbuf, float* Nbuf, u16* dout16, hipStream_t st) {
   const int nrows = g.B * g.Sq * g.Hq;
-  const int rows_per_block = kScanThreads / (D / 8);
+  const int rows_per_block = kScanThreads / (D / 8) * kRowstatPasses;
   const unsigned grid = 2u + (unsigned)((nrows + rows_per_block - 1) / rows_per_block);
-  if (D == 128)
-    sched_rowstat<128><<<grid, kScanThreads, 0, st>>>(dstart, dend, g, nkt, max_split_base,
-                                                      stash_budget, hdr, tile_info, items, tile_rows, dq_order, out,
-                                                      dout, lse, Lbuf, Nbuf);
-  else
-    sched_rowstat<64><<<grid, kScanThreads, 0, st>>>(dstart, dend, g, nkt, max_split_base,
-                                                     stash_budget, hdr, tile_info, items, tile_rows, dq_order, out,
-                                                     dout, lse, Lbuf, Nbuf);
+#define DMGQA_RS(DD)                                                                          \
+  sched_rowstat<DD><<<grid, kScanThreads, 0, st>>>(kfirst, dstart, dend, g, nkt, max_split_base, \
+                                                   stash_budget, hdr, tile_info, items,          \
+                                                   tile_rows, dq_order, out, dout, lse,          \
+                                                   scale_parts, Lbuf, Nbuf, dout16)
+  if (D == 128) DMGQA_RS(128); else DMGQA_RS(64);
+#undef DMGQA_RS
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_scan(const u16* dout, long long n_dout, const u16* v, long long n_v,
+                             int2* parts, hipStream_t st) {
+  scale_scan<<<kScaleParts, kScaleThreads, 0, st>>>(dout, n_dout, v, n_v, parts);
   return hipGetLastError();
 }
 

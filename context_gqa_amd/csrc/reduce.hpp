@@ -17,11 +17,12 @@ inline unsigned reduce_grid(const Geo& g, int nkt) {
 }
 
 // Workgroup `blk`: adds the tile's partial slots in item order (so the
-// result does not depend on timing) and writes dK (scaled) or dV.
+// result does not depend on timing) and writes dK or dV (scaled).
 template <int D>
 __device__ __forceinline__ void reduce_partials(const int2* __restrict__ tile_info,
                                                 const float* __restrict__ partial,
                                                 float* __restrict__ dk, float* __restrict__ dv,
+                                                const SchedHeader* __restrict__ hdr,
                                                 const Geo& g, int nkt, int blk) {
   constexpr int BN = kDkdvBN;
   constexpr int kChunks = reduce_chunks<D>();
@@ -42,7 +43,8 @@ __device__ __forceinline__ void reduce_partials(const int2* __restrict__ tile_in
     const size_t slot = (size_t)(info.y + sp) * g.Hkv + kvh;
     s += *reinterpret_cast<const f32x4*>(partial + slot * 2 * BN * D + e);
   }
-  if (which == 0) s *= g.scale;
+  // the partial sums of dK and dV carry the fp16 scales (SchedHeader)
+  s *= which == 0 ? g.scale * hdr->dk_mul : hdr->dv_mul;
   float* dst = (which == 0 ? dk : dv) + ((size_t)b * g.Skv + t0 + kvloc) * kvstride +
                (size_t)kvh * D + col;
   *reinterpret_cast<f32x4*>(dst) = s;

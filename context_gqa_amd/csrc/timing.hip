@@ -26,9 +26,9 @@ std::vector<hipEvent_t> g_pool;  // all events ever created
 size_t g_used = 0;
 int g_open[kNumKernels];
 
-const char* kNames[kNumKernels] = {"prep",       "fwd",           "sched_dkdv", "bwd_dq",
-                                   "bwd_dkdv",   "bwd_reduce",    "sched_rowstat",
-                                   "tile_order", "bwd_dq_rest"};
+const char* kNames[kNumKernels] = {"prep",          "fwd",        "bwd_dq",
+                                   "bwd_dkdv",      "bwd_reduce", "sched_rowstat",
+                                   "tile_order",    "bwd_dq_rest", "scale_scan"};
 
 hipEvent_t take_event() {
   if (g_used == g_pool.size()) {

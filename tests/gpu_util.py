@@ -75,12 +75,12 @@ def bwd_workspace_bytes(case: W.Case, ws: str) -> int:
 EXPECT_PATH = {"full": (M.DMGQA_BWD_PATH_STASH,), "mixed": (M.DMGQA_BWD_PATH_MIXED,),
                "recompute": (M.DMGQA_BWD_PATH_RECOMPUTE,),
                "default": (M.DMGQA_BWD_PATH_STASH, M.DMGQA_BWD_PATH_MIXED)}
-# which of these kernels each path launches (the schedule with the row
-# statistics for the stash paths, the schedule alone without the stash, the
-# recomputing dQ of the key tiles past the budget)
-PATH_KERNELS = {M.DMGQA_BWD_PATH_STASH: {"sched_rowstat"},
-                M.DMGQA_BWD_PATH_MIXED: {"sched_rowstat", "bwd_dq_rest"},
-                M.DMGQA_BWD_PATH_RECOMPUTE: {"sched_dkdv"}}
+# which of these kernels each path launches (the recomputing dQ of the key
+# tiles past the stash budget; the separate partial-sum reduce, which the
+# stash paths run inside the dQ-from-stash launch)
+PATH_KERNELS = {M.DMGQA_BWD_PATH_STASH: set(),
+                M.DMGQA_BWD_PATH_MIXED: {"bwd_dq_rest"},
+                M.DMGQA_BWD_PATH_RECOMPUTE: {"bwd_reduce"}}
 
 
 def gpu_bwd(case: W.Case, d, out, lse, use_cu=False, ws="default"):
@@ -110,6 +110,7 @@ def gpu_bwd(case: W.Case, d, out, lse, use_cu=False, ws="default"):
     watched = set().union(*PATH_KERNELS.values())
     launched = {k for k in watched if ran.get(k, (0.0, 0))[1] > 0}
     assert launched == PATH_KERNELS[path], (ws, path, ran)
+    assert ran.get("bwd_dkdv", (0.0, 0))[1] == 1 and ran.get("bwd_dq", (0.0, 0))[1] == 1, ran
     return res
 
 
