@@ -328,8 +328,8 @@ def all_ranks(args) -> int:
     lse = torch.empty(B, Sq, Hq, dtype=torch.float32, device=dev)
     dk = torch.empty(B, S, Hkv, D, dtype=torch.float32, device=dev)
     dv = torch.empty_like(dk)
-    bounds = torch.empty(M.docmask_gqa_doc_bounds_size(B, S, S) // 4, dtype=torch.int32,
-                         device=dev)
+    plan = torch.empty(M.docmask_gqa_batch_plan_size(B, S, S, Hq, Hkv, D, cfg.cp_size) // 4,
+                       dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     res = {"study": "per-rank imbalance", "workload": f"{cfg.name}: {cfg.description}",
            "cp_size": cfg.cp_size, "ranks": ranks, "seeds": seeds, "reps": args.steps,
@@ -352,17 +352,18 @@ def all_ranks(args) -> int:
                 fl = useful_flops(pairs, Hq, D, cfg.backward)
 
                 def fwd():
-                    M.docmask_gqa_doc_bounds(doc, B=B, S=S, Skv=Skv, out=bounds)
+                    M.docmask_gqa_batch_plan(doc, B=B, S=S, Skv=Skv, Hq=Hq, Hkv=Hkv, D=D,
+                                             cp_size=cfg.cp_size, cp_rank=r, out=plan)
                     M.docmask_gqa_attn_fwd(q, k, v, cp_size=cfg.cp_size, cp_rank=r,
                                            softmax_scale=case.scale, out=out, lse=lse,
-                                           workspace=wsf, bounds=bounds)
+                                           workspace=wsf, plan=plan)
 
                 def bwd():
                     if not cfg.backward:
                         return
                     M.docmask_gqa_attn_bwd(q, k, v, out, do, lse, cp_size=cfg.cp_size, cp_rank=r,
                                            softmax_scale=case.scale, dq=dq, dk=dkr, dv=dvr,
-                                           workspace=wsb, bounds=bounds)
+                                           workspace=wsb, plan=plan)
                 for _ in range(args.warmup):
                     fwd(); bwd()
                 ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -491,6 +492,9 @@ def main(argv=None) -> int:
                                dtype=torch.uint8, device=dev)
         t["bounds"] = torch.empty(M.docmask_gqa_doc_bounds_size(B, S, Skv) // 4,
                                   dtype=torch.int32, device=dev)
+        t["plan"] = torch.empty(M.docmask_gqa_batch_plan_size(B, S, Skv, Hq, Hkv, D,
+                                                              cfg.cp_size) // 4,
+                                dtype=torch.int32, device=dev)
         wsb_size = {"default": M.docmask_gqa_bwd_workspace_size,
                     "full": M.docmask_gqa_bwd_workspace_size_full,
                     "recompute": M.docmask_gqa_bwd_workspace_size_min}[stash_kind]
@@ -501,19 +505,25 @@ def main(argv=None) -> int:
                          flops=useful_flops(pairs, Hq, D, cfg.backward),
                          bytes=algorithmic_bytes(case, cfg.backward)))
 
+    def mask_kw(t):
+        return {"bounds": t["bounds"]} if "lo" in t else {"plan": t["plan"]}
+
     def fwd_part(i):
-        """The document bounds of seed i's batch (computed from doc_ids in
-        every step) and the forward."""
+        """The masking input of seed i's batch, built from doc_ids in every
+        step (the batch plan: bounds and query-tile orders; interval masks:
+        their bounds), and the forward."""
         r = runs[i % len(runs)]
         t, case = r["t"], r["case"]
+        B_, Sq_, Hq_, D_ = t["q"].shape
         if "lo" in t:
             M.docmask_gqa_interval_bounds(t["lo"], Skv=case.Skv, out=t["bounds"])
         else:
-            M.docmask_gqa_doc_bounds(t["doc"], B=case.cfg.B, S=cfg.S, Skv=case.Skv,
-                                     out=t["bounds"])
+            M.docmask_gqa_batch_plan(t["doc"], B=B_, S=cfg.S, Skv=case.Skv, Hq=Hq_,
+                                     Hkv=cfg.Hkv, D=D_, cp_size=cfg.cp_size, cp_rank=rank,
+                                     out=t["plan"])
         M.docmask_gqa_attn_fwd(t["q"], t["k"], t["v"], cp_size=cfg.cp_size, cp_rank=rank,
                                softmax_scale=case.scale, out=t["out"], lse=t["lse"],
-                               workspace=t["wsf"], bounds=t["bounds"])
+                               workspace=t["wsf"], **mask_kw(t))
 
     def bwd_part(i):
         r = runs[i % len(runs)]
@@ -522,7 +532,7 @@ def main(argv=None) -> int:
             M.docmask_gqa_attn_bwd(t["q"], t["k"], t["v"], t["out"], t["dout"], t["lse"],
                                    cp_size=cfg.cp_size, cp_rank=rank, softmax_scale=case.scale,
                                    dq=t["dq"], dk=t["dk"], dv=t["dv"], workspace=t["wsb"],
-                                   bounds=t["bounds"])
+                                   **mask_kw(t))
 
     def step(i):
         """One step on seed i's inputs, on the current stream: the document
@@ -699,8 +709,9 @@ def main(argv=None) -> int:
                    "masking": ("sliding window of %d keys inside the documents: interval "
                                "bounds from the window starts once per step" % cfg.window)
                               if cfg.window is not None else
-                              "document bounds from doc_ids once per step, read by the "
-                              "forward and the backward"},
+                              "batch plan (document bounds and both query-tile orders) "
+                              "from doc_ids once per step, read by the forward and the "
+                              "backward"},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "per_seed_tflops": [round(x, 2) for x in per_seed],
         "median_seed_tflops": round(float(np.median(per_seed)), 2),

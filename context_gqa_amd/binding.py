@@ -58,6 +58,14 @@ SIGNATURES = {
     "docmask_gqa_attn_bwd_bounds": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                                    _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                                    _f32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "docmask_gqa_batch_plan_size": (_sz, [_i32] * 7),
+    "docmask_gqa_batch_plan": (ctypes.c_int, [_vp, _vp] + [_i32] * 9 + [_vp, _sz, _vp]),
+    "docmask_gqa_attn_fwd_plan": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                                 _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp,
+                                                 _sz, _vp]),
+    "docmask_gqa_attn_bwd_plan": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                                 _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                 _f32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "docmask_gqa_doc_bounds_size": (_sz, [_i32] * 3),
     "docmask_gqa_doc_bounds": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "docmask_gqa_check_docs": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
@@ -170,6 +178,23 @@ def _bounds_ok(bounds, doc_ids, cu_seqlens, B, S, Skv):
         raise ValueError("bounds is smaller than docmask_gqa_doc_bounds_size(B, S, Skv)")
 
 
+def _mask_form(doc_ids, cu_seqlens, bounds, plan, B, S, Skv, Hq, Hkv, D, cp_size):
+    """Which masking input a call got: "docs" (doc_ids / cu_seqlens),
+    "bounds" or "plan" (exactly one form)."""
+    import torch
+    if plan is not None:
+        if bounds is not None or doc_ids is not None or cu_seqlens is not None:
+            raise ValueError("pass plan alone, without bounds / doc_ids / cu_seqlens")
+        _need(plan, "plan", torch.int32, 1)
+        if plan.numel() * 4 < docmask_gqa_batch_plan_size(B, S, Skv, Hq, Hkv, D, cp_size):
+            raise ValueError("plan is smaller than docmask_gqa_batch_plan_size")
+        return "plan"
+    if bounds is not None:
+        _bounds_ok(bounds, doc_ids, cu_seqlens, B, S, Skv)
+        return "bounds"
+    return "docs"
+
+
 def _docs(doc_ids, cu_seqlens, B, S):
     import torch
     if (doc_ids is None) == (cu_seqlens is None):
@@ -206,14 +231,39 @@ def docmask_gqa_doc_bounds(doc_ids=None, cu_seqlens=None, *, B: int, S: int, Skv
     return out
 
 
+def docmask_gqa_batch_plan_size(B, S, Skv, Hq, Hkv, D, cp_size) -> int:
+    return int(lib().docmask_gqa_batch_plan_size(B, S, Skv, Hq, Hkv, D, cp_size))
+
+
+def docmask_gqa_batch_plan(doc_ids=None, cu_seqlens=None, *, B: int, S: int, Skv: int, Hq: int,
+                           Hkv: int, D: int, cp_size: int, cp_rank: int, out=None,
+                           stream=None):
+    """Bounds and query-tile orders of one batch layout as one int32 buffer,
+    for the attention calls' `plan=` argument (its first 2 * B * Skv entries
+    are the bounds array of docmask_gqa_doc_bounds)."""
+    import torch
+    doc_ids, cu_seqlens, n_docs = _docs(doc_ids, cu_seqlens, B, S)
+    need = docmask_gqa_batch_plan_size(B, S, Skv, Hq, Hkv, D, cp_size)
+    dev = (doc_ids if doc_ids is not None else cu_seqlens).device
+    if out is None:
+        out = torch.empty(max(need // 4, 1), dtype=torch.int32, device=dev)
+    _need(out, "plan", torch.int32, 1)
+    rc = lib().docmask_gqa_batch_plan(_ptr(doc_ids), _ptr(cu_seqlens), n_docs, B, S, Skv, Hq,
+                                      Hkv, D, cp_size, cp_rank, _ptr(out), out.numel() * 4,
+                                      _stream(stream))
+    if rc != DMGQA_OK:
+        raise DocmaskGQAError(rc, "docmask_gqa_batch_plan")
+    return out
+
+
 def docmask_gqa_attn_fwd(q, k, v, doc_ids=None, cu_seqlens=None, *, cp_size: int,
                          cp_rank: int, softmax_scale: Optional[float] = None, out=None,
                          lse=None, workspace=None, stream=None,
-                         bounds=None) -> Tuple["object", "object"]:
+                         bounds=None, plan=None) -> Tuple["object", "object"]:
     """out [B,Sq,Hq,D] bf16 and lse [B,Sq,Hq] fp32 of the rank's local rows.
     q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] bf16; doc_ids [B,S] or cu_seqlens
     [n_docs+1] int32 with S = Sq * cp_size, or bounds from
-    docmask_gqa_doc_bounds."""
+    docmask_gqa_doc_bounds, or a plan from docmask_gqa_batch_plan."""
     import torch
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 4)
@@ -223,10 +273,9 @@ def docmask_gqa_attn_fwd(q, k, v, doc_ids=None, cu_seqlens=None, *, cp_size: int
     if tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != D:
         raise ValueError("k and v must be [B, Skv, Hkv, D] matching q")
     S = Sq * cp_size
-    if bounds is None:
+    form = _mask_form(doc_ids, cu_seqlens, bounds, plan, B, S, Skv, Hq, Hkv, D, cp_size)
+    if form == "docs":
         doc_ids, cu_seqlens, n_docs = _docs(doc_ids, cu_seqlens, B, S)
-    else:
-        _bounds_ok(bounds, doc_ids, cu_seqlens, B, S, Skv)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -238,16 +287,17 @@ def docmask_gqa_attn_fwd(q, k, v, doc_ids=None, cu_seqlens=None, *, cp_size: int
     need = docmask_gqa_fwd_workspace_size(B, S, Skv, Hq, Hkv, D, cp_size)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    if bounds is None:
+    if form == "docs":
         rc = lib().docmask_gqa_attn_fwd(
             _ptr(q), _ptr(k), _ptr(v), _ptr(doc_ids), _ptr(cu_seqlens), n_docs, B, S, Skv, Hq,
             Hkv, D, cp_size, cp_rank, float(softmax_scale), _ptr(out), _ptr(lse),
             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     else:
-        rc = lib().docmask_gqa_attn_fwd_bounds(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(bounds), B, S, Skv, Hq, Hkv, D, cp_size, cp_rank,
-            float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
-            workspace.numel() * workspace.element_size(), _stream(stream))
+        fn = lib().docmask_gqa_attn_fwd_bounds if form == "bounds" else \
+            lib().docmask_gqa_attn_fwd_plan
+        rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(bounds if form == "bounds" else plan), B, S,
+                Skv, Hq, Hkv, D, cp_size, cp_rank, float(softmax_scale), _ptr(out), _ptr(lse),
+                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     if rc != DMGQA_OK:
         raise DocmaskGQAError(rc, "docmask_gqa_attn_fwd")
     return out, lse
@@ -285,9 +335,11 @@ def docmask_gqa_attn_fwd_noalloc(q, k, v, doc_ids=None, cu_seqlens=None, *, cp_s
 
 def docmask_gqa_attn_bwd(q, k, v, out, dout, lse, doc_ids=None, cu_seqlens=None, *,
                          cp_size: int, cp_rank: int, softmax_scale: Optional[float] = None,
-                         dq=None, dk=None, dv=None, workspace=None, stream=None, bounds=None):
+                         dq=None, dk=None, dv=None, workspace=None, stream=None, bounds=None,
+                         plan=None):
     """dq [B,Sq,Hq,D] bf16, dk/dv [B,Skv,Hkv,D] fp32.  Masking by doc_ids /
-    cu_seqlens, or by bounds from docmask_gqa_doc_bounds."""
+    cu_seqlens, by bounds from docmask_gqa_doc_bounds, or by a plan from
+    docmask_gqa_batch_plan."""
     import torch
     for t, n in ((q, "q"), (out, "out"), (dout, "dout")):
         _need(t, n, torch.bfloat16, 4)
@@ -301,10 +353,9 @@ def docmask_gqa_attn_bwd(q, k, v, out, dout, lse, doc_ids=None, cu_seqlens=None,
     if tuple(v.shape) != tuple(k.shape):
         raise ValueError("k and v must match")
     S = Sq * cp_size
-    if bounds is None:
+    form = _mask_form(doc_ids, cu_seqlens, bounds, plan, B, S, Skv, Hq, Hkv, D, cp_size)
+    if form == "docs":
         doc_ids, cu_seqlens, n_docs = _docs(doc_ids, cu_seqlens, B, S)
-    else:
-        _bounds_ok(bounds, doc_ids, cu_seqlens, B, S, Skv)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if dq is None:
@@ -319,18 +370,19 @@ def docmask_gqa_attn_bwd(q, k, v, out, dout, lse, doc_ids=None, cu_seqlens=None,
     need = docmask_gqa_bwd_workspace_size(B, S, Skv, Hq, Hkv, D, cp_size)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    if bounds is None:
+    if form == "docs":
         rc = lib().docmask_gqa_attn_bwd(
             _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(doc_ids),
             _ptr(cu_seqlens), n_docs, B, S, Skv, Hq, Hkv, D, cp_size, cp_rank,
             float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
     else:
-        rc = lib().docmask_gqa_attn_bwd_bounds(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(bounds), B, S,
-            Skv, Hq, Hkv, D, cp_size, cp_rank, float(softmax_scale), _ptr(dq), _ptr(dk),
-            _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
-            _stream(stream))
+        fn = lib().docmask_gqa_attn_bwd_bounds if form == "bounds" else \
+            lib().docmask_gqa_attn_bwd_plan
+        rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                _ptr(bounds if form == "bounds" else plan), B, S, Skv, Hq, Hkv, D, cp_size,
+                cp_rank, float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                workspace.numel() * workspace.element_size(), _stream(stream))
     if rc != DMGQA_OK:
         raise DocmaskGQAError(rc, "docmask_gqa_attn_bwd")
     return dq, dk, dv

@@ -267,7 +267,7 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* doc_ids
              const int32_t* cu_seqlens, int32_t n_docs, const int32_t* bounds, int32_t B,
              int32_t S, int32_t Skv, int32_t Hq, int32_t Hkv, int32_t D, int32_t cp_size,
              int32_t cp_rank, float softmax_scale, void* out, float* lse, void* workspace,
-             size_t workspace_bytes, void* stream) {
+             size_t workspace_bytes, void* stream, const int32_t* order_in = nullptr) {
   Shape s;
   int rc = check_shape(B, S, Skv, Hq, Hkv, D, cp_size, cp_rank, &s);
   if (rc != DMGQA_OK) return rc;
@@ -289,11 +289,17 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* doc_ids
   rc = call_bounds(doc_ids, cu_seqlens, n_docs, bounds, s, ws, L, st, &dstart, &dend);
   if (rc != DMGQA_OK) return rc;
   const Geo g = make_geo(s, softmax_scale);
-  int32_t* order = reinterpret_cast<int32_t*>(ws + L.order);
-  timing_begin(kKOrder, st);
-  hipError_t e = launch_tile_order_fwd(dstart, nullptr, g, order, st);
-  timing_end(kKOrder, st);
-  if (e != hipSuccess) return DMGQA_ERR_HIP;
+  // the query-tile order: the plan's, or built here
+  const int32_t* order = order_in;
+  hipError_t e = hipSuccess;
+  if (!order) {
+    int32_t* o = reinterpret_cast<int32_t*>(ws + L.order);
+    timing_begin(kKOrder, st);
+    e = launch_tile_order_fwd(dstart, nullptr, g, o, st);
+    timing_end(kKOrder, st);
+    if (e != hipSuccess) return DMGQA_ERR_HIP;
+    order = o;
+  }
   timing_begin(kKFwd, st);
   e = launch_fwd(D, static_cast<const u16*>(q), static_cast<const u16*>(k),
                  static_cast<const u16*>(v), dstart, nullptr, order, static_cast<u16*>(out), lse, g,
@@ -482,7 +488,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
              const float* lse, const int32_t* doc_ids, const int32_t* cu_seqlens, int32_t n_docs,
              const int32_t* bounds, int32_t B, int32_t S, int32_t Skv, int32_t Hq, int32_t Hkv,
              int32_t D, int32_t cp_size, int32_t cp_rank, float softmax_scale, void* dq,
-             float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream) {
+             float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream,
+             const int32_t* dq_order_in = nullptr) {
   Shape s;
   int rc = check_shape(B, S, Skv, Hq, Hkv, D, cp_size, cp_rank, &s);
   if (rc != DMGQA_OK) return rc;
@@ -515,7 +522,10 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   int2* items = reinterpret_cast<int2*>(ws + L.items);
   int4* tile_rows = reinterpret_cast<int4*>(ws + L.tile_rows);
   float* partial = reinterpret_cast<float*>(ws + L.partial);
-  int32_t* dq_order = reinterpret_cast<int32_t*>(ws + L.order);
+  // the dQ kernel's query-tile order: the plan's, or built beside the row
+  // statistics
+  int32_t* dq_order_ws = dq_order_in ? nullptr : reinterpret_cast<int32_t*>(ws + L.order);
+  const int32_t* dq_order = dq_order_in ? dq_order_in : dq_order_ws;
   const u16* qh = static_cast<const u16*>(q);
   const u16* kh = static_cast<const u16*>(k);
   const u16* vh = static_cast<const u16*>(v);
@@ -536,7 +546,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   timing_begin(kKSchedRowstat, st);
   e = launch_sched_rowstat(D, nullptr, dstart, dend, g, L.nkt, L.max_split_base,
                            plan.mode == kRecompute ? 0 : plan.budget, hdr, tile_info, items,
-                           tile_rows, plan.mode == kRecompute ? nullptr : dq_order, oh, doh, lse,
+                           tile_rows, plan.mode == kRecompute ? nullptr : dq_order_ws, oh, doh, lse,
                            scale_parts, Lbuf, Nbuf, dout16, st);
   timing_end(kKSchedRowstat, st);
   if (e != hipSuccess) return DMGQA_ERR_HIP;
@@ -706,6 +716,102 @@ int docmask_gqa_doc_bounds(const int32_t* doc_ids, const int32_t* cu_seqlens, in
   int32_t* dend = bounds + (size_t)B * Skv;
   return prep_bounds(doc_ids, cu_seqlens, n_docs, B, S, Skv, dstart, dend,
                      bounds + 2 * (size_t)B * Skv, st);
+}
+
+}  // extern "C"
+
+namespace dmgqa {
+
+// Batch plan layout (int32 offsets): the bounds as in a bounds array
+// (dstart [B, Skv] then dend [B, Skv]), the forward's and the dQ kernel's
+// query-tile orders (B * nt each, nt query tiles of kFwdBM rows per batch
+// row), then the bounds scan's block aggregates (scratch of the multi-launch
+// path).
+struct BatchPlanLayout {
+  size_t fwd_order, dq_order, agg, total_ints;
+};
+
+BatchPlanLayout batch_plan_layout(const Shape& s) {
+  BatchPlanLayout P;
+  const size_t nt = ((size_t)s.Sq * s.G + kFwdBM - 1) / kFwdBM;
+  P.fwd_order = 2 * (size_t)s.B * s.Skv;
+  P.dq_order = P.fwd_order + (size_t)s.B * nt;
+  P.agg = P.dq_order + (size_t)s.B * nt;
+  P.total_ints = P.agg + 2 * (size_t)s.B * (((size_t)s.Skv + 1023) / 1024);
+  return P;
+}
+
+}  // namespace dmgqa
+
+extern "C" {
+
+size_t docmask_gqa_batch_plan_size(int32_t B, int32_t S, int32_t Skv, int32_t Hq, int32_t Hkv,
+                                   int32_t D, int32_t cp_size) {
+  Shape s;
+  if (check_shape(B, S, S, Hq, Hkv, D, cp_size, 0, &s) != DMGQA_OK) return 0;
+  if (Skv <= 0 || Skv > S || s.empty) return 0;
+  s.Skv = Skv;
+  return batch_plan_layout(s).total_ints * sizeof(int32_t);
+}
+
+int docmask_gqa_batch_plan(const int32_t* doc_ids, const int32_t* cu_seqlens, int32_t n_docs,
+                           int32_t B, int32_t S, int32_t Skv, int32_t Hq, int32_t Hkv, int32_t D,
+                           int32_t cp_size, int32_t cp_rank, int32_t* plan, size_t plan_bytes,
+                           void* stream) {
+  Shape s;
+  int rc = check_shape(B, S, Skv, Hq, Hkv, D, cp_size, cp_rank, &s);
+  if (rc != DMGQA_OK) return rc;
+  if (s.empty) return DMGQA_OK;
+  rc = check_docs_args(doc_ids, cu_seqlens, n_docs, s);
+  if (rc != DMGQA_OK) return rc;
+  if (!plan || !aligned(plan, 4)) return DMGQA_ERR_INVALID_ARG;
+  const BatchPlanLayout P = batch_plan_layout(s);
+  if (plan_bytes < P.total_ints * sizeof(int32_t)) return DMGQA_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const Geo g = make_geo(s, 1.f);   // the orders do not depend on the scale
+  int32_t* dstart = plan;
+  int32_t* dend = plan + (size_t)s.B * s.Skv;
+  rc = prep_bounds(doc_ids, cu_seqlens, n_docs, s.B, s.S, s.Skv, dstart, dend, plan + P.agg, st);
+  if (rc != DMGQA_OK) return rc;
+  timing_begin(kKOrder, st);
+  const hipError_t e = launch_plan_orders(dstart, g, plan + P.fwd_order, plan + P.dq_order, st);
+  timing_end(kKOrder, st);
+  return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
+}
+
+int docmask_gqa_attn_fwd_plan(const void* q, const void* k, const void* v, const int32_t* plan,
+                              int32_t B, int32_t S, int32_t Skv, int32_t Hq, int32_t Hkv,
+                              int32_t D, int32_t cp_size, int32_t cp_rank, float softmax_scale,
+                              void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  Shape s;
+  const int rc = check_shape(B, S, Skv, Hq, Hkv, D, cp_size, cp_rank, &s);
+  if (rc != DMGQA_OK) return rc;
+  if (s.empty) return fwd_impl(q, k, v, nullptr, nullptr, 0, plan, B, S, Skv, Hq, Hkv, D,
+                               cp_size, cp_rank, softmax_scale, out, lse, workspace,
+                               workspace_bytes, stream);
+  if (!plan) return DMGQA_ERR_INVALID_ARG;
+  return fwd_impl(q, k, v, nullptr, nullptr, 0, plan, B, S, Skv, Hq, Hkv, D, cp_size, cp_rank,
+                  softmax_scale, out, lse, workspace, workspace_bytes, stream,
+                  plan + batch_plan_layout(s).fwd_order);
+}
+
+int docmask_gqa_attn_bwd_plan(const void* q, const void* k, const void* v, const void* out,
+                              const void* dout, const float* lse, const int32_t* plan,
+                              int32_t B, int32_t S, int32_t Skv, int32_t Hq, int32_t Hkv,
+                              int32_t D, int32_t cp_size, int32_t cp_rank, float softmax_scale,
+                              void* dq, float* dk, float* dv, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  Shape s;
+  const int rc = check_shape(B, S, Skv, Hq, Hkv, D, cp_size, cp_rank, &s);
+  if (rc != DMGQA_OK) return rc;
+  if (s.empty) return bwd_impl(q, k, v, out, dout, lse, nullptr, nullptr, 0, plan, B, S, Skv, Hq,
+                               Hkv, D, cp_size, cp_rank, softmax_scale, dq, dk, dv, workspace,
+                               workspace_bytes, stream);
+  if (!plan) return DMGQA_ERR_INVALID_ARG;
+  return bwd_impl(q, k, v, out, dout, lse, nullptr, nullptr, 0, plan, B, S, Skv, Hq, Hkv, D,
+                  cp_size, cp_rank, softmax_scale, dq, dk, dv, workspace, workspace_bytes, stream,
+                  plan + batch_plan_layout(s).dq_order);
 }
 
 int docmask_gqa_interval_bounds(const int32_t* lo, int32_t B, int32_t S, int32_t Skv,

@@ -42,7 +42,7 @@ struct SchedHeader {
 // Per-call exponent scan of the backward: partial maxima of |dO| and |V|
 // (bf16 magnitude bits), one int2 per block of kScaleParts blocks; the
 // consumers reduce them (scale_exponents in prep.hip).
-constexpr int kScaleParts = 256;
+constexpr int kScaleParts = 512;
 hipError_t launch_scale_scan(const u16* dout, long long n_dout, const u16* v, long long n_v,
                              int2* parts, hipStream_t st);
 
@@ -99,6 +99,9 @@ hipError_t launch_sched_rowstat(int D, const int32_t* kfirst, const int32_t* dst
                                 float* Lbuf, float* Nbuf, u16* dout16, hipStream_t st);
 // Heaviest-first dispatch order of the forward's query tiles (one block):
 // order[i] = b * nt + tile for B * nt items, nt = ceil(Sq * G / kFwdBM).
+// Both query-tile orders of a batch plan from its bounds (two workgroups).
+hipError_t launch_plan_orders(const int32_t* dstart, const Geo& g, int32_t* fwd_order,
+                              int32_t* dq_order, hipStream_t st);
 hipError_t launch_tile_order_fwd(const int32_t* dstart, const int32_t* dhi, const Geo& g,
                                  int32_t* order, hipStream_t st);
 // dQ from the dS stash, and (in workgroups appended to its grid) the sum of

@@ -594,6 +594,24 @@ __global__ __launch_bounds__(kScanThreads) void tile_order_fwd_iv(
   tile_order_body<kFwdBN, true>(dstart, g, order, dhi);
 }
 
+// Plan of one batch layout: the bounds (the scans above) and both query-tile
+// orders (forward, BN = kFwdBN; dQ, BN = kDkdvBN) that the attention calls
+// read instead of computing them per call.  (A single-workgroup kernel for
+// bounds and orders together measured 19 us against 14 us for the scans and
+// this launch: one workgroup's strided reads of the ids cost more than the
+// launches it saves.)
+
+// Both orders from bounds already written (any B): block 0 the forward's,
+// block 1 the dQ kernel's.
+__global__ __launch_bounds__(kScanThreads) void plan_orders(const int32_t* __restrict__ dstart,
+                                                            Geo g, int32_t* __restrict__ fwd_order,
+                                                            int32_t* __restrict__ dq_order) {
+  if (blockIdx.x == 0)
+    tile_order_body<kFwdBN>(dstart, g, fwd_order);
+  else
+    tile_order_body<kDkdvBN>(dstart, g, dq_order);
+}
+
 // The dK/dV schedule and the fp16 scales (block 0), the dQ tile order
 // (block 1, unless dq_order is null) and the row statistics (the other
 // blocks) in one launch: the single-block parts run beside the row
@@ -680,6 +698,12 @@ hipError_t launch_sched_rowstat(int D, const int32_t* kfirst, const int32_t* dst
 hipError_t launch_scale_scan(const u16* dout, long long n_dout, const u16* v, long long n_v,
                              int2* parts, hipStream_t st) {
   scale_scan<<<kScaleParts, kScaleThreads, 0, st>>>(dout, n_dout, v, n_v, parts);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_orders(const int32_t* dstart, const Geo& g, int32_t* fwd_order,
+                              int32_t* dq_order, hipStream_t st) {
+  plan_orders<<<2, kScanThreads, 0, st>>>(dstart, g, fwd_order, dq_order);
   return hipGetLastError();
 }
 

@@ -289,6 +289,54 @@ int docmask_gqa_attn_bwd_bounds(const void* q, const void* k, const void* v,
                                 float* dk, float* dv, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* Batch plan: the bounds of docmask_gqa_doc_bounds together with the
+ * query-tile orders that the forward and the backward's dQ kernel
+ * otherwise build in every call (query tiles of 128 rows by decreasing
+ * number of key tiles they reach, so that the longest tiles start first).
+ * The bounds and orders depend only on the document layout and on (B, S,
+ * Skv, Hq, Hkv, cp_size, cp_rank), not on q, k, v: the same layout serves
+ * every layer of a training step ("Paper notes: The Llama 3 Herd of
+ * Models", "Two architectural choices": the document mask is a property of
+ * the packed sequence), so a caller builds the plan once per batch and
+ * passes it to each layer's *_plan calls.  The bounds scan of
+ * docmask_gqa_doc_bounds, then one launch for both orders.
+ *   docmask_gqa_batch_plan_size: bytes of the plan for any rank of the
+ *     shape (0 for invalid sizes); D only enters the shape checks.
+ *   docmask_gqa_batch_plan: doc_ids or cu_seqlens as for the attention
+ *     calls; plan: device buffer of at least that many bytes, 4-byte aligned,
+ *     owned by the caller and kept while later calls read it; asynchronous
+ *     on `stream`.  Layout (int32): the bounds array [2, B, Skv] as written by
+ *     docmask_gqa_doc_bounds (so the plan also serves as `bounds` of the
+ *     *_bounds calls), the forward order, the dQ order, scratch.
+ *   docmask_gqa_attn_fwd_plan / docmask_gqa_attn_bwd_plan: as the *_bounds
+ *     calls, reading the plan's bounds and order; workspace sizes as for
+ *     docmask_gqa_attn_fwd / docmask_gqa_attn_bwd.  The plan must come from
+ *     docmask_gqa_batch_plan with the same B, S, Skv, Hq, Hkv, cp_size and
+ *     cp_rank (not checked: another plan is undefined behaviour). */
+size_t docmask_gqa_batch_plan_size(int32_t B, int32_t S, int32_t Skv,
+                                   int32_t Hq, int32_t Hkv, int32_t D,
+                                   int32_t cp_size);
+int docmask_gqa_batch_plan(const int32_t* doc_ids, const int32_t* cu_seqlens,
+                           int32_t n_docs, int32_t B, int32_t S, int32_t Skv,
+                           int32_t Hq, int32_t Hkv, int32_t D, int32_t cp_size,
+                           int32_t cp_rank, int32_t* plan, size_t plan_bytes,
+                           void* stream);
+int docmask_gqa_attn_fwd_plan(const void* q, const void* k, const void* v,
+                              const int32_t* plan, int32_t B, int32_t S,
+                              int32_t Skv, int32_t Hq, int32_t Hkv, int32_t D,
+                              int32_t cp_size, int32_t cp_rank,
+                              float softmax_scale, void* out, float* lse,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
+int docmask_gqa_attn_bwd_plan(const void* q, const void* k, const void* v,
+                              const void* out, const void* dout,
+                              const float* lse, const int32_t* plan, int32_t B,
+                              int32_t S, int32_t Skv, int32_t Hq, int32_t Hkv,
+                              int32_t D, int32_t cp_size, int32_t cp_rank,
+                              float softmax_scale, void* dq, float* dk,
+                              float* dv, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Debug check of the document-id precondition.  Copies doc_ids [B, S] to the
  * host, synchronising `stream`.  Returns 0 if every id forms one contiguous
  * run in each batch row, 1 if some id reappears after a different id,

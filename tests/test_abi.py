@@ -257,6 +257,67 @@ def test_bounds_variants_reject():
                                         b.p, b.p, 0, None) == WS
 
 
+# ---------------------------------------------------------------- batch plan API
+
+def test_batch_plan_size():
+    f = M.docmask_gqa_batch_plan_size
+    # the bounds array, two orders of B * nt query tiles (128 rows), and the
+    # bounds scan's aggregates
+    nt = 8192 * 16 // 128
+    assert f(1, 8192, 8192, 16, 1, 128, 1) == (2 * 8192 + 2 * nt + 2 * 8) * 4
+    # rank-independent: Sq = S / cp local tokens, the key prefix given
+    nt = (131072 // 16) * 16 // 128
+    assert f(1, 131072, 65536, 16, 1, 128, 16) == (2 * 65536 + 2 * nt + 2 * 64) * 4
+    # S = 1000, cp = 2: 500 local tokens x 3 heads = 12 tiles per batch row
+    assert f(2, 1000, 700, 6, 2, 64, 2) == (2 * 2 * 700 + 2 * 2 * 12 + 2 * 2 * 1) * 4
+    # the plan's head is a bounds array
+    assert f(1, 8192, 8192, 16, 1, 128, 1) > M.docmask_gqa_doc_bounds_size(1, 8192, 8192)
+    assert f(0, 8, 8, 1, 1, 64, 1) == 0 and f(1, 8, 9, 1, 1, 64, 1) == 0
+    assert f(1, 8192, 8192, 16, 3, 128, 1) == 0 and f(1, 8192, 8192, 16, 1, 96, 1) == 0
+
+
+def _plan_call(**kw):
+    b = _Buf(1 << 16)
+    a = dict(doc=b.p, cu=None, n_docs=0, B=1, S=512, Skv=512, Hq=4, Hkv=1, D=64, cp=1, rank=0,
+             out=b.p, nbytes=1 << 16)
+    a.update({k: (b.p if v == "same" else v) for k, v in kw.items()})
+    return M.lib().docmask_gqa_batch_plan(a["doc"], a["cu"], a["n_docs"], a["B"], a["S"],
+                                          a["Skv"], a["Hq"], a["Hkv"], a["D"], a["cp"],
+                                          a["rank"], a["out"], a["nbytes"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(out=None), INV),
+    (dict(doc=None), INV),                                # neither
+    (dict(cu="same", n_docs=2), INV),                     # both
+    (dict(doc=None, cu="same", n_docs=2, B=2), UNS),      # cu_seqlens with B > 1
+    (dict(Skv=513), INV),
+    (dict(rank=1), INV),                                  # rank out of range
+    (dict(Hkv=3), INV),
+    (dict(nbytes=100), WS),
+])
+def test_batch_plan_rejects(kw, want):
+    assert _plan_call(**kw) == want
+
+
+def test_plan_variants_reject():
+    b = _Buf()
+    L = M.lib()
+    common = (1, 512, 512, 4, 1, 64, 1, 0, 0.125)
+    assert L.docmask_gqa_attn_fwd_plan(b.p, b.p, b.p, None, *common, b.p, b.p, b.p, 1 << 12,
+                                      None) == INV
+    assert L.docmask_gqa_attn_fwd_plan(b.p, b.p, b.p, b.p, *common, b.p, b.p, b.p, 0,
+                                      None) == WS
+    assert L.docmask_gqa_attn_bwd_plan(b.p, b.p, b.p, b.p, b.p, b.p, None, *common, b.p, b.p,
+                                      b.p, b.p, 1 << 12, None) == INV
+    assert L.docmask_gqa_attn_bwd_plan(b.p, b.p, b.p, b.p, b.p, b.p, b.p, *common, b.p, b.p,
+                                      b.p, b.p, 0, None) == WS
+    # empty shapes return before reading any pointer
+    empty = (0, 512, 512, 4, 1, 64, 1, 0, 0.125)
+    assert L.docmask_gqa_attn_fwd_plan(None, None, None, None, *empty, None, None, None, 0,
+                                      None) == 0
+
+
 # ---------------------------------------------------------------- cross-attention forward
 
 def test_cross_workspace_size():

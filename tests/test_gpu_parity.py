@@ -362,3 +362,61 @@ def test_bounds_path_matches_doc_path(name, seed, rank, use_cu):
         torch.cuda.synchronize()
         for x, y in zip(ga, gb):
             assert torch.equal(x, y)
+
+
+PLAN_CASES = [
+    # (id, config, seed, rank, lengths or None, use_cu): document ids and
+    # cu_seqlens, B = 1 and 2, Skv from 512 to 102400 keys, D 64 and 128
+    ("tiny", W.CONFIGS["tiny"], 0, 0, None, False),
+    ("tp405b", W.CONFIGS["tp405b"], 3, 0, None, False),
+    ("short_docs_r0", W.CONFIGS["short_docs"], 1, 0, None, False),
+    ("short_docs_r3", W.CONFIGS["short_docs"], 2, 3, None, False),
+    ("ragged_g3_d64_r1", _cfg("b", 1000, 2, 6, 2, 64), 2, 1, [_rng_lengths(1000, 1, 200, 2)],
+     False),
+    ("tiny_cu", W.CONFIGS["tiny"], 1, 0, None, True),
+    ("batch2_cp3_g16_r2", _cfg("d", 768, 3, 16, 1, 128, B=2), 4, 2,
+     [_rng_lengths(768, 1, 300, 4), _rng_lengths(768, 50, 700, 5)], False),
+    ("long_cp_r7", W.CONFIGS["long_cp"], 0, 7, None, False),
+]
+
+
+@pytest.mark.parametrize("cid,cfg,seed,rank,lengths,use_cu", PLAN_CASES,
+                         ids=[c[0] for c in PLAN_CASES])
+def test_plan_path_matches_doc_path(cid, cfg, seed, rank, lengths, use_cu):
+    """docmask_gqa_batch_plan: its bounds equal the host's document starts /
+    ends (bit-exact), both orders are permutations of the (batch row, query
+    tile) items, and the *_plan calls reproduce the doc_ids calls bit for
+    bit (the order only decides which workgroup computes a tile)."""
+    case = _small_case(cfg, seed, rank, lengths, None) if lengths else W.make_case(cfg, seed, rank)
+    say(f"[plan {cid} seed {seed} rank {rank} cu={use_cu}]")
+    d = dev(case, use_cu=use_cu)
+    B, Sq, Hq, D = case.q.shape
+    S = Sq * case.cfg.cp_size
+    Hkv = case.cfg.Hkv
+    kw = {"cu_seqlens": d["cu_seqlens"]} if use_cu else {"doc_ids": d["doc_ids"]}
+    plan = M.docmask_gqa_batch_plan(**kw, B=B, S=S, Skv=case.Skv, Hq=Hq, Hkv=Hkv, D=D,
+                                    cp_size=case.cfg.cp_size, cp_rank=rank)
+    torch.cuda.synchronize()
+    p = plan.cpu().numpy()
+    got = p[:2 * B * case.Skv].reshape(2, B, case.Skv)
+    for b in range(B):
+        start, end = doc_start_end(case.lengths[b])
+        assert np.array_equal(got[0, b], start[:case.Skv])
+        assert np.array_equal(got[1, b], np.minimum(end[:case.Skv], case.Skv))
+    n_items = B * ((Sq * (Hq // Hkv) + 127) // 128)
+    for k in range(2):
+        o = p[2 * B * case.Skv + k * n_items:2 * B * case.Skv + (k + 1) * n_items]
+        assert np.array_equal(np.sort(o), np.arange(n_items))
+    out_a, lse_a = gpu_fwd(case, d, use_cu=use_cu)
+    out_b, lse_b = M.docmask_gqa_attn_fwd(d["q"], d["k"], d["v"], cp_size=case.cfg.cp_size,
+                                          cp_rank=rank, softmax_scale=case.scale, plan=plan)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
+    if case.cfg.backward or cid.startswith("tiny"):
+        ga = gpu_bwd(case, d, out_a, lse_a, use_cu=use_cu)
+        gb = M.docmask_gqa_attn_bwd(d["q"], d["k"], d["v"], out_a, d["dout"], lse_a,
+                                    cp_size=case.cfg.cp_size, cp_rank=rank,
+                                    softmax_scale=case.scale, plan=plan)
+        torch.cuda.synchronize()
+        for x, y in zip(ga, gb):
+            assert torch.equal(x, y)
