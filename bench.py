@@ -132,16 +132,25 @@ def sample_clocks(delay_s: float = 0.5):
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_hash() -> str:
-    """Hash of the HIP sources: a stored traffic figure is reported only for
-    the exact kernels it was measured on."""
+# The sources each measured kernel is compiled from (its .hip file and the
+# headers it includes), for kernel_source_hash.
+KERNEL_SOURCES = {
+    "bwd_dkdv": ("dkdv.hip", "common.hpp", "dma.hpp", "index.hpp", "kernels.hpp"),
+    "fwd": ("fwd.hip", "common.hpp", "dma.hpp", "index.hpp", "kernels.hpp", "qtile.hpp"),
+    "bwd_dq": ("dqs.hip", "common.hpp", "dma.hpp", "index.hpp", "kernels.hpp", "qtile.hpp",
+               "reduce.hpp"),
+}
+
+
+def kernel_source_hash(kernel: str = "bwd_dkdv") -> str:
+    """Hash of the sources of `kernel`: a stored traffic figure is reported
+    only for the exact kernel it was measured on."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "context_gqa_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -155,7 +164,7 @@ def measured_traffic(kernel: str, workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get("source_hash") != kernel_source_hash(kernel):
         return None
     return rec["bytes_per_launch"]
 
@@ -196,7 +205,7 @@ def traffic_from_pmc(fetch_csv: str, write_csv: str, kernel: str, workload: str,
             "copy_write_kib": w_copy, "fetch_scale": round(f_scale, 4),
             "write_scale": round(w_scale, 4),
             "bytes_per_launch": int(f_k * 1024 * f_scale + w_k * 1024 * w_scale),
-            "source_hash": kernel_source_hash(), "command": command}
+            "source_hash": kernel_source_hash(kernel), "command": command}
 
 
 def cpu_baseline(runs, min_s: float = 10.0, max_s: float = 30.0) -> dict:
@@ -319,8 +328,12 @@ def all_ranks(args) -> int:
     Sq = 2 * c
     f_ws = max(M.docmask_gqa_fwd_workspace_size(B, S, W.kv_prefix_len(S, cfg.cp_size, r), Hq,
                                                  Hkv, D, cfg.cp_size) for r in ranks)
-    b_ws = max(M.docmask_gqa_bwd_workspace_size(B, S, W.kv_prefix_len(S, cfg.cp_size, r), Hq,
-                                                Hkv, D, cfg.cp_size) for r in ranks)
+    stash_kind = "recompute" if args.recompute else args.stash
+    b_size = {"default": M.docmask_gqa_bwd_workspace_size,
+              "full": M.docmask_gqa_bwd_workspace_size_full,
+              "recompute": M.docmask_gqa_bwd_workspace_size_min}[stash_kind]
+    b_ws = max(b_size(B, S, W.kv_prefix_len(S, cfg.cp_size, r), Hq, Hkv, D, cfg.cp_size)
+               for r in ranks)
     wsf = torch.empty(max(1, f_ws), dtype=torch.uint8, device=dev)
     wsb = torch.empty(max(1, b_ws), dtype=torch.uint8, device=dev)
     out = torch.empty(B, Sq, Hq, D, dtype=torch.bfloat16, device=dev)
@@ -333,7 +346,7 @@ def all_ranks(args) -> int:
     stream = torch.cuda.current_stream()
     res = {"study": "per-rank imbalance", "workload": f"{cfg.name}: {cfg.description}",
            "cp_size": cfg.cp_size, "ranks": ranks, "seeds": seeds, "reps": args.steps,
-           "masks": {}}
+           "backward_workspace": stash_kind, "masks": {}}
     for mask in ("document", "causal"):
         per = []
         for seed in seeds:
