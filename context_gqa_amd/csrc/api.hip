@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <unordered_set>
@@ -50,6 +51,27 @@ int check_shape(int B, int S, int Skv, int Hq, int Hkv, int D, int cp, int rank,
   sh->B = B; sh->S = S; sh->Skv = Skv; sh->Hq = Hq; sh->Hkv = Hkv; sh->D = D;
   sh->cp = cp; sh->rank = rank; sh->G = G; sh->c = c; sh->Sq = (int)Sq;
   sh->empty = (B == 0 || S == 0);
+  return DMGQA_OK;
+}
+
+// Debug mode (environment variable DMGQA_DEBUG set to anything but "0",
+// read at every call): each call validates its masking input with the
+// synchronous checkers below before any launch -- a copy to the host and a
+// synchronisation of the stream, so not for graph capture or timed runs --
+// and returns DMGQA_ERR_INVALID_ARG on a violated precondition.
+bool debug_mode() {
+  const char* e = std::getenv("DMGQA_DEBUG");
+  return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
+}
+
+// Checker result (0 valid, 1 violated, negative status) as a call status.
+int debug_status(int r) { return r == 0 ? DMGQA_OK : (r > 0 ? DMGQA_ERR_INVALID_ARG : r); }
+
+int debug_check_docs(const int32_t* doc_ids, const int32_t* cu, int n_docs, int B, int S,
+                     hipStream_t st) {
+  if (!debug_mode()) return DMGQA_OK;
+  if (doc_ids) return debug_status(docmask_gqa_check_docs(doc_ids, B, S, st));
+  if (cu) return debug_status(docmask_gqa_check_cu_seqlens(cu, n_docs, S, st));
   return DMGQA_OK;
 }
 
@@ -283,6 +305,8 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* doc_ids
   if (workspace_bytes < L.total_min) return DMGQA_ERR_WORKSPACE;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  rc = debug_check_docs(doc_ids, cu_seqlens, n_docs, s.B, s.S, st);
+  if (rc != DMGQA_OK) return rc;
   char* ws = static_cast<char*>(workspace);
   const int32_t* dstart;
   const int32_t* dend;
@@ -508,6 +532,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   const StashPlan plan = plan_stash(s, L, workspace_bytes);
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  rc = debug_check_docs(doc_ids, cu_seqlens, n_docs, s.B, s.S, st);
+  if (rc != DMGQA_OK) return rc;
   char* ws = static_cast<char*>(workspace);
   const int32_t* dstart;
   const int32_t* dend;
@@ -611,6 +637,10 @@ int bwd_cross_impl(const void* q, const void* k, const void* v, const void* out,
   const Layout L = layout(s, true);
   if (workspace_bytes < L.total_min) return DMGQA_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (debug_mode()) {
+    const int drc = debug_status(docmask_gqa_check_cross_intervals(lo, hi, B, S, Skv, st));
+    if (drc != DMGQA_OK) return drc;
+  }
   char* ws = static_cast<char*>(workspace);
   // per key: the first query position that reaches it and one past the last
   int32_t* kfirst = reinterpret_cast<int32_t*>(ws + L.dstart);
@@ -712,6 +742,8 @@ int docmask_gqa_doc_bounds(const int32_t* doc_ids, const int32_t* cu_seqlens, in
   if (!bounds || !aligned(bounds, 4)) return DMGQA_ERR_INVALID_ARG;
   if (bounds_bytes < docmask_gqa_doc_bounds_size(B, S, Skv)) return DMGQA_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int drc = debug_check_docs(doc_ids, cu_seqlens, n_docs, B, S, st);
+  if (drc != DMGQA_OK) return drc;
   int32_t* dstart = bounds;
   int32_t* dend = bounds + (size_t)B * Skv;
   return prep_bounds(doc_ids, cu_seqlens, n_docs, B, S, Skv, dstart, dend,
@@ -768,6 +800,8 @@ int docmask_gqa_batch_plan(const int32_t* doc_ids, const int32_t* cu_seqlens, in
   const BatchPlanLayout P = batch_plan_layout(s);
   if (plan_bytes < P.total_ints * sizeof(int32_t)) return DMGQA_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  rc = debug_check_docs(doc_ids, cu_seqlens, n_docs, s.B, s.S, st);
+  if (rc != DMGQA_OK) return rc;
   const Geo g = make_geo(s, 1.f);   // the orders do not depend on the scale
   int32_t* dstart = plan;
   int32_t* dend = plan + (size_t)s.B * s.Skv;
@@ -823,6 +857,10 @@ int docmask_gqa_interval_bounds(const int32_t* lo, int32_t B, int32_t S, int32_t
   if (!bounds || !aligned(bounds, 4)) return DMGQA_ERR_INVALID_ARG;
   if (bounds_bytes < docmask_gqa_doc_bounds_size(B, S, Skv)) return DMGQA_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (debug_mode()) {
+    const int drc = debug_status(docmask_gqa_check_intervals(lo, B, S, st));
+    if (drc != DMGQA_OK) return drc;
+  }
   timing_begin(kKPrep, st);
   const hipError_t e = launch_prep_interval(lo, B, S, Skv, bounds, bounds + (size_t)B * Skv, st);
   timing_end(kKPrep, st);
@@ -851,6 +889,10 @@ int docmask_gqa_attn_fwd_cross(const void* q, const void* k, const void* v, cons
     return DMGQA_ERR_INVALID_ARG;
   if (workspace_bytes < cross_workspace_bytes(s)) return DMGQA_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (debug_mode()) {
+    const int drc = debug_status(docmask_gqa_check_cross_intervals(lo, hi, B, S, Skv, st));
+    if (drc != DMGQA_OK) return drc;
+  }
   const Geo g = make_geo(s, softmax_scale);
   int32_t* order = static_cast<int32_t*>(workspace);
   timing_begin(kKOrder, st);

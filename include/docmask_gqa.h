@@ -337,6 +337,13 @@ int docmask_gqa_attn_bwd_plan(const void* q, const void* k, const void* v,
                               float* dv, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* Debug mode: with the environment variable DMGQA_DEBUG set to a value
+ * other than "0" (read at every call), each call that takes document ids,
+ * cu_seqlens or interval arrays first runs the matching synchronous check
+ * below on them and returns DMGQA_ERR_INVALID_ARG (launching nothing) if the
+ * precondition does not hold.  The checks copy the arrays to the host and
+ * synchronise the stream: for debugging, not for graph capture or timing. */
+
 /* Debug check of the document-id precondition.  Copies doc_ids [B, S] to the
  * host, synchronising `stream`.  Returns 0 if every id forms one contiguous
  * run in each batch row, 1 if some id reappears after a different id,
