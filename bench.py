@@ -136,8 +136,8 @@ TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 # headers it includes), for kernel_source_hash.
 KERNEL_SOURCES = {
     "bwd_dkdv": ("dkdv.hip", "common.hpp", "dma.hpp", "index.hpp", "kernels.hpp"),
-    "fwd": ("fwd.hip", "common.hpp", "dma.hpp", "index.hpp", "kernels.hpp", "qtile.hpp"),
-    "bwd_dq": ("dqs.hip", "common.hpp", "dma.hpp", "index.hpp", "kernels.hpp", "qtile.hpp",
+    "fwd": ("fwd.hip", "common.hpp", "dma.hpp", "index.hpp", "kernels.hpp"),
+    "bwd_dq": ("dqs.hip", "common.hpp", "dma.hpp", "index.hpp", "kernels.hpp",
                "reduce.hpp"),
 }
 

@@ -22,7 +22,6 @@
 //             result does not depend on which workgroup ran which item.
 #include "common.hpp"
 #include "kernels.hpp"
-#include "qtile.hpp"
 #include "reduce.hpp"
 #include "tileload.hpp"
 

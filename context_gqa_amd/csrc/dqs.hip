@@ -11,7 +11,6 @@
 #include "common.hpp"
 #include "dma.hpp"
 #include "kernels.hpp"
-#include "qtile.hpp"
 #include "reduce.hpp"
 
 namespace dmgqa {

@@ -26,7 +26,6 @@
 // the 64 banks, and a DMA instruction moves 64 contiguous bytes of 16 rows.
 #include "common.hpp"
 #include "kernels.hpp"
-#include "qtile.hpp"
 #include "dma.hpp"
 
 namespace dmgqa {

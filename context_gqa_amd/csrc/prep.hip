@@ -10,7 +10,6 @@
 // attention kernels read these arrays instead of comparing document ids.
 #include "common.hpp"
 #include "kernels.hpp"
-#include "qtile.hpp"
 
 namespace dmgqa {
 
