@@ -17,8 +17,16 @@
 // exchange.  P V is computed as O^T = V^T P^T with V read from LDS by
 // transposed reads.
 //
+// The loop is software-pipelined across key tiles: tile j+1's score
+// products are issued while tile j's exponentials run (each vector
+// instruction placed right after an MFMA executes in its shadow, measured on
+// gfx950: up to about one MFMA's 32 cycles of vector work per MFMA is
+// free), and tile j+1's row maximum is taken while tile j's P V products
+// run.  What is left between two tiles is the barrier, the mask of a
+// partial tile and the reference update.
+//
 // K/V tiles (64 keys) stream through 2 LDS stages, filled by global->LDS
-// DMA one tile ahead.  A tile holds 64 rows x D bf16 in groups
+// DMA (K two tiles ahead, V one).  A tile holds 64 rows x D bf16 in groups
 // of 4 sixteen-byte chunks: group c/4 of row r occupies the 64 bytes at
 // (c/4) * 4096 + 64 * r, chunk c in slot (c % 4) ^ ((r / 4) % 4), so the
 // 128-bit reads of K (32 rows of one chunk per 32-lane half) and the
@@ -201,50 +209,76 @@ __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict
     });
   };
 
-  auto step = [&](int it, const char* cK, auto&& mid) __attribute__((always_inline)) {
-    const char* cV = cK + kTile;
-    const int t0 = tile_start(it);
-    // K operands for all k-steps are read up front (2*KK LDS reads in
-    // flight), so LDS latency overlaps the MFMA chain.
+  // ---- software pipeline: tile j's softmax under tile j+1's score products
+  //
+  // Iteration j holds S_j = K_j Q^T (computed in iteration j-1) and:
+  //   1. masks S_j (partial tiles), takes the row maximum, moves the
+  //      reference m (and rescales O and l) when needed;
+  //   2. issues the 16 products S_{j+1} = K_{j+1} Q^T, each followed by a
+  //      share of the exponentials of S_j, so the vector work runs while the
+  //      matrix pipe is busy with the next tile (within one wave the vector
+  //      instructions after an MFMA execute in its shadow);
+  //   3. issues the 16 products O += P_j V_j, each followed by the packing
+  //      and row sums that remain.
+  // Stage s holds K and V tiles of 64 keys.  K_j and V_j live in stage j%2;
+  // at the top of iteration j (after the barrier: every wave has finished
+  // iteration j-1, so S_j's K reads and P_{j-1} V_{j-1}'s V reads are done)
+  // the DMA loads K_{j+2} into stage j%2 and V_{j+1} into stage (j+1)%2.
+  auto k_op = [&](const char* cK, int kk, int half) __attribute__((always_inline)) {
+    return ld_lds_b128(cK + (kk >> 1) * kGroupBytes + 32 * 64 * half + off_b[kk & 1]);
+  };
+  // S = K Q^T of one tile with nothing interleaved (the first tile)
+  auto s_plain = [&](const char* cK, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
     bf16x8 kf0[KK], kf1[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      kf0[kk] = ld_lds_b128(cK + (kk >> 1) * kGroupBytes + off_b[kk & 1]);
-      kf1[kk] = ld_lds_b128(cK + (kk >> 1) * kGroupBytes + 32 * 64 + off_b[kk & 1]);
+      kf0[kk] = k_op(cK, kk, 0);
+      kf1[kk] = k_op(cK, kk, 1);
     }
-    f32x16 s0 = zero16(), s1 = zero16();
+    s0 = zero16();
+    s1 = zero16();
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       s0 = mfma32(kf0[kk], qop[kk], s0);
       s1 = mfma32(kf1[kk], qop[kk], s1);
     }
-    sched_reads_ahead<2 * KK, KK, 2>();
-    // the next tile's V DMA, while the score products run
-    mid();
-    const bool full = qtile_full(kr, t0, BN);
-    if (!full) {
-      // allowed keys lo..last relative to this lane's first key t0 + 4h;
-      // register r holds key offset 8*(r/4) + r%4 (+32 for s1)
-      // key offset c is allowed iff lo_rel <= c <= hi_rel, one unsigned
-      // compare (hi_rel >= lo_rel: a row always reaches at least one key)
-      const int lo_rel = lo - (t0 + 4 * h);
-      const unsigned span = (unsigned)(last - lo);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c = 8 * (r >> 2) + (r & 3);
-        if ((unsigned)(c - lo_rel) > span) s0[r] = -INFINITY;
-        if ((unsigned)(c + 32 - lo_rel) > span) s1[r] = -INFINITY;
-      }
-    }
-    // row maximum: two independent max3 chains, then the other half-wave
+  };
+  // Step 1 for tile j (first key t0): mask, maximum, reference.  Returns the
+  // exponent offset m * scale * log2(e) (0 while m is -inf).
+  // The row maximum of an unmasked tile (both lanes of a row combined).
+  auto row_max = [&](const f32x16& s0, const f32x16& s1) __attribute__((always_inline)) {
     float ma = max3f(s0[0], s0[1], s0[2]), mb = max3f(s1[0], s1[1], s1[2]);
 #pragma unroll
     for (int r = 3; r < 15; r += 2) {
       ma = max3f(ma, s0[r], s0[r + 1]);
       mb = max3f(mb, s1[r], s1[r + 1]);
     }
-    float mx = max3f(ma, mb, fmaxf(s0[15], s1[15]));
-    mx = fmaxf(mx, other_half(mx));
+    const float mx = max3f(ma, mb, fmaxf(s0[15], s1[15]));
+    return fmaxf(mx, other_half(mx));
+  };
+  // mx_pre: the row maximum of S_j taken during the previous iteration's
+  // P V products (have_pre), valid when the tile needs no mask.
+  auto prepare = [&](int t0, f32x16& s0, f32x16& s1, float mx_pre, bool have_pre)
+                     __attribute__((always_inline)) {
+    const bool full = qtile_full(kr, t0, BN);
+    float mx = mx_pre;
+    if (!full || !have_pre) {
+      if (!full) {
+        // allowed keys lo..last relative to this lane's first key t0 + 4h;
+        // register r holds key offset 8*(r/4) + r%4 (+32 for s1); key
+        // offset c is allowed iff lo_rel <= c <= hi_rel, one unsigned
+        // compare (a row always reaches at least one key, so hi_rel >= lo_rel)
+        const int lo_rel = lo - (t0 + 4 * h);
+        const unsigned span = (unsigned)(last - lo);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 8 * (r >> 2) + (r & 3);
+          if ((unsigned)(c - lo_rel) > span) s0[r] = -INFINITY;
+          if ((unsigned)(c + 32 - lo_rel) > span) s1[r] = -INFINITY;
+        }
+      }
+      mx = row_max(s0, s1);
+    }
     const bool need = mx != -INFINITY && (m == -INFINITY || (mx - m) * g.scale_log2 > kRescaleLog2);
     if (__any(need)) {
       const float mnew = need ? mx : m;
@@ -256,51 +290,163 @@ __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       m = mnew;
     }
-    const float msc = m == -INFINITY ? 0.f : m * g.scale_log2;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], g.scale_log2, -msc));
-      s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], g.scale_log2, -msc));
-    }
-    // the row sum is taken over the bf16 P that multiplies V
-    float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < BN / 16; ++ks) {
-      const bf16x8 pop = pack_bf16(ks < 2 ? s0 : s1, ks & 1);
-      float& rs = (ks & 1) ? rs1 : rs0;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) rs = sum2_bf16(bf16x2{pop[e], pop[e + 1]}, rs);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] = mfma32(tr_group(cV, off_t, ks, db), pop, o[db]);
-    }
-    l += rs0 + rs1;
+    return m == -INFINITY ? 0.f : m * g.scale_log2;
   };
+  // Steps 2 and 3 as NS + NP slots, each one MFMA and its share of the
+  // vector work, fenced so the compiler keeps the order: slots 0 .. NS-1
+  // the products of S_{j+1} (NEXT) and the exponentials of S_j, VPS values
+  // per slot (value v is s0[v] for v < 16, else s1[v-16]); P_j in bf16 as
+  // four k-step operands, each packed one slot after its last exponential,
+  // its row sum one slot later; slots NS .. NS+NP-1 the products P_j V_j.
+  // Operands are read two slots ahead of their MFMA.
+  constexpr int NS = 2 * KK, NP = (BN / 16) * DB, VPS = 32 / NS;
+  constexpr int kPackSlot[4] = {(7) / VPS + 1, (15) / VPS + 1, (23) / VPS + 1, (31) / VPS + 1};
+  // With NEXT the slots also issue the DMA of V_{j+1} (into stage sn) and
+  // K_{j+2} (into stage sj; past the last tile it re-loads the last one,
+  // into a stage no later iteration reads), one instruction every other
+  // slot: issued in one burst after the barrier, the eight waves of a CU
+  // stalled on the vector memory queue.
+  constexpr int NDMA = D / 32;   // DMA instructions per tile and wave
+  // first slot of the next tile's row maximum (two slots after its last
+  // score product; nine steps, kMaxPer per slot)
+  constexpr int kMaxSlot = NS + 2;
+  constexpr int kMaxPer = (9 + (NS + NP - kMaxSlot) - 1) / (NS + NP - kMaxSlot);
+  // slots of the first V and K DMA instructions (then every other slot)
+  constexpr int kDmaV = 1, kDmaK = 1 + 2 * NDMA;
+  static_assert(kDmaV + 2 * NDMA <= NS + NP && kDmaK + 2 * NDMA <= NS + NP, "DMA slots");
+  auto pipelined = [&](auto next_c, const char* cKn, const char* cV, float msc, f32x16& s0,
+                       f32x16& s1, f32x16& n0, f32x16& n1, unsigned offV, unsigned offK,
+                       const char* sj, const char* sn, float& mx_next)
+                       __attribute__((always_inline)) {
+    constexpr bool NEXT = decltype(next_c)::value;
+    bf16x8 kb[3], vb[3], pop[4];
+    float rs0 = 0.f, rs1 = 0.f;
+    float ma = 0.f, mb = 0.f;
+    auto read_for = [&](auto slot_c) __attribute__((always_inline)) {
+      constexpr int S = decltype(slot_c)::value;
+      if constexpr (S < NS) {
+        if constexpr (NEXT) kb[S % 3] = k_op(cKn, S >> 1, S & 1);
+      } else if constexpr (S < NS + NP) {
+        constexpr int P = S - NS;
+        vb[P % 3] = tr_group(cV, off_t, P / DB, P % DB);
+      }
+    };
+    if constexpr (NEXT) {
+      n0 = zero16();
+      n1 = zero16();
+    }
+    read_for(std::integral_constant<int, 0>{});
+    read_for(std::integral_constant<int, 1>{});
+    static_for<NS + NP>([&](auto slot_c) __attribute__((always_inline)) {
+      constexpr int S = decltype(slot_c)::value;
+      read_for(std::integral_constant<int, S + 2>{});
+      if constexpr (S < NS) {
+        if constexpr (NEXT) {
+          if constexpr ((S & 1) == 0)
+            n0 = mfma32(kb[S % 3], qop[S >> 1], n0);
+          else
+            n1 = mfma32(kb[S % 3], qop[S >> 1], n1);
+        }
+        static_for<VPS>([&](auto e_c) __attribute__((always_inline)) {
+          constexpr int V = VPS * S + decltype(e_c)::value;
+          if constexpr (V < 16)
+            s0[V] = __builtin_amdgcn_exp2f(fmaf(s0[V], g.scale_log2, -msc));
+          else
+            s1[V - 16] = __builtin_amdgcn_exp2f(fmaf(s1[V - 16], g.scale_log2, -msc));
+        });
+      } else {
+        constexpr int P = S - NS;
+        o[P % DB] = mfma32(vb[P % 3], pop[P / DB], o[P % DB]);
+      }
+      if constexpr (NEXT && S >= kDmaV && S < kDmaV + 2 * NDMA && (S - kDmaV) % 2 == 0) {
+        constexpr int C = (S - kDmaV) / 2;
+        dma_lds16<64 * C>(vbase, offV,
+                          stg_lds + (unsigned)(sn - stg) + kTile + 64 * 16 * wave + C * kGroupBytes);
+      }
+      if constexpr (NEXT && S >= kDmaK && S < kDmaK + 2 * NDMA && (S - kDmaK) % 2 == 0) {
+        constexpr int C = (S - kDmaK) / 2;
+        dma_lds16<64 * C>(kbase, offK,
+                          stg_lds + (unsigned)(sj - stg) + 64 * 16 * wave + C * kGroupBytes);
+      }
+      static_for<4>([&](auto q_c) __attribute__((always_inline)) {
+        constexpr int Q = decltype(q_c)::value;
+        if constexpr (S == kPackSlot[Q]) pop[Q] = pack_bf16(Q < 2 ? s0 : s1, Q & 1);
+        if constexpr (S == kPackSlot[Q] + 1) {
+          float& rs = (Q & 1) ? rs1 : rs0;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) rs = sum2_bf16(bf16x2{pop[Q][e], pop[Q][e + 1]}, rs);
+        }
+      });
+      if constexpr (S == kPackSlot[3] + 2) l += rs0 + rs1;
+      // NEXT: the row maximum of S_{j+1} (complete after the score
+      // products), one step per slot from slot kMaxSlot on
+      if constexpr (NEXT && S >= kMaxSlot) {
+        static_for<kMaxPer>([&](auto t_c) __attribute__((always_inline)) {
+          constexpr int T = (S - kMaxSlot) * kMaxPer + decltype(t_c)::value;
+          if constexpr (T == 0) {
+            ma = max3f(n0[0], n0[1], n0[2]);
+            mb = max3f(n1[0], n1[1], n1[2]);
+          } else if constexpr (T < 7) {
+            ma = max3f(ma, n0[2 * T + 1], n0[2 * T + 2]);
+            mb = max3f(mb, n1[2 * T + 1], n1[2 * T + 2]);
+          } else if constexpr (T == 7) {
+            ma = max3f(ma, mb, fmaxf(n0[15], n1[15]));
+          } else if constexpr (T == 8) {
+            mx_next = fmaxf(ma, other_half(ma));
+          }
+        });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  static_assert(kPackSlot[3] + 2 < NS + NP, "row sums inside the slots");
+  static_assert(kMaxPer * (NS + NP - kMaxSlot) >= 9, "row maximum inside the slots");
+  static_assert(kPackSlot[0] <= NS && kPackSlot[3] <= NS + (3 * NP) / 4, "operands packed in time");
 
-  // Two stages: before tile it, wait for its DMA, barrier (every wave's
-  // DMA of tile it is in, and every wave has finished tile it-1, whose
-  // stage is refilled next), start tile it+1's K DMA, compute (tile it+1's
-  // V DMA is issued once the score products are under way).
   if (ntiles > 0) {
-    char* sA = stg;
-    char* sB = stg + kStage;
+    // prologue: K_0, V_0 into stage 0 and K_1 into stage 1; S_0
     {
       const unsigned off0 = dma_off(0);
-      issue_k(off0, sA);
-      issue_v(off0, sA);
+      issue_k(off0, stg);
+      issue_v(off0, stg);
+      if (ntiles > 1) issue_k(dma_off(1), stg + kStage);
     }
-    for (int it = 0; it < ntiles; ++it) {
+    f32x16 sa0, sa1, sb0, sb1;
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    s_plain(stg, sa0, sa1);
+    // iteration j: S_j in (c0, c1), S_{j+1} into (n0, n1) unless j is the
+    // last tile (NEXT false; the last tile is peeled off the loop so that
+    // the two forms never share a branch, out of which the compiler would
+    // hoist their common exponentials)
+    float mx_pre = 0.f;
+    auto iteration = [&](auto next_c, int j, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1)
+                         __attribute__((always_inline)) {
       wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      const bool more = it + 1 < ntiles;
-      const unsigned offn = dma_off(it + 1);
-      if (more) issue_k(offn, sB);
-      step(it, sA, [&]() __attribute__((always_inline)) {
-        if (more) issue_v(offn, sB);
-      });
-      char* t = sA;
-      sA = sB;
-      sB = t;
+      char* sj = stg + (j & 1) * kStage;
+      char* sn = stg + ((j + 1) & 1) * kStage;
+      unsigned offV = 0, offK = 0;
+      if constexpr (decltype(next_c)::value) {
+        offV = dma_off(j + 1);
+        offK = dma_off(j + 2);
+      }
+      const float msc = prepare(tile_start(j), c0, c1, mx_pre, j > 0);
+      pipelined(next_c, sn, sj + kTile, msc, c0, c1, n0, n1, offV, offK, sj, sn, mx_pre);
+    };
+    int j = 0;
+    for (; j + 2 < ntiles; j += 2) {
+      iteration(std::true_type{}, j, sa0, sa1, sb0, sb1);
+      iteration(std::true_type{}, j + 1, sb0, sb1, sa0, sa1);
+    }
+    // one or two tiles left, S_j in sa
+    if (j + 1 < ntiles) {
+      iteration(std::true_type{}, j, sa0, sa1, sb0, sb1);
+      iteration(std::false_type{}, j + 1, sb0, sb1, sa0, sa1);
+    } else {
+      iteration(std::false_type{}, j, sa0, sa1, sb0, sb1);
     }
   }
 
