@@ -22,6 +22,12 @@
 //       and dS' = P * dP' take one multiply each)
 //   P (fp16), dS' (bf16)           (VALU)
 //   dV' += P^T dO', dK += dS'^T Q  (MFMA, transposed LDS reads)
+// Each LDS operand read is issued a fixed number of products ahead of the
+// MFMA that consumes it, through a small ring of registers, in program order
+// (scheduling fences: left to itself the compiler placed each read just
+// before its product, and every MFMA waited out the LDS latency); dS' is
+// formed under the dV products, and the previous sub-block's stash read and
+// store bracket the score products.
 //
 // Lane layout (lane l = 16*g4 + j): the S / dP tiles are C[row][key] with
 // key = j; lane group g4 holds the rows 16t + 4*g4 + r (t = 0, 1, r = 0..3).
@@ -352,13 +358,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     // Done one sub-block later (and once after the last), between the next
     // sub-block's score products and its own (1), so the scratch is read
     // before it is written again.
-    auto stash_store = [&](int R) __attribute__((always_inline)) {
+    // (the read and the store are split so that the score products of the
+    // next sub-block run between them)
+    auto stash_read = [&]() __attribute__((always_inline)) {
       const u16* T = s_tr + wave * kWaveKeys * kTrLd;
-      const int i = lane & 31, h = lane >> 5;
-      const int grow = tr_x * g.G + R + i;
-      const unsigned off = R + i < r_end ? (unsigned)(((grow >> 5) - tr_z) * kStashBlockBytes +
-                                                      wave * 1024 + (32 * h + (grow & 31)) * 16)
-                                         : 0x80000000u;
       // transposed read (as a padded-tile operand read, with the pieces
       // permuted): 16-lane group grp reads keys 4(grp/2) + s/4 (+8),
       // rows 16(grp%2) + 4(s%4) .. +3
@@ -368,7 +371,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       const i16x4 lo = ds_read_tr(T + k0 * kTrLd + 4 * (pc ^ tr_swz(k0)));
       const i16x4 hi = ds_read_tr(T + k1 * kTrLd + 4 * (pc ^ tr_swz(k1)));
       const bf16x4 la = __builtin_bit_cast(bf16x4, lo), ha = __builtin_bit_cast(bf16x4, hi);
-      const bf16x8 op = {la[0], la[1], la[2], la[3], ha[0], ha[1], ha[2], ha[3]};
+      return bf16x8{la[0], la[1], la[2], la[3], ha[0], ha[1], ha[2], ha[3]};
+    };
+    // store of the sub-block from virtual row R (none when `valid` is
+    // false: the offset then lies past the buffer, which drops the store)
+    auto stash_write = [&](const bf16x8& op, int R, bool valid) __attribute__((always_inline)) {
+      const int i = lane & 31, h = lane >> 5;
+      const int grow = tr_x * g.G + R + i;
+      const unsigned off = valid && R + i < r_end
+                               ? (unsigned)(((grow >> 5) - tr_z) * kStashBlockBytes + wave * 1024 +
+                                            (32 * h + (grow & 31)) * 16)
+                               : 0x80000000u;
       // non-temporal: the stash is read once, by the dQ kernel, long after
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, op), srs, off, 0,
                                              kCachePolicyNT);
@@ -383,28 +396,55 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
         sc[t] = ld_lds_f32x4(st + Lds::kL + 4 * (q0 + 16 * t + 4 * g4));
         pc[t] = ld_lds_f32x4(st + Lds::kN + 4 * (q0 + 16 * t + 4 * g4));
       }
-      bf16x8 qa[2][KS], oa[2][KS];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          qa[t][ks] = ld_lds_b128(st + ks * kGroupBytes + 64 * (q0 + 16 * t) + off_b);
-          oa[t][ks] = ld_lds_b128(st + Lds::kTile + ks * kGroupBytes + 64 * (q0 + 16 * t) + off_b);
-        }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) sc[t] = mfma16(qa[t][ks], kop[ks], sc[t]);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) pc[t] = mfma16h(oa[t][ks], vop[ks], pc[t]);
+      // product p: S (p < 2KS: rows 16t, t = p%2, k-step p/2) then dP; its
+      // operand read kAhead products before it, through a ring of
+      // registers, in program order (fenced)
+      constexpr int NPR = 4 * KS, kAhead = 4;
+      auto read_op = [&](auto p_c) __attribute__((always_inline)) {
+        constexpr int P = decltype(p_c)::value;
+        constexpr int T = P & 1, KSI = (P % (2 * KS)) >> 1;
+        constexpr int base = P < 2 * KS ? 0 : Lds::kTile;
+        return ld_lds_b128(st + base + KSI * kGroupBytes + 64 * (q0 + 16 * T) + off_b);
+      };
+      bf16x8 ring[kAhead + 1];
+      static_for<kAhead>([&](auto p_c) __attribute__((always_inline)) {
+        ring[decltype(p_c)::value] = read_op(p_c);
+      });
+      static_for<NPR>([&](auto p_c) __attribute__((always_inline)) {
+        constexpr int P = decltype(p_c)::value;
+        if constexpr (P + kAhead < NPR)
+          ring[(P + kAhead) % (kAhead + 1)] = read_op(std::integral_constant<int, P + kAhead>{});
+        constexpr int T = P & 1, KSI = (P % (2 * KS)) >> 1;
+        if constexpr (P < 2 * KS)
+          sc[T] = mfma16(ring[P % (kAhead + 1)], kop[KSI], sc[T]);
+        else
+          pc[T] = mfma16h(ring[P % (kAhead + 1)], vop[KSI], pc[T]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     };
 
     // The rest of a sub-block (virtual rows from R, rows q0.. of stage st)
     // from its S and dP: P, dV += P^T dO, dS, dK += dS^T Q.
     auto rest = [&](auto masked, const char* st, int q0, int R, const f32x4 (&sc)[2],
                     const f32x4 (&pc)[2]) __attribute__((always_inline)) {
+      const char* tQ = st + 64 * q0;
+      const char* tO = st + Lds::kTile + 64 * q0;
+      // product r: dV' += P^T dO' (r < ND, d tile r) then dK += dS'^T Q
+      // (d tile r - ND); its transposed operand read kAheadT products
+      // before it through a ring, in program order (fenced); the first
+      // reads are issued before P is formed, and dS' is formed under the dV
+      // products
+      constexpr int kAheadT = 3;
+      auto read_t = [&](auto r_c) __attribute__((always_inline)) {
+        constexpr int R_ = decltype(r_c)::value;
+        constexpr int nd = R_ % ND;
+        const char* tile = R_ < ND ? tO : tQ;
+        return tr_pair(tile + (nd >> 1) * kGroupBytes + off_t[nd & 1]);
+      };
+      bf16x8 rg[kAheadT + 1];
+      static_for<kAheadT>([&](auto r_c) __attribute__((always_inline)) {
+        rg[decltype(r_c)::value] = read_t(r_c);
+      });
       // p[4t + r]: row 16t + 4*g4 + r of the sub-block, key j
       float p[8];
 #pragma unroll
@@ -427,22 +467,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
         pw[e] = __builtin_bit_cast(unsigned, hp);
       }
       const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
-      const char* tQ = st + 64 * q0;
-      const char* tO = st + Lds::kTile + 64 * q0;
-      bf16x8 dot[ND];
-#pragma unroll
-      for (int nd = 0; nd < ND; ++nd) dot[nd] = tr_pair(tO + (nd >> 1) * kGroupBytes + off_t[nd & 1]);
-#pragma unroll
-      for (int nd = 0; nd < ND; ++nd) dva[nd] = mfma16h(pop, dot[nd], dva[nd]);
       bf16x8 dsop;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dsop[e] = (__bf16)(p[e] * pc[e >> 2][e & 3]);
-      if constexpr (STASH) stash_put(dsop);
-      bf16x8 qt[ND];
-#pragma unroll
-      for (int nd = 0; nd < ND; ++nd) qt[nd] = tr_pair(tQ + (nd >> 1) * kGroupBytes + off_t[nd & 1]);
-#pragma unroll
-      for (int nd = 0; nd < ND; ++nd) dka[nd] = mfma16(dsop, qt[nd], dka[nd]);
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<2 * ND>([&](auto r_c) __attribute__((always_inline)) {
+        constexpr int R_ = decltype(r_c)::value;
+        if constexpr (R_ + kAheadT < 2 * ND)
+          rg[(R_ + kAheadT) % (kAheadT + 1)] = read_t(std::integral_constant<int, R_ + kAheadT>{});
+        if constexpr (R_ < ND) {
+          dva[R_] = mfma16h(pop, rg[R_ % (kAheadT + 1)], dva[R_]);
+          // dS' = P * dP' (bf16), two values per dV product (ND >= 4)
+          if constexpr (R_ < 4) {
+            dsop[2 * R_] = (__bf16)(p[2 * R_] * pc[(2 * R_) >> 2][(2 * R_) & 3]);
+            dsop[2 * R_ + 1] = (__bf16)(p[2 * R_ + 1] * pc[(2 * R_ + 1) >> 2][(2 * R_ + 1) & 3]);
+          }
+        } else {
+          dka[R_ - ND] = mfma16(dsop, rg[R_ % (kAheadT + 1)], dka[R_ - ND]);
+        }
+        // dS' (complete after slot 3) to the transpose scratch
+        if constexpr (STASH && R_ == 4) stash_put(dsop);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     };
 
     // Sub-block j lives in stage (j/2) % 4 at row 32*(j%2).  Block n+2's
@@ -475,16 +519,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
         constexpr int h2 = decltype(second)::value ? 1 : 0;
         const int R = r_begin + 64 * jb + 32 * h2;
         f32x4 sc[2], pc[2];
+        // the previous sub-block's dS (if any) from the transpose scratch,
+        // stored once the score products are issued
+        bf16x8 prev;
+        if constexpr (STASH) prev = stash_read();
         sdp(st, 32 * h2, sc, pc);
         // DMA instructions of a later block, while the products run
         if constexpr (h2 == 0)
           issue_q(nx);
         else
           issue_o(nx);
-        // the previous sub-block's dS to the stash, now that its transposed
-        // read has the score products to hide behind
-        if constexpr (STASH)
-          if (R > r_begin) stash_store(R - 32);
+        if constexpr (STASH) stash_write(prev, R - 32, R > r_begin);
         if (w_lo <= R && R + 32 <= w_hi)
           rest(std::false_type{}, st, 32 * h2, R, sc, pc);
         else
@@ -494,7 +539,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       if (2 * jb + 1 < nsb) sub_block(std::true_type{});
     }
     if constexpr (STASH)
-      if (nsb > 0) stash_store(r_begin + 32 * (nsb - 1));
+      if (nsb > 0) stash_write(stash_read(), r_begin + 32 * (nsb - 1), true);
 
     // No DMA (including the re-loads past the item's end) may still be
     // writing LDS once the item is done.
