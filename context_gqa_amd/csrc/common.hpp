@@ -110,27 +110,6 @@ __device__ __forceinline__ bf16x8 tr_operand(const u16* base, int row0, int ks, 
   return r;
 }
 
-// Same operand from a padded row-major LDS tile with row stride LD elements
-// (no swizzle), so every read of a k-step is a constant offset from one
-// per-lane address.
-template <int LD>
-__device__ __forceinline__ bf16x8 tr_operand_pad(const u16* base, int row0, int ks, int n0,
-                                                 int lane) {
-  const int s = lane & 15;
-  const int grp = lane >> 4;
-  const int h = grp >> 1;
-  const u16* p = base + (row0 + 4 * h + (s >> 2)) * LD + 16 * (grp & 1) + 4 * (s & 3) +
-                 16 * ks * LD + n0;
-  i16x4 lo = ds_read_tr(p);
-  i16x4 hi = ds_read_tr(p + 8 * LD);
-  bf16x8 r;
-  bf16x4 a = __builtin_bit_cast(bf16x4, lo);
-  bf16x4 b = __builtin_bit_cast(bf16x4, hi);
-  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
-  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
-  return r;
-}
-
 // Registers 8*(ks%2) .. 8*(ks%2)+7 of an S^T-shaped accumulator as a bf16
 // MFMA operand (round to nearest even).
 __device__ __forceinline__ bf16x8 pack_bf16(const f32x16& acc, int half) {
@@ -157,21 +136,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float sum2_bf16(bf16x2 x, float acc) {
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
   return __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
-}
-
-// Scheduling hint for a run of N MFMAs that each consume one LDS read:
-// issue AHEAD reads first, then groups of STEP MFMAs each followed by STEP
-// more reads, then the remaining MFMAs.  Keeps LDS latency off the MFMA
-// issue path without holding every operand in registers at once.
-template <int N, int AHEAD, int STEP>
-__device__ __forceinline__ void sched_reads_ahead() {
-  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);   // DS read
-#pragma unroll
-  for (int j = 0; j < (N - AHEAD) / STEP; ++j) {
-    __builtin_amdgcn_sched_group_barrier(0x008, STEP, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, STEP, 0);  // DS read
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
 }
 
 // x / G and x % G (x >= 0); shifts when G is a power of two.
