@@ -142,15 +142,50 @@ KERNEL_SOURCES = {
 }
 
 
+def code_only(text: str) -> str:
+    """C++ source without its comments, whitespace runs outside string and
+    character literals collapsed to one space (literals kept as written)."""
+    out, i, n = [], 0, len(text)
+
+    def space():
+        if out and out[-1] != " ":
+            out.append(" ")
+
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+            space()
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            space()
+        elif c.isspace():
+            space()
+            i += 1
+        else:
+            out.append(c)
+            i += 1
+    return "".join(out).strip()
+
+
 def kernel_source_hash(kernel: str = "bwd_dkdv") -> str:
-    """Hash of the sources of `kernel`: a stored traffic figure is reported
-    only for the exact kernel it was measured on."""
+    """Hash of the code of `kernel`'s sources (comments and layout left
+    out): a stored traffic figure is reported only for the kernel it was
+    measured on."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "context_gqa_amd", "csrc")
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -355,11 +355,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     };
     // (2) transposed read: lane (h, i) gets row i, keys 8(e/4) + 4h + e%4
     // of the wave's 16, stored as chunk (w, lane) of the row's stash block.
-    // Done one sub-block later (and once after the last), between the next
-    // sub-block's score products and its own (1), so the scratch is read
-    // before it is written again.
-    // (the read and the store are split so that the score products of the
-    // next sub-block run between them)
+    // Read at the start of the next sub-block (and once after the last),
+    // before that sub-block's (1) rewrites the scratch, and stored once its
+    // score products are issued, so they run between the read and the store.
     auto stash_read = [&]() __attribute__((always_inline)) {
       const u16* T = s_tr + wave * kWaveKeys * kTrLd;
       // transposed read (as a padded-tile operand read, with the pieces

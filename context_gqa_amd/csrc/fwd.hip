@@ -218,12 +218,13 @@ __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict
   //      share of the exponentials of S_j, so the vector work runs while the
   //      matrix pipe is busy with the next tile (within one wave the vector
   //      instructions after an MFMA execute in its shadow);
-  //   3. issues the 16 products O += P_j V_j, each followed by the packing
-  //      and row sums that remain.
-  // Stage s holds K and V tiles of 64 keys.  K_j and V_j live in stage j%2;
-  // at the top of iteration j (after the barrier: every wave has finished
-  // iteration j-1, so S_j's K reads and P_{j-1} V_{j-1}'s V reads are done)
-  // the DMA loads K_{j+2} into stage j%2 and V_{j+1} into stage (j+1)%2.
+  //   3. issues the 16 products O += P_j V_j, with the packing and row sums
+  //      that remain and the row maximum of S_{j+1} in their shadow.
+  // Stage s holds K and V tiles of 64 keys.  K_j and V_j live in stage j%2.
+  // Iteration j starts with a barrier (every wave has finished iteration
+  // j-1, so S_j's K reads and P_{j-1} V_{j-1}'s V reads are done); after it
+  // the DMA loads K_{j+2} into stage j%2 and V_{j+1} into stage (j+1)%2,
+  // which the barrier of iteration j+1 waits for.
   auto k_op = [&](const char* cK, int kk, int half) __attribute__((always_inline)) {
     return ld_lds_b128(cK + (kk >> 1) * kGroupBytes + 32 * 64 * half + off_b[kk & 1]);
   };
@@ -243,8 +244,6 @@ __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict
       s1 = mfma32(kf1[kk], qop[kk], s1);
     }
   };
-  // Step 1 for tile j (first key t0): mask, maximum, reference.  Returns the
-  // exponent offset m * scale * log2(e) (0 while m is -inf).
   // The row maximum of an unmasked tile (both lanes of a row combined).
   auto row_max = [&](const f32x16& s0, const f32x16& s1) __attribute__((always_inline)) {
     float ma = max3f(s0[0], s0[1], s0[2]), mb = max3f(s1[0], s1[1], s1[2]);
@@ -256,8 +255,10 @@ __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict
     const float mx = max3f(ma, mb, fmaxf(s0[15], s1[15]));
     return fmaxf(mx, other_half(mx));
   };
-  // mx_pre: the row maximum of S_j taken during the previous iteration's
-  // P V products (have_pre), valid when the tile needs no mask.
+  // Step 1 for tile j (first key t0): mask, maximum, reference.  Returns the
+  // exponent offset m * scale * log2(e) (0 while m is -inf).  mx_pre: the
+  // row maximum of S_j taken during the previous iteration's P V products
+  // (have_pre), valid when the tile needs no mask.
   auto prepare = [&](int t0, f32x16& s0, f32x16& s1, float mx_pre, bool have_pre)
                      __attribute__((always_inline)) {
     const bool full = qtile_full(kr, t0, BN);
@@ -401,7 +402,10 @@ __global__ __launch_bounds__(kRows * 2, 2) void fwd_kernel(const u16* __restrict
   };
   static_assert(kPackSlot[3] + 2 < NS + NP, "row sums inside the slots");
   static_assert(kMaxPer * (NS + NP - kMaxSlot) >= 9, "row maximum inside the slots");
-  static_assert(kPackSlot[0] <= NS && kPackSlot[3] <= NS + (3 * NP) / 4, "operands packed in time");
+  // operand Q of P_j is first used by P V product Q * DB (slot NS + Q * DB)
+  static_assert(kPackSlot[0] <= NS && kPackSlot[1] <= NS + DB && kPackSlot[2] <= NS + 2 * DB &&
+                    kPackSlot[3] <= NS + 3 * DB,
+                "each P operand packed before its first P V product");
 
   if (ntiles > 0) {
     // prologue: K_0, V_0 into stage 0 and K_1 into stage 1; S_0

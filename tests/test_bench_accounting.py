@@ -62,3 +62,14 @@ def test_score_matrix_bytes_example():
 
 def test_multi_gpu_request_exits():
     assert bench.main(["--gpus", "2"]) == 2
+
+
+def test_kernel_hash_follows_code_not_comments():
+    """The traffic record's source hash ignores comments and layout, keeps
+    string literals (inline assembly) and changes with any code token."""
+    c = bench.code_only
+    assert c('a /* x */ b // y\n"// s" \'/\' c\n  d') == 'a b "// s" \'/\' c d'
+    assert c("x = 1;  // one\n") == c("x   =   1;\n/* no code */")
+    assert c("x = 1;") != c("x = 2;")
+    assert c('asm("v_mov_b32 %0, %1")') != c('asm("v_mov_b32  %0, %1")')
+    assert len(bench.kernel_source_hash("bwd_dkdv")) == 16
