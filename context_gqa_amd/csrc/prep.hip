@@ -595,10 +595,12 @@ __global__ __launch_bounds__(kScanThreads) void tile_order_fwd_iv(
 
 // Plan of one batch layout: the bounds (the scans above) and both query-tile
 // orders (forward, BN = kFwdBN; dQ, BN = kDkdvBN) that the attention calls
-// read instead of computing them per call.  (A single-workgroup kernel for
-// bounds and orders together measured 19 us against 14 us for the scans and
-// this launch: one workgroup's strided reads of the ids cost more than the
-// launches it saves.)
+// read instead of computing them per call.  (Single-workgroup kernels for
+// bounds and orders together measured 19 us, with strided reads of the ids,
+// and 23 us, with eight ids per thread scanned in registers and the bounds
+// kept in LDS for the orders, against 17 us for the scans and this launch:
+// the two counting sorts, which run side by side here, then run one after
+// the other.)
 
 // Both orders from bounds already written (any B): block 0 the forward's,
 // block 1 the dQ kernel's.

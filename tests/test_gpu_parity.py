@@ -403,10 +403,28 @@ def test_plan_path_matches_doc_path(cid, cfg, seed, rank, lengths, use_cu):
         start, end = doc_start_end(case.lengths[b])
         assert np.array_equal(got[0, b], start[:case.Skv])
         assert np.array_equal(got[1, b], np.minimum(end[:case.Skv], case.Skv))
-    n_items = B * ((Sq * (Hq // Hkv) + 127) // 128)
-    for k in range(2):
+    G = Hq // Hkv
+    nt = (Sq * G + 127) // 128
+    n_items = B * nt
+    pos = local_positions(S, case.cfg.cp_size, rank)
+    for k, bn in enumerate((64, 128)):   # forward order, dQ order
         o = p[2 * B * case.Skv + k * n_items:2 * B * case.Skv + (k + 1) * n_items]
         assert np.array_equal(np.sort(o), np.arange(n_items))
+        # heaviest first: the number of bn-key tiles a query tile's rows
+        # reach (the union over its tokens of [start, p]) never grows along
+        # the order (costs past the last sort class share it)
+        cost = np.empty(n_items, dtype=np.int64)
+        for x in range(n_items):
+            b, t = divmod(x, nt)
+            toks = np.unique(np.arange(128 * t, min(128 * t + 128, Sq * G)) // G)
+            pp = pos[toks]
+            st = got[0, b][pp]
+            tiles = set()
+            for a, z in zip(st // bn, pp // bn):
+                tiles.update(range(a, z + 1))
+            cost[x] = min(len(tiles), 4095)
+        assert np.all(np.diff(cost[o]) <= 0), f"order {k} not heaviest first"
+
     out_a, lse_a = gpu_fwd(case, d, use_cu=use_cu)
     out_b, lse_b = M.docmask_gqa_attn_fwd(d["q"], d["k"], d["v"], cp_size=case.cfg.cp_size,
                                           cp_rank=rank, softmax_scale=case.scale, plan=plan)
