@@ -230,10 +230,11 @@ __device__ void sched_body(const int32_t* __restrict__ kfirst, const int32_t* __
   scan_s[threadIdx.x] = my_slots;
   scan_b[threadIdx.x] = my_blocks;
   __syncthreads();
+  const int tx = threadIdx.x;
   for (int o = 1; o < kScanThreads; o <<= 1) {
-    int vi = threadIdx.x >= o ? scan_i[threadIdx.x - o] : 0;
-    int vs = threadIdx.x >= o ? scan_s[threadIdx.x - o] : 0;
-    int vb = threadIdx.x >= o ? scan_b[threadIdx.x - o] : 0;
+    int vi = tx >= o ? scan_i[tx - o] : 0;
+    int vs = tx >= o ? scan_s[tx - o] : 0;
+    int vb = tx >= o ? scan_b[tx - o] : 0;
     __syncthreads();
     scan_i[threadIdx.x] += vi;
     scan_s[threadIdx.x] += vs;
@@ -287,7 +288,7 @@ __device__ void sched_body(const int32_t* __restrict__ kfirst, const int32_t* __
   scan_i[threadIdx.x] = n_items_mine;
   __syncthreads();
   for (int o = kScanThreads / 2; o > 0; o >>= 1) {
-    if (threadIdx.x < o) scan_i[threadIdx.x] += scan_i[threadIdx.x + o];
+    if (tx < o) scan_i[tx] += scan_i[tx + o];
     __syncthreads();
   }
   if (threadIdx.x == 0) {
@@ -555,7 +556,7 @@ __device__ void tile_order_body(const int32_t* __restrict__ dstart, const Geo& g
   }
 #pragma unroll
   for (int e = 0; e < kKeep; ++e)
-    if (threadIdx.x + e * kScanThreads < n) atomicAdd(&cnt[keep[e]], 1);
+    if ((int)threadIdx.x + e * kScanThreads < n) atomicAdd(&cnt[keep[e]], 1);
   for (int x = threadIdx.x + kKeep * kScanThreads; x < n; x += kScanThreads)
     atomicAdd(&cnt[cls(x)], 1);
   __syncthreads();
