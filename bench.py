@@ -302,8 +302,13 @@ def cross_study(args) -> int:
         dv = torch.empty_like(dk)
         wsf = torch.empty(max(M.lib().docmask_gqa_fwd_cross_workspace_size(1, S, Skv, Hq, Hkv, D),
                               1), dtype=torch.uint8, device="cuda")
-        wsb = torch.empty(max(M.lib().docmask_gqa_bwd_cross_workspace_size(1, S, Skv, Hq, Hkv, D),
-                              1), dtype=torch.uint8, device="cuda")
+        # the default workspace holds the dS stash; --stash recompute (or
+        # --recompute) gives the minimum, where dQ recomputes the scores
+        size_bwd = (M.lib().docmask_gqa_bwd_cross_workspace_size_min
+                    if args.recompute or args.stash == "recompute"
+                    else M.lib().docmask_gqa_bwd_cross_workspace_size)
+        wsb = torch.empty(max(size_bwd(1, S, Skv, Hq, Hkv, D), 1), dtype=torch.uint8,
+                          device="cuda")
 
         def fwd():
             M.docmask_gqa_attn_fwd_cross(q, k, v, lo_d, hi_d, out=out, lse=lse, workspace=wsf)
@@ -338,6 +343,8 @@ def cross_study(args) -> int:
               f"{res[-1]['tflops']} TFLOP/s", file=sys.stderr, flush=True)
     print(json.dumps({"study": "cross-attention forward + backward", "heads": "16/1",
                       "head_dim": 128, "samples": 32, "text": "100-199", "image": "1200-3000",
+                      "dq": "recompute" if args.recompute or args.stash == "recompute"
+                      else "stash",
                       "steps": args.steps, "warmup": args.warmup, "per_seed": res}))
     return 0
 

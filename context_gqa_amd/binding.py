@@ -76,6 +76,7 @@ SIGNATURES = {
     "docmask_gqa_attn_fwd_cross": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                                   _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "docmask_gqa_bwd_cross_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "docmask_gqa_bwd_cross_workspace_size_min": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "docmask_gqa_attn_bwd_cross": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                                   _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp,
                                                   _vp, _vp, _sz, _vp]),

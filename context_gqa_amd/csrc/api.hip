@@ -126,6 +126,12 @@ long long stash_blocks_bound(const Shape& s, int nkt) {
   return total * s.B;
 }
 
+// The same bound for cross attention (keys indexed apart from the queries):
+// a key tile's reaching queries are one range of at most the S query tokens.
+long long cross_stash_blocks_bound(const Shape& s, int nkt) {
+  return (long long)s.B * nkt * (((long long)s.S * s.G + kStashRows - 1) / kStashRows + 1);
+}
+
 // The same bound for any rank that may pass this Skv (the size queries take
 // no rank): the maximum over those ranks, or, for more than 64 ranks, every
 // key tile reaching every local row.
@@ -195,11 +201,11 @@ bool stash_addressable(const Shape& s) {
   return ((long long)s.Sq * s.G / kStashRows + 2) * (long long)kStashBlockBytes < (1LL << 31);
 }
 
-StashPlan plan_stash(const Shape& s, const Layout& L, size_t workspace_bytes) {
+// bound: stash blocks per KV head that the layout can need at most.
+StashPlan plan_stash(const Shape& s, const Layout& L, size_t workspace_bytes, long long bound) {
   StashPlan p{kRecompute, L.total_min, 0, 0};
   if (!stash_addressable(s) || workspace_bytes <= L.total_min) return p;
   const long long per_block = (long long)s.Hkv * kStashBlockBytes;
-  const long long bound = stash_blocks_bound(s, L.nkt);
   const size_t avail = workspace_bytes - L.total_min;
   if (bound < (1LL << 31) && (long long)avail >= bound * per_block) {
     p.mode = kStash;
@@ -218,13 +224,12 @@ StashPlan plan_stash(const Shape& s, const Layout& L, size_t workspace_bytes) {
   return p;
 }
 
-// Workspace of the default backward: the whole worst-case stash if it fits in
-// kDefaultStashBudget, else that budget plus the partial-dQ buffer (or the
-// whole stash, if that is smaller).
-size_t default_bwd_bytes(const Shape& s, const Layout& L) {
+// Workspace of the default backward: the whole worst-case stash (`worst`
+// blocks per KV head) if it fits in kDefaultStashBudget, else that budget
+// plus the partial-dQ buffer (or the whole stash, if that is smaller).
+size_t default_bwd_bytes(const Shape& s, const Layout& L, long long worst) {
   if (!stash_addressable(s)) return L.total_min;
   const long long per_block = (long long)s.Hkv * kStashBlockBytes;
-  const long long worst = stash_blocks_any_rank(s, L.nkt);
   const size_t full = worst < (1LL << 31) ? L.total_min + align_up((size_t)(worst * per_block))
                                           : SIZE_MAX;
   if (worst * per_block <= kDefaultStashBudget) return full;
@@ -424,7 +429,8 @@ size_t docmask_gqa_bwd_workspace_size(int32_t B, int32_t S, int32_t Skv, int32_t
   if (check_shape(B, S, S, Hq, Hkv, D, cp_size, 0, &s) != DMGQA_OK) return 0;
   s.Skv = Skv > 0 && Skv <= S ? Skv : S;
   if (s.empty) return 0;
-  return default_bwd_bytes(s, layout(s, true));
+  const Layout L = layout(s, true);
+  return default_bwd_bytes(s, L, stash_blocks_any_rank(s, L.nkt));
 }
 
 size_t docmask_gqa_bwd_workspace_size_min(int32_t B, int32_t S, int32_t Skv, int32_t Hq,
@@ -444,7 +450,7 @@ int docmask_gqa_bwd_path(int32_t B, int32_t S, int32_t Skv, int32_t Hq, int32_t 
   if (s.empty) return DMGQA_BWD_PATH_RECOMPUTE;
   const Layout L = layout(s, true);
   if (workspace_bytes < L.total_min) return DMGQA_ERR_WORKSPACE;
-  switch (plan_stash(s, L, workspace_bytes).mode) {
+  switch (plan_stash(s, L, workspace_bytes, stash_blocks_bound(s, L.nkt)).mode) {
     case kStash: return DMGQA_BWD_PATH_STASH;
     case kMixed: return DMGQA_BWD_PATH_MIXED;
     default: return DMGQA_BWD_PATH_RECOMPUTE;
@@ -529,7 +535,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   if (rc != DMGQA_OK) return rc;
   const Layout L = layout(s, true);
   if (workspace_bytes < L.total_min) return DMGQA_ERR_WORKSPACE;
-  const StashPlan plan = plan_stash(s, L, workspace_bytes);
+  const StashPlan plan = plan_stash(s, L, workspace_bytes, stash_blocks_bound(s, L.nkt));
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   rc = debug_check_docs(doc_ids, cu_seqlens, n_docs, s.B, s.S, st);
@@ -570,7 +576,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   timing_end(kKScale, st);
   if (e != hipSuccess) return DMGQA_ERR_HIP;
   timing_begin(kKSchedRowstat, st);
-  e = launch_sched_rowstat(D, nullptr, dstart, dend, g, L.nkt, L.max_split_base,
+  e = launch_sched_rowstat(D, nullptr, dstart, nullptr, dend, g, L.nkt, L.max_split_base,
                            plan.mode == kRecompute ? 0 : plan.budget, hdr, tile_info, items,
                            tile_rows, plan.mode == kRecompute ? nullptr : dq_order_ws, oh, doh, lse,
                            scale_parts, Lbuf, Nbuf, dout16, st);
@@ -589,7 +595,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
     timing_end(kKDkdv, st);
     if (e != hipSuccess) return DMGQA_ERR_HIP;
     timing_begin(kKDq, st);
-    e = launch_bwd_dq_stash(D, kh, dstart, tile_rows, stash, plan.budget, dq_order, dqh, dq_part,
+    e = launch_bwd_dq_stash(D, kh, dstart, nullptr, tile_rows, stash, plan.budget, dq_order, dqh,
+                            dq_part,
                             tile_info, partial, dk, dv, hdr, g, L.nkt, st);
     timing_end(kKDq, st);
     if (e != hipSuccess || plan.mode == kStash) return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
@@ -615,9 +622,12 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
 }
 
-// Cross-attention backward (recompute path): key ranges from lo / hi, the
-// schedule, dQ recomputing the scores (it also stores the row statistics),
-// dK/dV, and the sum of the split tiles' partial slots.
+// Cross-attention backward: key ranges from lo / hi, the exponent scan, the
+// schedule with the row statistics, then as the causal backward: with room
+// for a dS stash beyond the minimum workspace, dK/dV storing dS and dQ from
+// the stash (with the split tiles' partial slots added in its tail; mixed:
+// the key tiles past the budget recomputed by the dQ kernel); without it, dQ
+// recomputing the scores, dK/dV and the sum of the partial slots.
 int bwd_cross_impl(const void* q, const void* k, const void* v, const void* out,
                    const void* dout, const float* lse, const int32_t* lo, const int32_t* hi,
                    int32_t B, int32_t S, int32_t Skv, int32_t Hq, int32_t Hkv, int32_t D,
@@ -636,6 +646,8 @@ int bwd_cross_impl(const void* q, const void* k, const void* v, const void* out,
     return DMGQA_ERR_INVALID_ARG;
   const Layout L = layout(s, true);
   if (workspace_bytes < L.total_min) return DMGQA_ERR_WORKSPACE;
+  const StashPlan plan =
+      plan_stash(s, L, workspace_bytes, cross_stash_blocks_bound(s, L.nkt));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (debug_mode()) {
     const int drc = debug_status(docmask_gqa_check_cross_intervals(lo, hi, B, S, Skv, st));
@@ -671,15 +683,37 @@ int bwd_cross_impl(const void* q, const void* k, const void* v, const void* out,
                         (long long)s.B * s.Skv * s.Hkv * D, scale_parts, st);
   timing_end(kKScale, st);
   if (e != hipSuccess) return DMGQA_ERR_HIP;
+  // the dQ stash kernel's query-tile order, built beside the row statistics
+  int32_t* dq_order = reinterpret_cast<int32_t*>(ws + L.order);
   timing_begin(kKSchedRowstat, st);
-  e = launch_sched_rowstat(D, kfirst, lo, kend, g, L.nkt, L.max_split_base, 0, hdr, tile_info,
-                           items, tile_rows, nullptr, oh, doh, lse, scale_parts, Lbuf, Nbuf,
-                           dout16, st);
+  e = launch_sched_rowstat(D, kfirst, lo, hi, kend, g, L.nkt, L.max_split_base,
+                           plan.mode == kRecompute ? 0 : plan.budget, hdr, tile_info, items,
+                           tile_rows, plan.mode == kRecompute ? nullptr : dq_order, oh, doh, lse,
+                           scale_parts, Lbuf, Nbuf, dout16, st);
   timing_end(kKSchedRowstat, st);
   if (e != hipSuccess) return DMGQA_ERR_HIP;
+  u16* dqh = static_cast<u16*>(dq);
+  if (plan.mode != kRecompute) {
+    u16* stash = reinterpret_cast<u16*>(ws + plan.stash);
+    float* dq_part =
+        plan.mode == kMixed ? reinterpret_cast<float*>(ws + plan.dq_part) : nullptr;
+    timing_begin(kKDkdv, st);
+    e = launch_bwd_dkdv(D, qh, kh, vh, dout16, Lbuf, Nbuf, kfirst, kend, hdr, tile_info, items,
+                        tile_rows, stash, plan.budget, partial, dk, dv, g, L.nkt, st);
+    timing_end(kKDkdv, st);
+    if (e != hipSuccess) return DMGQA_ERR_HIP;
+    timing_begin(kKDq, st);
+    e = launch_bwd_dq_stash(D, kh, lo, hi, tile_rows, stash, plan.budget, dq_order, dqh, dq_part,
+                            tile_info, partial, dk, dv, hdr, g, L.nkt, st);
+    timing_end(kKDq, st);
+    if (e != hipSuccess || plan.mode == kStash) return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
+    timing_begin(kKDqRest, st);
+    e = launch_bwd_dq(D, qh, kh, vh, oh, doh, lse, lo, hi, dqh, tile_rows, dq_part, g, L.nkt, st);
+    timing_end(kKDqRest, st);
+    return e == hipSuccess ? DMGQA_OK : DMGQA_ERR_HIP;
+  }
   timing_begin(kKDq, st);
-  e = launch_bwd_dq(D, qh, kh, vh, oh, doh, lse, lo, hi, static_cast<u16*>(dq), tile_rows,
-                    nullptr, g, L.nkt, st);
+  e = launch_bwd_dq(D, qh, kh, vh, oh, doh, lse, lo, hi, dqh, tile_rows, nullptr, g, L.nkt, st);
   timing_end(kKDq, st);
   if (e != hipSuccess) return DMGQA_ERR_HIP;
   timing_begin(kKDkdv, st);
@@ -908,6 +942,14 @@ int docmask_gqa_attn_fwd_cross(const void* q, const void* k, const void* v, cons
 
 size_t docmask_gqa_bwd_cross_workspace_size(int32_t B, int32_t S, int32_t Skv, int32_t Hq,
                                             int32_t Hkv, int32_t D) {
+  Shape s;
+  if (check_cross_shape(B, S, Skv, Hq, Hkv, D, &s) != DMGQA_OK || s.empty) return 0;
+  const Layout L = layout(s, true);
+  return default_bwd_bytes(s, L, cross_stash_blocks_bound(s, L.nkt));
+}
+
+size_t docmask_gqa_bwd_cross_workspace_size_min(int32_t B, int32_t S, int32_t Skv, int32_t Hq,
+                                                int32_t Hkv, int32_t D) {
   Shape s;
   if (check_cross_shape(B, S, Skv, Hq, Hkv, D, &s) != DMGQA_OK || s.empty) return 0;
   return layout(s, true).total_min;

@@ -58,7 +58,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const int32_t* dh = CROSS ? dhi + (size_t)b * g.S : nullptr;
   const int4* trow_b = tile_rows + (size_t)b * nkt;
   if (dq_part != nullptr) {
-    const QTileKeys k2 = qtile_keys<BM, kDkdvBN>(row0, ds, g);
+    const QTileKeys k2 =
+        CROSS ? qtile_keys_iv<BM, kDkdvBN>(row0, ds, dh, g) : qtile_keys<BM, kDkdvBN>(row0, ds, g);
     const int kt_last = k2.nb > 0 ? k2.b0 + k2.nb - 1 : k2.a0 + k2.na - 1;
     if (k2.na + k2.nb == 0 || trow_b[kt_last].w >= 0) return;
   }

@@ -69,11 +69,13 @@ __device__ __forceinline__ void dma_asm16(const void* sbase, unsigned voff, unsi
 // 128 rows; their K tiles stream through two LDS stages (DMA one tile
 // ahead), and the wave's dS operands are loaded into registers two tiles
 // ahead.  Rows of a block outside the tile's reach hold
-// no stash data and are zeroed.
-template <int D>
+// no stash data and are zeroed.  CROSS: query position p reaches keys
+// dstart[p] .. dhi[p]-1 (both [B, S], keys indexed on their own); else keys
+// dstart[p] .. p (dstart [B, Skv]).
+template <int D, bool CROSS>
 __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
     const u16* __restrict__ k, const int32_t* __restrict__ dstart,
-    const int4* __restrict__ tile_rows, const u16* __restrict__ stash, int stash_kvh_blocks,
+    const int32_t* __restrict__ dhi, const int4* __restrict__ tile_rows, const u16* __restrict__ stash, int stash_kvh_blocks,
     const int32_t* __restrict__ order, u16* __restrict__ dq, float* __restrict__ dq_part,
     const int2* __restrict__ tile_info, const float* __restrict__ partial,
     float* __restrict__ dk, float* __restrict__ dv, const SchedHeader* __restrict__ hdr, Geo g,
@@ -110,8 +112,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
     off_t[hf] = (4 * h + (s16 >> 2) + 8 * hf) * 64 +
                 16 * ((2 * (grp & 1) + ((s16 & 3) >> 1)) ^ ((h + 2 * hf) & 3)) + 8 * (s16 & 1);
 
-  const int32_t* ds = dstart + (size_t)b * g.Skv;
-  const QTileKeys kr = qtile_keys<128, BN>(128 * qb, ds, g);
+  const int32_t* ds = dstart + (size_t)b * (CROSS ? g.S : g.Skv);
+  const QTileKeys kr =
+      CROSS ? qtile_keys_iv<128, BN>(128 * qb, ds, dhi + (size_t)b * g.S, g)
+            : qtile_keys<128, BN>(128 * qb, ds, g);
   const int ntiles = kr.na + kr.nb;
   const size_t kvstride = (size_t)g.Hkv * D;
   const u16* kbase = k + (size_t)b * g.Skv * kvstride + (size_t)kvh * D;
@@ -278,25 +282,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_stash_kernel(
   }
 }
 
-hipError_t launch_bwd_dq_stash(int D, const u16* k, const int32_t* dstart, const int4* tile_rows,
-                               const u16* stash, int stash_kvh_blocks, const int32_t* order,
-                               u16* dq, float* dq_part, const int2* tile_info,
-                               const float* partial, float* dk, float* dv,
+hipError_t launch_bwd_dq_stash(int D, const u16* k, const int32_t* dstart, const int32_t* dhi,
+                               const int4* tile_rows, const u16* stash, int stash_kvh_blocks,
+                               const int32_t* order, u16* dq, float* dq_part,
+                               const int2* tile_info, const float* partial, float* dk, float* dv,
                                const SchedHeader* hdr, const Geo& g, int nkt, hipStream_t st) {
   const int nqb = (g.Sq * g.G + 127) / 128;
   const unsigned grid = (unsigned)nqb * g.B * g.Hkv;
-  if (D == 128)
-    bwd_dq_stash_kernel<128><<<grid + reduce_grid<128>(g, nkt), 256, 0, st>>>(
-        k, dstart, tile_rows, stash, stash_kvh_blocks, order, dq, dq_part, tile_info, partial, dk,
-        dv, hdr, g,
-        nkt,
-        (int)grid);
-  else
-    bwd_dq_stash_kernel<64><<<grid + reduce_grid<64>(g, nkt), 256, 0, st>>>(
-        k, dstart, tile_rows, stash, stash_kvh_blocks, order, dq, dq_part, tile_info, partial, dk,
-        dv, hdr, g,
-        nkt,
-        (int)grid);
+#define DMGQA_DQS(DD, CC)                                                                      \
+  bwd_dq_stash_kernel<DD, CC><<<grid + reduce_grid<DD>(g, nkt), 256, 0, st>>>(                 \
+      k, dstart, dhi, tile_rows, stash, stash_kvh_blocks, order, dq, dq_part, tile_info, partial, \
+      dk, dv, hdr, g, nkt, (int)grid)
+  if (D == 128) {
+    if (dhi) DMGQA_DQS(128, true); else DMGQA_DQS(128, false);
+  } else {
+    if (dhi) DMGQA_DQS(64, true); else DMGQA_DQS(64, false);
+  }
+#undef DMGQA_DQS
   return hipGetLastError();
 }
 

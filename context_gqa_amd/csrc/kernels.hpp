@@ -90,13 +90,16 @@ hipError_t launch_bwd_dkdv(int D, const u16* q, const u16* k, const u16* v, cons
 // Schedule (block 0, with the fp16 scales into hdr), the dQ tile order
 // (block 1; skipped when dq_order is null) and the row statistics (the other
 // blocks: -lse/scale, -D * 2^(eo+ev), and dO' = dO * 2^eo in fp16 into
-// dout16) in one launch.  kfirst: see the schedule note above.
+// dout16) in one launch.  kfirst: see the schedule note above.  The dQ
+// order takes dstart (and dhi, the explicit ends, for cross attention; null
+// for causal interval masks) as the forward's order does.
 hipError_t launch_sched_rowstat(int D, const int32_t* kfirst, const int32_t* dstart,
-                                const int32_t* dend, const Geo& g, int nkt, int max_split_base,
-                                int stash_budget, SchedHeader* hdr, int2* tile_info, int2* items,
-                                int4* tile_rows, int32_t* dq_order, const u16* out,
-                                const u16* dout, const float* lse, const int2* scale_parts,
-                                float* Lbuf, float* Nbuf, u16* dout16, hipStream_t st);
+                                const int32_t* dhi, const int32_t* dend, const Geo& g, int nkt,
+                                int max_split_base, int stash_budget, SchedHeader* hdr,
+                                int2* tile_info, int2* items, int4* tile_rows, int32_t* dq_order,
+                                const u16* out, const u16* dout, const float* lse,
+                                const int2* scale_parts, float* Lbuf, float* Nbuf, u16* dout16,
+                                hipStream_t st);
 // Heaviest-first dispatch order of the forward's query tiles (one block):
 // order[i] = b * nt + tile for B * nt items, nt = ceil(Sq * G / kFwdBM).
 // Both query-tile orders of a batch plan from its bounds (two workgroups).
@@ -107,8 +110,10 @@ hipError_t launch_tile_order_fwd(const int32_t* dstart, const int32_t* dhi, cons
 // dQ from the dS stash, and (in workgroups appended to its grid) the sum of
 // the partial dK/dV slots.  A query tile that also reaches key tiles without
 // stash writes its unscaled fp32 partial sums to dq_part instead of dq (only
-// when dq_part is not null), for launch_bwd_dq to finish.
-hipError_t launch_bwd_dq_stash(int D, const u16* k, const int32_t* dstart, const int4* tile_rows,
+// when dq_part is not null), for launch_bwd_dq to finish.  dhi as for
+// launch_fwd.
+hipError_t launch_bwd_dq_stash(int D, const u16* k, const int32_t* dstart, const int32_t* dhi,
+                               const int4* tile_rows,
                                const u16* stash, int stash_kvh_blocks, const int32_t* order, u16* dq,
                                float* dq_part, const int2* tile_info, const float* partial,
                                float* dk, float* dv, const SchedHeader* hdr, const Geo& g, int nkt,

@@ -618,9 +618,10 @@ __global__ __launch_bounds__(kScanThreads) void plan_orders(const int32_t* __res
 // (block 1, unless dq_order is null) and the row statistics (the other
 // blocks) in one launch: the single-block parts run beside the row
 // statistics.
-template <int D>
+template <int D, bool CROSS>
 __global__ __launch_bounds__(kScanThreads) void sched_rowstat(
     const int32_t* __restrict__ kfirst, const int32_t* __restrict__ dstart,
+    const int32_t* __restrict__ dhi,
     const int32_t* __restrict__ dend, Geo g, int nkt, int max_split_base, int stash_budget,
     SchedHeader* __restrict__ hdr, int2* __restrict__ tile_info, int2* __restrict__ items,
     int4* __restrict__ tile_rows, int32_t* __restrict__ dq_order, const u16* __restrict__ out,
@@ -638,7 +639,7 @@ __global__ __launch_bounds__(kScanThreads) void sched_rowstat(
       hdr->dv_mul = __builtin_amdgcn_ldexpf(1.f, -ex.x);
     }
   } else if (blockIdx.x == 1) {
-    if (dq_order != nullptr) tile_order_body<kDkdvBN>(dstart, g, dq_order);
+    if (dq_order != nullptr) tile_order_body<kDkdvBN, CROSS>(dstart, g, dq_order, dhi);
   } else {
     rowstat_rows<D>(out, dout, lse, Lbuf, Nbuf, dout16, g.B * g.Sq * g.Hq, 1.f / g.scale,
                     scale_parts, (int)blockIdx.x - 2);
@@ -679,20 +680,24 @@ hipError_t launch_prep_cross_keys(const int32_t* lo, const int32_t* hi, int B, i
 }
 
 hipError_t launch_sched_rowstat(int D, const int32_t* kfirst, const int32_t* dstart,
-                                const int32_t* dend, const Geo& g, int nkt, int max_split_base,
-                                int stash_budget, SchedHeader* hdr, int2* tile_info, int2* items,
-                                int4* tile_rows, int32_t* dq_order, const u16* out,
-                                const u16* dout, const float* lse, const int2* scale_parts,
-                                float* Lbuf, float* Nbuf, u16* dout16, hipStream_t st) {
+                                const int32_t* dhi, const int32_t* dend, const Geo& g, int nkt,
+                                int max_split_base, int stash_budget, SchedHeader* hdr,
+                                int2* tile_info, int2* items, int4* tile_rows, int32_t* dq_order,
+                                const u16* out, const u16* dout, const float* lse,
+                                const int2* scale_parts, float* Lbuf, float* Nbuf, u16* dout16,
+                                hipStream_t st) {
   const int nrows = g.B * g.Sq * g.Hq;
   const int rows_per_block = kScanThreads / (D / 8) * kRowstatPasses;
   const unsigned grid = 2u + (unsigned)((nrows + rows_per_block - 1) / rows_per_block);
-#define DMGQA_RS(DD)                                                                          \
-  sched_rowstat<DD><<<grid, kScanThreads, 0, st>>>(kfirst, dstart, dend, g, nkt, max_split_base, \
-                                                   stash_budget, hdr, tile_info, items,          \
-                                                   tile_rows, dq_order, out, dout, lse,          \
-                                                   scale_parts, Lbuf, Nbuf, dout16)
-  if (D == 128) DMGQA_RS(128); else DMGQA_RS(64);
+#define DMGQA_RS(DD, CC)                                                                      \
+  sched_rowstat<DD, CC><<<grid, kScanThreads, 0, st>>>(                                      \
+      kfirst, dstart, dhi, dend, g, nkt, max_split_base, stash_budget, hdr, tile_info, items, \
+      tile_rows, dq_order, out, dout, lse, scale_parts, Lbuf, Nbuf, dout16)
+  if (D == 128) {
+    if (dhi) DMGQA_RS(128, true); else DMGQA_RS(128, false);
+  } else {
+    if (dhi) DMGQA_RS(64, true); else DMGQA_RS(64, false);
+  }
 #undef DMGQA_RS
   return hipGetLastError();
 }

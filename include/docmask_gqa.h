@@ -239,12 +239,23 @@ int docmask_gqa_interval_bounds(const int32_t* lo, int32_t B, int32_t S,
  * Forward workspace: docmask_gqa_fwd_cross_workspace_size bytes (the tile
  * order).  The backward takes the forward's out and lse and dout, and writes
  * dq and dk, dv (summed over each KV head's query heads, zero for keys no
- * query reaches) as the causal backward does; its dQ always recomputes the
- * scores (no stash).  Workspace: docmask_gqa_bwd_cross_workspace_size bytes
- * (the keys' query ranges, the schedule, the row statistics and the partial
- * sums).  Only the image encoder and the cross-attention layers are trained
- * in that setting (same section), so this is the backward that runs.
- * Errors and ownership as above. */
+ * query reaches) as the causal backward does, with the same three ways of
+ * forming dQ, chosen from workspace_bytes:
+ *  - docmask_gqa_bwd_cross_workspace_size_min bytes (the keys' query ranges,
+ *    the schedule, the row statistics and the partial sums): no stash, dQ
+ *    recomputes the scores;
+ *  - more: a bf16 dS stash in the rest, key tiles stashed in order while
+ *    their blocks fit (every tile when the rest holds the worst case, in
+ *    which each key tile reaches all S query tokens; otherwise the mixed
+ *    form, which also needs an fp32 [B, S, Hq, D] partial-dQ buffer and
+ *    recomputes the key tiles past the budget);
+ *  - docmask_gqa_bwd_cross_workspace_size: the minimum plus the worst-case
+ *    stash, or the partial-dQ buffer plus a 2 GiB stash budget when the
+ *    worst case is larger (at the multimodal sizes above the blocks the
+ *    samples actually reach, a few hundred MiB, fit in that budget).
+ * Only the image encoder and the cross-attention layers are trained in that
+ * setting (same section), so this is the backward that runs.  Errors and
+ * ownership as above. */
 size_t docmask_gqa_fwd_cross_workspace_size(int32_t B, int32_t S, int32_t Skv,
                                             int32_t Hq, int32_t Hkv, int32_t D);
 int docmask_gqa_attn_fwd_cross(const void* q, const void* k, const void* v,
@@ -255,6 +266,8 @@ int docmask_gqa_attn_fwd_cross(const void* q, const void* k, const void* v,
                                size_t workspace_bytes, void* stream);
 size_t docmask_gqa_bwd_cross_workspace_size(int32_t B, int32_t S, int32_t Skv,
                                             int32_t Hq, int32_t Hkv, int32_t D);
+size_t docmask_gqa_bwd_cross_workspace_size_min(int32_t B, int32_t S, int32_t Skv,
+                                                int32_t Hq, int32_t Hkv, int32_t D);
 int docmask_gqa_attn_bwd_cross(const void* q, const void* k, const void* v,
                                const void* out, const void* dout,
                                const float* lse, const int32_t* lo,

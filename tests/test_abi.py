@@ -383,14 +383,25 @@ def _cross_bwd(**kw):
 
 def test_cross_bwd_workspace_size():
     f = M.lib().docmask_gqa_bwd_cross_workspace_size
-    n = f(1, 63, 300, 4, 1, 64)
+    fmin = M.lib().docmask_gqa_bwd_cross_workspace_size_min
+    n = fmin(1, 63, 300, 4, 1, 64)
     # the keys' query ranges (2 x Skv int32) come first, then the schedule,
     # the row statistics (2 x S x Hq fp32) and the partial-sum slots
     assert n >= 2 * 300 * 4 + 2 * 63 * 4 * 4
+    # the default adds the worst-case dS stash: every one of the 3 key
+    # tiles reaching all 63 x 4 query rows (8 blocks of 32 rows, one more
+    # for alignment), 32 x 128 bf16 per block
+    assert f(1, 63, 300, 4, 1, 64) >= n + 3 * 9 * 32 * 128 * 2
+    # past the 2 GiB stash budget: the budget plus the fp32 partial-dQ
+    # buffer [B, S, Hq, D]
+    big = f(1, 4870, 66775, 16, 1, 128)
+    assert (2 << 30) + 4870 * 16 * 128 * 4 <= big - fmin(1, 4870, 66775, 16, 1, 128) \
+        <= (2 << 30) + 4870 * 16 * 128 * 4 + (1 << 20)
     assert f(1, 4870, 66775, 16, 1, 128) > f(1, 4870, 6000, 16, 1, 128)
-    assert f(0, 63, 300, 4, 1, 64) == 0
-    assert f(1, 63, 0, 4, 1, 64) == 0
-    assert f(1, 63, 300, 6, 4, 64) == 0
+    for g in (f, fmin):
+        assert g(0, 63, 300, 4, 1, 64) == 0
+        assert g(1, 63, 0, 4, 1, 64) == 0
+        assert g(1, 63, 300, 6, 4, 64) == 0
 
 
 @pytest.mark.parametrize("kw,want", [

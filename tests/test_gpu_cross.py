@@ -59,26 +59,66 @@ def test_cross_fwd_full_oracle(cid, texts, images, Hq, Hkv, D, seed):
     compare("lse", host(lse), rlse)
 
 
-def _cross_fwd_bwd(q, k, v, do, lo, hi, scale):
+ALIGN = 256   # workspace sections are aligned to this many bytes
+
+
+def _align(x):
+    return (x + ALIGN - 1) // ALIGN * ALIGN
+
+
+def reached_stash_blocks(lo, hi, Skv, G):
+    """dS stash blocks (32 query rows x 128 keys) the layout reaches: per
+    128-key tile, its reaching queries [first p with hi[p] > t0, first p with
+    lo[p] > last key) as query rows x G, in blocks aligned to 32 rows."""
+    total = 0
+    for b in range(lo.shape[0]):
+        for t0 in range(0, Skv, 128):
+            tl = min(t0 + 127, Skv - 1)
+            p0 = int(np.searchsorted(hi[b], t0, side="right"))
+            p1 = int(np.searchsorted(lo[b], tl, side="right"))
+            if p1 > p0:
+                total += -(-p1 * G // 32) - (p0 * G // 32)
+    return total
+
+
+def bwd_workspace(kind, lo, hi, B, S, Skv, Hq, Hkv, D):
+    """'min': no stash (dQ recomputes the scores); 'default': the size query
+    (the stash); 'mixed': the minimum, the fp32 partial-dQ buffer and half of
+    the stash blocks the layout reaches, so that some key tiles are stashed
+    and the rest recomputed."""
+    if kind == "default":
+        return None
+    n = M.lib().docmask_gqa_bwd_cross_workspace_size_min(B, S, Skv, Hq, Hkv, D)
+    if kind == "mixed":
+        need = reached_stash_blocks(lo, hi, Skv, Hq // Hkv)
+        n += _align(B * S * Hq * D * 4) + max(need // 2, 1) * Hkv * 32 * 128 * 2
+    return torch.empty(n, dtype=torch.uint8, device="cuda")
+
+
+def _cross_fwd_bwd(q, k, v, do, lo, hi, scale, ws="default"):
     lo_d, hi_d = torch.from_numpy(lo).cuda(), torch.from_numpy(hi).cuda()
     qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
     out, lse = M.docmask_gqa_attn_fwd_cross(qd, kd, vd, lo_d, hi_d, softmax_scale=scale)
+    B, S, Hq, D = q.shape
+    work = bwd_workspace(ws, lo, hi, B, S, k.shape[1], Hq, k.shape[2], D)
     dq, dk, dv = M.docmask_gqa_attn_bwd_cross(qd, kd, vd, out, dod, lse, lo_d, hi_d,
-                                              softmax_scale=scale)
+                                              softmax_scale=scale, workspace=work)
     torch.cuda.synchronize()
     return out, lse, dq, dk, dv
 
 
+@pytest.mark.parametrize("ws", ["default", "min", "mixed"])
 @pytest.mark.parametrize("cid,texts,images,Hq,Hkv,D,seed", CASES, ids=[c[0] for c in CASES])
-def test_cross_bwd_full_oracle(cid, texts, images, Hq, Hkv, D, seed):
-    """Every element of the backward against the oracle; image tokens no
-    text token attends to get exactly zero dk / dv."""
+def test_cross_bwd_full_oracle(cid, texts, images, Hq, Hkv, D, seed, ws):
+    """Every element of the backward against the oracle, on each way of
+    forming dQ (stash, recompute, mixed); image tokens no text token attends
+    to get exactly zero dk / dv."""
     lo, hi, q, k, v, do = _case(texts, images, Hq, Hkv, D, seed)
     B, S = lo.shape
     Skv = k.shape[1]
-    say(f"[cross bwd {cid}] B={B} S={S} Skv={Skv} Hq={Hq} Hkv={Hkv} D={D}")
+    say(f"[cross bwd {cid} ws={ws}] B={B} S={S} Skv={Skv} Hq={Hq} Hkv={Hkv} D={D}")
     scale = 1.0 / np.sqrt(D)
-    out, lse, dq, dk, dv = _cross_fwd_bwd(q, k, v, do, lo, hi, scale)
+    out, lse, dq, dk, dv = _cross_fwd_bwd(q, k, v, do, lo, hi, scale, ws)
     rdq, rdk, rdv, rout, rlse = oracle.attn_bwd(q, k, v, do, None, 1, 0, scale,
                                                 return_fwd=True, lo=lo, hi=hi)
     compare("out", host(out), rout)
@@ -105,15 +145,16 @@ def test_cross_bwd_multimodal_elementwise():
     q, k, v, do = W.cross_tensors(1, S, Skv, 16, 1, 128, seed=12, dout=True)
     say(f"[cross bwd multimodal] S={S} Skv={Skv}")
     scale = 1.0 / np.sqrt(128)
-    out, lse, dq, dk, dv = _cross_fwd_bwd(q, k, v, do, lo[None], hi[None], scale)
     rdq, rdk, rdv, rout, rlse = oracle.attn_bwd(q, k, v, do, None, 1, 0, scale,
                                                 return_fwd=True, lo=lo[None], hi=hi[None])
-    tag = f"cross multimodal S={S} Skv={Skv}"
-    compare("out", host(out), rout, tag=tag)
-    compare("lse", host(lse), rlse, tag=tag)
-    compare("dq", host(dq), rdq, tag=tag)
-    compare("dk", host(dk), rdk, tag=tag)
-    compare("dv", host(dv), rdv, tag=tag)
+    for ws in ("default", "mixed"):
+        out, lse, dq, dk, dv = _cross_fwd_bwd(q, k, v, do, lo[None], hi[None], scale, ws)
+        tag = f"cross multimodal S={S} Skv={Skv} ws={ws}"
+        compare("out", host(out), rout, tag=tag)
+        compare("lse", host(lse), rlse, tag=tag)
+        compare("dq", host(dq), rdq, tag=tag)
+        compare("dk", host(dk), rdk, tag=tag)
+        compare("dv", host(dv), rdv, tag=tag)
 
 
 def test_check_cross_intervals():
