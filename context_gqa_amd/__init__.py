@@ -12,5 +12,5 @@ from .binding import (  # noqa: F401
     docmask_gqa_attn_fwd_cross, docmask_gqa_check_cross_intervals, docmask_gqa_attn_bwd_cross,
     docmask_gqa_bwd_workspace_size_full, docmask_gqa_bwd_path, DMGQA_BWD_PATH_RECOMPUTE,
     DMGQA_BWD_PATH_STASH, DMGQA_BWD_PATH_MIXED, docmask_gqa_attn_fwd_noalloc,
-    docmask_gqa_batch_plan, docmask_gqa_batch_plan_size,
+    docmask_gqa_batch_plan, docmask_gqa_batch_plan_size, docmask_gqa_bwd_cross_path,
 )

@@ -77,6 +77,7 @@ SIGNATURES = {
                                                   _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
     "docmask_gqa_bwd_cross_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "docmask_gqa_bwd_cross_workspace_size_min": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "docmask_gqa_bwd_cross_path": (ctypes.c_int, [_i32] * 6 + [_sz]),
     "docmask_gqa_attn_bwd_cross": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                                   _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp,
                                                   _vp, _vp, _sz, _vp]),
@@ -142,6 +143,12 @@ def docmask_gqa_bwd_path(B, S, Skv, Hq, Hkv, D, cp_size, cp_rank, workspace_byte
     status)."""
     return int(lib().docmask_gqa_bwd_path(B, S, Skv, Hq, Hkv, D, cp_size, cp_rank,
                                           int(workspace_bytes)))
+
+
+def docmask_gqa_bwd_cross_path(B, S, Skv, Hq, Hkv, D, workspace_bytes) -> int:
+    """DMGQA_BWD_PATH_* the cross-attention backward takes with this
+    workspace (or a negative status)."""
+    return int(lib().docmask_gqa_bwd_cross_path(B, S, Skv, Hq, Hkv, D, int(workspace_bytes)))
 
 
 def _ptr(t) -> Optional[int]:

@@ -955,6 +955,21 @@ size_t docmask_gqa_bwd_cross_workspace_size_min(int32_t B, int32_t S, int32_t Sk
   return layout(s, true).total_min;
 }
 
+int docmask_gqa_bwd_cross_path(int32_t B, int32_t S, int32_t Skv, int32_t Hq, int32_t Hkv,
+                               int32_t D, size_t workspace_bytes) {
+  Shape s;
+  const int rc = check_cross_shape(B, S, Skv, Hq, Hkv, D, &s);
+  if (rc != DMGQA_OK) return rc;
+  if (s.empty) return DMGQA_BWD_PATH_RECOMPUTE;
+  const Layout L = layout(s, true);
+  if (workspace_bytes < L.total_min) return DMGQA_ERR_WORKSPACE;
+  switch (plan_stash(s, L, workspace_bytes, cross_stash_blocks_bound(s, L.nkt)).mode) {
+    case kStash: return DMGQA_BWD_PATH_STASH;
+    case kMixed: return DMGQA_BWD_PATH_MIXED;
+    default: return DMGQA_BWD_PATH_RECOMPUTE;
+  }
+}
+
 int docmask_gqa_attn_bwd_cross(const void* q, const void* k, const void* v, const void* out,
                                const void* dout, const float* lse, const int32_t* lo,
                                const int32_t* hi, int32_t B, int32_t S, int32_t Skv, int32_t Hq,

@@ -268,6 +268,14 @@ size_t docmask_gqa_bwd_cross_workspace_size(int32_t B, int32_t S, int32_t Skv,
                                             int32_t Hq, int32_t Hkv, int32_t D);
 size_t docmask_gqa_bwd_cross_workspace_size_min(int32_t B, int32_t S, int32_t Skv,
                                                 int32_t Hq, int32_t Hkv, int32_t D);
+/* Which way the cross-attention backward will form dQ with a workspace of
+ * workspace_bytes (no HIP call): the DMGQA_BWD_PATH_* values of
+ * docmask_gqa_bwd_path, or a negative status for shapes the backward would
+ * reject (DMGQA_ERR_WORKSPACE below the minimum).  The stash path needs
+ * the worst case above; smaller workspaces past the minimum and the
+ * partial-dQ buffer give the mixed path. */
+int docmask_gqa_bwd_cross_path(int32_t B, int32_t S, int32_t Skv, int32_t Hq,
+                               int32_t Hkv, int32_t D, size_t workspace_bytes);
 int docmask_gqa_attn_bwd_cross(const void* q, const void* k, const void* v,
                                const void* out, const void* dout,
                                const float* lse, const int32_t* lo,

@@ -404,6 +404,31 @@ def test_cross_bwd_workspace_size():
         assert g(1, 63, 300, 6, 4, 64) == 0
 
 
+def test_cross_bwd_path():
+    """The dQ path a workspace selects for the cross backward: the minimum
+    recomputes, the worst-case stash stashes every tile, sizes in between
+    (past the partial-dQ buffer) give the mixed path; at the multimodal
+    sizes the default (a 2 GiB budget) is the mixed path."""
+    f = M.lib().docmask_gqa_bwd_cross_workspace_size
+    fmin = M.lib().docmask_gqa_bwd_cross_workspace_size_min
+    p = M.docmask_gqa_bwd_cross_path
+    small = (1, 63, 300, 4, 1, 64)
+    n, full = fmin(*small), f(*small)
+    assert p(*small, n) == M.DMGQA_BWD_PATH_RECOMPUTE
+    assert p(*small, n - 1) == WS
+    assert p(*small, full) == M.DMGQA_BWD_PATH_STASH
+    # below the worst case: the partial dQ [1, 63, 4, 64] fp32, then blocks
+    dqb = 63 * 4 * 64 * 4
+    assert p(*small, n + dqb) == M.DMGQA_BWD_PATH_RECOMPUTE
+    assert p(*small, n + dqb + 4096 + 32 * 128 * 2) == M.DMGQA_BWD_PATH_MIXED
+    assert p(*small, full - 32 * 128 * 2) == M.DMGQA_BWD_PATH_MIXED
+    big = (1, 4870, 66775, 16, 1, 128)
+    assert p(*big, f(*big)) == M.DMGQA_BWD_PATH_MIXED
+    assert p(*big, fmin(*big)) == M.DMGQA_BWD_PATH_RECOMPUTE
+    assert p(1, 63, 300, 6, 4, 64, 1 << 20) == INV
+    assert p(1, 0, 300, 4, 1, 64, 0) == M.DMGQA_BWD_PATH_RECOMPUTE
+
+
 @pytest.mark.parametrize("kw,want", [
     (dict(q=None), INV), (dict(out=None), INV), (dict(dout=None), INV), (dict(lse=None), INV),
     (dict(lo=None), INV), (dict(hi=None), INV), (dict(dq=None), INV), (dict(dk=None), INV),

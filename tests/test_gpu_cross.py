@@ -85,7 +85,9 @@ def bwd_workspace(kind, lo, hi, B, S, Skv, Hq, Hkv, D):
     """'min': no stash (dQ recomputes the scores); 'default': the size query
     (the stash); 'mixed': the minimum, the fp32 partial-dQ buffer and half of
     the stash blocks the layout reaches, so that some key tiles are stashed
-    and the rest recomputed."""
+    and the rest recomputed (with a single key tile, where the partial-dQ
+    buffer alone is as large as the whole stash, that size stashes every
+    tile: tiny_d64, fewer_keys)."""
     if kind == "default":
         return None
     n = M.lib().docmask_gqa_bwd_cross_workspace_size_min(B, S, Skv, Hq, Hkv, D)
@@ -100,7 +102,22 @@ def _cross_fwd_bwd(q, k, v, do, lo, hi, scale, ws="default"):
     qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
     out, lse = M.docmask_gqa_attn_fwd_cross(qd, kd, vd, lo_d, hi_d, softmax_scale=scale)
     B, S, Hq, D = q.shape
-    work = bwd_workspace(ws, lo, hi, B, S, k.shape[1], Hq, k.shape[2], D)
+    Skv, Hkv = k.shape[1], k.shape[2]
+    work = bwd_workspace(ws, lo, hi, B, S, Skv, Hq, Hkv, D)
+    nbytes = (M.lib().docmask_gqa_bwd_cross_workspace_size(B, S, Skv, Hq, Hkv, D)
+              if work is None else work.numel())
+    path = M.docmask_gqa_bwd_cross_path(B, S, Skv, Hq, Hkv, D, nbytes)
+    # the smallest mixed workspace (the partial dQ and one block) already
+    # holds the worst case when it is one or two blocks: then it stashes
+    one_block = (M.lib().docmask_gqa_bwd_cross_workspace_size_min(B, S, Skv, Hq, Hkv, D) +
+                 _align(B * S * Hq * D * 4) + Hkv * 32 * 128 * 2)
+    mixed_ok = M.docmask_gqa_bwd_cross_path(B, S, Skv, Hq, Hkv, D, one_block) == \
+        M.DMGQA_BWD_PATH_MIXED
+    want = {"min": (M.DMGQA_BWD_PATH_RECOMPUTE,),
+            "mixed": (M.DMGQA_BWD_PATH_MIXED if mixed_ok else M.DMGQA_BWD_PATH_STASH,),
+            "default": (M.DMGQA_BWD_PATH_STASH, M.DMGQA_BWD_PATH_MIXED)}[ws]
+    assert path in want, (ws, path)
+    say(f"  dQ path {path} ({ws} workspace, {nbytes} bytes)")
     dq, dk, dv = M.docmask_gqa_attn_bwd_cross(qd, kd, vd, out, dod, lse, lo_d, hi_d,
                                               softmax_scale=scale, workspace=work)
     torch.cuda.synchronize()
