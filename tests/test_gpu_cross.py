@@ -174,6 +174,23 @@ def test_cross_bwd_multimodal_elementwise():
         compare("dv", host(dv), rdv, tag=tag)
 
 
+@pytest.mark.parametrize("ws", ["default", "mixed", "min"])
+def test_cross_deterministic(ws):
+    """Two calls on the same inputs give bit-identical out, lse, dq, dk and
+    dv on each dQ path (the split dK/dV items are summed in a fixed order),
+    at the multimodal size."""
+    text, image = W.cross_lengths(32, seed=13)
+    lo, hi = W.cross_bounds(text, image)
+    S, Skv = sum(text), sum(image)
+    q, k, v, do = W.cross_tensors(1, S, Skv, 16, 1, 128, seed=14, dout=True)
+    say(f"[cross deterministic ws={ws}] S={S} Skv={Skv}")
+    scale = 1.0 / np.sqrt(128)
+    a = _cross_fwd_bwd(q, k, v, do, lo[None], hi[None], scale, ws)
+    b = _cross_fwd_bwd(q, k, v, do, lo[None], hi[None], scale, ws)
+    for x, y, n in zip(a, b, ("out", "lse", "dq", "dk", "dv")):
+        assert torch.equal(x, y), n
+
+
 def test_check_cross_intervals():
     lo, hi = W.cross_bounds([3, 5, 4], [10, 2, 7])
     Skv = 19
