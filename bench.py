@@ -479,7 +479,8 @@ def main(argv=None) -> int:
     ap.add_argument("--stash", choices=("default", "full", "recompute"), default="default",
                     help="backward workspace: the library's default (the whole dS stash, or a "
                          "2 GiB stash budget for long shares), the whole worst-case stash, "
-                         "or the minimum (no stash: dQ recomputes the scores)")
+                         "or the minimum (no stash: dQ recomputes the scores); with --cross "
+                         "'full' is the default")
     ap.add_argument("--recompute", action="store_true", help="same as --stash recompute")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run three device-to-device copies of 512 MiB (the reference "
