@@ -73,3 +73,50 @@ def test_kernel_hash_follows_code_not_comments():
     assert c("x = 1;") != c("x = 2;")
     assert c('asm("v_mov_b32 %0, %1")') != c('asm("v_mov_b32  %0, %1")')
     assert len(bench.kernel_source_hash("bwd_dkdv")) == 16
+
+
+def _pmc_csv(path, counter, rows):
+    import csv
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, value in rows:
+            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_traffic_from_pmc_scales_by_the_copy(tmp_path):
+    """Per-launch bytes: the kernel's average counter reading (KiB) times
+    the factor that maps the copy kernel's reading onto the bytes it moved;
+    other kernels and counters are ignored."""
+    n = bench.COPY_CALIBRATION_BYTES
+    ours = "void dmgqa::bwd_dkdv_kernel<128, true>(unsigned short const*)"
+    copy = "__amd_rocclr_copyBuffer"
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    # the copy reads n bytes but the counter shows 2n (scale 1/2); it
+    # writes n bytes and the counter shows n (scale 1)
+    _pmc_csv(fetch, "FETCH_SIZE", [(ours, 1000.0), (ours, 1200.0), (copy, 2 * n / 1024),
+                                   ("dmgqa::fwd_kernel<128, false>", 9e9)])
+    _pmc_csv(write, "WRITE_SIZE", [(ours, 300.0), (ours, 500.0), (copy, n / 1024)])
+    rec = bench.traffic_from_pmc(str(fetch), str(write), "bwd_dkdv", "tp405b", "cmd")
+    assert rec["fetch_kib_per_launch"] == 1100.0 and rec["write_kib_per_launch"] == 400.0
+    assert rec["fetch_scale"] == 0.5 and rec["write_scale"] == 1.0
+    assert rec["bytes_per_launch"] == int(1100 * 1024 * 0.5 + 400 * 1024)
+    assert rec["source_hash"] == bench.kernel_source_hash("bwd_dkdv")
+    _pmc_csv(write, "WRITE_SIZE", [(copy, n / 1024)])
+    with pytest.raises(SystemExit):
+        bench.traffic_from_pmc(str(fetch), str(write), "bwd_dkdv", "tp405b", "cmd")
+
+
+def test_measured_traffic_only_for_the_measured_code(tmp_path, monkeypatch):
+    """A stored traffic figure is reported while its source hash matches the
+    kernel's code, and dropped (None) once the code has changed."""
+    import json
+    monkeypatch.setattr(bench, "TRAFFIC_DIR", str(tmp_path))
+    assert bench.measured_traffic("bwd_dkdv", "tp405b") is None
+    rec = {"bytes_per_launch": 12345, "source_hash": bench.kernel_source_hash("bwd_dkdv")}
+    (tmp_path / "traffic_bwd_dkdv_tp405b.json").write_text(json.dumps(rec))
+    assert bench.measured_traffic("bwd_dkdv", "tp405b") == 12345
+    rec["source_hash"] = "0" * 16
+    (tmp_path / "traffic_bwd_dkdv_tp405b.json").write_text(json.dumps(rec))
+    assert bench.measured_traffic("bwd_dkdv", "tp405b") is None
+
